@@ -1,0 +1,300 @@
+/*
+ * sdv.h — C ABI of the MI355X (gfx950) speculative-decoding verify-attention library.
+ *
+ * The library computes the multi-token verify step of speculative decoding over a
+ * paged KV cache.  Each request r contributes qo_len = 1 + draft_len query tokens;
+ * token t (0 <= t < qo_len) attends the first
+ *
+ *     bound(r, t) = kv_len[r] - qo_len[r] + t + 1
+ *
+ * positions of its request, where kv_len counts the request's own verify tokens.
+ * (Source: "[TRTLLM-14093][feat] Eagle3 for M3 MSA path + CUDA graphs
+ * compatibility", MSA multi-token verify commit: the inclusive causal bound with
+ * offset kv_len - qo_len gives this ladder.)
+ *
+ * Two variants:
+ *   dense  — GQA draft-layer attention through a non-owning 32-token sub-page view
+ *            of 128-token physical pages:  kv_subpage_view_init, then
+ *            verify_attention_dense.
+ *   sparse — block-sparse target layer:  proxy_page_scores -> ladder_topk_pages ->
+ *            verify_attention_sparse.
+ *
+ * Conventions shared by every entry point
+ *   - Return value: SDV_OK (0) or a nonzero sdv_status.  On failure nothing was
+ *     enqueued and sdv_last_error() holds a message (thread-local).
+ *   - All argument checks run on the host before any HIP call, so every rejection
+ *     is reproducible without a GPU.
+ *   - Pointers marked "device" are caller-owned device memory; the library never
+ *     allocates, frees, synchronises or creates streams, and keeps no pointer after
+ *     the call returns.  Every kernel goes onto `stream` (0 = the default stream),
+ *     so the calls can be captured into a HIP graph.
+ *   - Grids are sized from capacities (batch, max_qo_len, page-table width), never
+ *     from current lengths: kv_len and qo_indptr are read on the device each launch,
+ *     so a captured launch stays correct when the lengths change.
+ *   - Query rows: request r owns rows qo_indptr[r] .. qo_indptr[r+1]-1 of q, out,
+ *     scores and top-k arrays; row-indexed buffers are sized for B * max_qo_len rows.
+ *   - Query head hq belongs to KV head hq / (num_q_heads / num_kv_heads).
+ *   - dev_err (nullable, device int32): a kernel that meets inconsistent data ORs an
+ *     SDV_DEVERR_* bit into it and skips the affected request or row; its outputs are
+ *     then unspecified.  Clear it before the call if you want to read it after.
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum sdv_status {
+  SDV_OK = 0,
+  SDV_ERR_NULL_POINTER = 1,   /* a required pointer is null                          */
+  SDV_ERR_DTYPE = 2,          /* unsupported element type or type combination        */
+  SDV_ERR_GEOMETRY = 3,       /* page geometry the native P128 draft view cannot serve */
+  SDV_ERR_SHAPE = 4,          /* sizes out of the supported range                     */
+  SDV_ERR_WORKSPACE = 5,      /* workspace missing or smaller than sdv_workspace_bytes */
+  SDV_ERR_HIP = 6,            /* a HIP launch reported an error                        */
+} sdv_status;
+
+typedef enum sdv_dtype {
+  SDV_F32 = 0,                /* IEEE binary32                                         */
+  SDV_BF16 = 1,               /* bfloat16                                              */
+  SDV_FP8_E4M3 = 2,           /* OCP E4M3FN (bias 7, max 448, no inf), with an fp32
+                                 per-tensor scale: value = decode(byte) * scale        */
+} sdv_dtype;
+
+/* Device error bits. */
+#define SDV_DEVERR_QO_LEN 1       /* qo_len < 1, qo_len > max_qo_len, kv_len < qo_len,
+                                     or qo_indptr rows beyond B * max_qo_len           */
+#define SDV_DEVERR_KV_CAPACITY 2  /* kv_len larger than the page table can address    */
+#define SDV_DEVERR_PAGE_RANGE 4   /* a slot, page or sub-page index outside the pool   */
+#define SDV_DEVERR_TOPK_INDEX 8   /* a top-k page index >= the token's valid pages     */
+
+#define SDV_PHYS_PAGE 128
+#define SDV_SUB_PAGE 32
+
+/* ---------------------------------------------------------------------------------
+ * Dense draft layer: the non-owning P32 view of P128 pages.
+ *
+ * Pool geometry (sources: "[None][perf] wrap up eagle changes in m3 side branch",
+ * commit fixing the draft view's index scale; "[None][perf] Default Minimax-m3 to
+ * unified draft-target kv manager + change CI test to GQA eagle head", section Root
+ * causes and fixes, item 2 "Grouped-HND draft KV transfer"):
+ *   - the view is rooted at the draft layer's K page of slot 0 (k_root);
+ *   - counted in 128-token pages from the root, slot s's K page is s * slot_stride
+ *     and its V page s * slot_stride + 1 (kv_offset = 1); slot_stride is the view's
+ *     index scale, and the pool's own page-index scale is NOT used (it may differ,
+ *     e.g. 171 against a stride of 8);
+ *   - each 128-token page is four independent head-major 32-token groups,
+ *     logically [group = 4][num_kv_heads][32][head_dim], elements contiguous.
+ *   So P32 page x (counted from k_root) holds element (head h, token o, channel c)
+ *   at element offset ((x * num_kv_heads + h) * 32 + o) * head_dim + c.
+ * ------------------------------------------------------------------------------- */
+typedef struct sdv_subpage_geom {
+  int32_t phys_page;        /* must be 128                                             */
+  int32_t sub_page;         /* must be 32                                              */
+  int32_t num_kv_heads;     /* >= 1                                                    */
+  int32_t head_dim;         /* 64 or 128                                               */
+  int32_t slot_stride;      /* P128 pages per slot, >= 2                               */
+  int32_t kv_offset;        /* V page minus K page within a slot; must be 1            */
+  int32_t num_layers;       /* layers the view spans; must be 1 (single-layer view)    */
+  int32_t num_slots;        /* slots addressable from k_root; ids must be < num_slots  */
+  int32_t pool_index_scale; /* the pool's page-index scale: recorded, never used       */
+  int32_t kv_dtype;         /* sdv_dtype of the stored K/V                             */
+  float k_scale;            /* dequantisation scales (1.0 unless fp8)                 */
+  float v_scale;
+  const void* k_root;       /* device: first element of slot 0's draft-layer K page    */
+} sdv_subpage_geom;
+
+/* Plain value describing a validated view; produced by kv_subpage_view_init. */
+typedef struct sdv_subpage_view {
+  const void* k_root;
+  int32_t kv_dtype;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t index_scale;      /* = slot_stride                                           */
+  int32_t num_slots;
+  float k_scale;
+  float v_scale;
+  int64_t num_sub_pages;    /* P32 pages from k_root through the last slot's V page:
+                               4 * ((num_slots - 1) * slot_stride + 2)                 */
+} sdv_subpage_view;
+
+/*
+ * kv_subpage_view_init — validate the draft view's geometry and write, for every
+ * request and every 32-token sub-page of its block-table capacity, the P32 page
+ * indices of its K and V:
+ *     slot = block_table[r * bt_stride + i / 4],  g = i % 4,
+ *     sub_offsets[r][0][i] = 4 * slot_stride * slot + g,
+ *     sub_offsets[r][1][i] = sub_offsets[r][0][i] + 4.
+ * Padding entries are left as the caller wrote them (0 = slot 0, valid memory; the
+ * pages keep the padding instead of clamping it: same PR #18066, commit removing
+ * code made redundant by the native P128 draft view).
+ *
+ * geom        host, read during the call.
+ * block_table device int32 [B][bt_stride], P128 slot ids; columns >= max_blocks unused.
+ * sub_offsets device int32 out [B][2][4 * max_blocks].
+ * view_out    host out: the validated view (plain value; copy freely).
+ * dev_err     nullable; SDV_DEVERR_PAGE_RANGE for a slot id outside [0, num_slots)
+ *             (that entry is then written as slot 0).
+ * Errors: SDV_ERR_GEOMETRY ("native P128 draft view unavailable: <reason>") for a
+ * page other than 128, sub-page other than 32, kv_offset != 1, num_layers != 1,
+ * slot_stride < 2, head_dim not 64/128, or num_slots * slot_stride * 4 >= 2^31.
+ */
+int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_table,
+                             int32_t B, int32_t max_blocks, int32_t bt_stride,
+                             int32_t* sub_offsets, sdv_subpage_view* view_out,
+                             int32_t* dev_err, hipStream_t stream);
+
+/*
+ * verify_attention_dense — dense GQA verify attention through the P32 view.
+ *   out[row(r,t)][hq] = sum_{j < bound(r,t)} softmax_j(scale * q . k_j) * v_j
+ * over the request's logical positions j, K/V gathered through sub_offsets
+ * (position j lives in P32 page sub_offsets[r][.][j / 32], token j % 32).
+ * Float32 accumulation.  (Sources: PR #17835 Description — the Eagle3 drafter reads
+ * its KV through the non-owning sub-page view; PR #3 MSA verify commit — the ladder.)
+ *
+ * q            device [B*max_qo_len rows capacity][num_q_heads][head_dim], q_dt.
+ * qo_indptr    device int32 [B+1];  kv_len device int32 [B].
+ * view         host: from kv_subpage_view_init.
+ * sub_offsets  device int32 [B][2][max_sub_pages]; kv_len[r] <= 32 * max_sub_pages.
+ * num_splits   >= 1: each (request, KV head) splits the sub-page capacity
+ *              [0, max_sub_pages) into num_splits equal contiguous chunks (trailing
+ *              chunks of short requests are empty); partials are merged by the
+ *              log-sum-exp combine.  num_splits = 1 needs no workspace.
+ * workspace    device, >= sdv_workspace_bytes(B*max_qo_len, num_q_heads, head_dim,
+ *              num_splits) bytes (nullable when that is 0).
+ * out          device [rows][num_q_heads][head_dim], out_dt (F32 or BF16).
+ * Supported: q_dt F32 with F32 K/V; q_dt BF16 with BF16 or FP8 K/V; head_dim 64 or
+ * 128; num_q_heads % num_kv_heads == 0; max_qo_len * G <= 64.
+ */
+int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_subpage_view* view,
+                               const int32_t* sub_offsets, int32_t max_sub_pages,
+                               float softmax_scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* out, int32_t out_dt,
+                               int32_t* dev_err, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Sparse target layer over ordinary head-major 128-token pages: page p of K holds
+ * [num_kv_heads][128][head_dim] contiguous elements at k + p * page_stride (V alike).
+ * Request r's position j is token j % 128 of page block_table[r * bt_stride + j/128].
+ * ------------------------------------------------------------------------------- */
+typedef struct sdv_paged_kv {
+  const void* k;            /* device: page 0 of K                                     */
+  const void* v;            /* device: page 0 of V                                     */
+  int64_t page_stride;      /* elements between pages, >= num_kv_heads * 128 * head_dim */
+  int32_t num_pages;        /* page ids must lie in [0, num_pages)                     */
+  int32_t page_size;        /* must be 128                                             */
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* 64 or 128                                               */
+  int32_t kv_dtype;         /* sdv_dtype                                               */
+  float k_scale;
+  float v_scale;
+} sdv_paged_kv;
+
+/*
+ * proxy_page_scores — score every page of every request for every verify token in
+ * one pass over K (PR #3 MSA verify commit: the proxy "OnlyScore" pass is natively
+ * multi-token under the ladder bound; its formula is not on the pages and is fixed
+ * here as):
+ *   scores[row(r,t)][h][p] = max_{hq in group h} q[row][hq] . ksum(r,t,h,p),
+ *   ksum = sum of K[j][h][:] over positions j of page p with j < bound(r,t),
+ * and -inf for pages with no such position.  Unscaled (no softmax or fp8 scale).
+ * Evaluated in float32 in a fixed order: ksum accumulated one position at a time in
+ * ascending order starting from 0; products q[c] * ksum[c] rounded separately (no
+ * fused multiply-add); summed by recursive halving over channels (c with c + n/2,
+ * n = head_dim, head_dim/2, ..., 2); -0 returned as +0.
+ *
+ * scores  device float [B*max_qo_len][num_kv_heads][max_pages]; entries for pages
+ *         p < ceil(kv_len[r] / 128) of each request are written, others untouched.
+ * block_table device int32 [B][bt_stride], request-local page p -> physical page.
+ * Supported: q F32 or BF16; K F32, BF16 or FP8; head_dim 64 or 128;
+ * max_qo_len * G * head_dim <= 16384.
+ */
+int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                          const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                          int32_t num_q_heads, const sdv_paged_kv* kv,
+                          const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                          float* scores, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * ladder_topk_pages — per (token, KV head): the k_eff = min(top_k, n_valid) best
+ * pages among p < n_valid(r,t) = ceil(bound(r,t) / 128), ordered by score
+ * descending then page index ascending (ties go to the lower page), written in rank
+ * order and padded with -1 (PR #3 MSA verify commit: per-token ladder valid-page
+ * counts, so a draft token cannot select pages past its own bound).
+ *
+ * scores    device float [B*max_qo_len][num_kv_heads][max_pages] (reads p < n_valid).
+ * topk_idx  device int32 out [B*max_qo_len][num_kv_heads][top_k].
+ * topk_cnt  device int32 out [B*max_qo_len][num_kv_heads], nullable.
+ * Supported: page_size 128; 1 <= top_k <= 1024; max_pages <= 4096.
+ */
+int32_t ladder_topk_pages(const float* scores, const int32_t* qo_indptr,
+                          const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                          int32_t num_kv_heads, int32_t max_pages, int32_t page_size,
+                          int32_t top_k, int32_t* topk_idx, int32_t* topk_cnt,
+                          int32_t* dev_err, hipStream_t stream);
+
+/*
+ * verify_attention_sparse — sparse GQA verify attention: token t, query head hq of
+ * KV head h attends position j iff page j / 128 is in topk_idx[row(r,t)][h][:] and
+ * j < bound(r,t).  Each (request, KV head) reads every page selected by any of its
+ * tokens once (the union), not once per token.  num_splits splits that union into
+ * near-equal contiguous chunks (split-KV with a log-sum-exp combine).
+ *
+ * topk_idx device int32 [B*max_qo_len][num_kv_heads][top_k], -1 = unused slot.
+ * Other arguments as in proxy_page_scores and verify_attention_dense.
+ * Supported: as verify_attention_dense; max_pages <= 16384.
+ */
+int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                int32_t num_q_heads, const sdv_paged_kv* kv,
+                                const int32_t* block_table, int32_t max_pages,
+                                int32_t bt_stride, const int32_t* topk_idx, int32_t top_k,
+                                float softmax_scale, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* out, int32_t out_dt,
+                                int32_t* dev_err, hipStream_t stream);
+
+/*
+ * lse_combine — merge split-KV partials:  LSE = log sum_s exp(lse[s]),
+ * out = sum_s exp(lse[s] - LSE) * partial_out[s]; partials with lse = -inf are
+ * skipped; a row with no live partial gets 0.
+ * partial_out device float [num_splits][num_rows][num_heads][head_dim];
+ * partial_lse device float [num_splits][num_rows][num_heads] (natural log);
+ * out device [num_rows][num_heads][head_dim], out_dt F32 or BF16;
+ * lse_out device float [num_rows][num_heads], nullable.
+ */
+int32_t lse_combine(const float* partial_out, const float* partial_lse, int32_t num_splits,
+                    int32_t num_rows, int32_t num_heads, int32_t head_dim, void* out,
+                    int32_t out_dt, float* lse_out, hipStream_t stream);
+
+/* Workspace (bytes) a split-KV attention call needs for q_rows_cap = B * max_qo_len
+ * query rows; 0 when num_splits == 1. */
+size_t sdv_workspace_bytes(int32_t q_rows_cap, int32_t num_q_heads, int32_t head_dim,
+                           int32_t num_splits);
+
+/* Static text for a status code. */
+const char* sdv_status_string(int32_t status);
+
+/* Message of the calling thread's most recent failed call ("" if none). */
+const char* sdv_last_error(void);
+
+/* Kernel family selection, for cross-checking: 0 = automatic (matrix-core kernels
+ * where supported), 1 = force the vector-ALU kernels.  Returns the previous value. */
+int32_t sdv_set_kernel_family(int32_t family);
+
+/* Measurement helper: fill `bytes` (multiple of 16) of device memory with a 32-bit
+ * pattern — used to evict caches between timed runs. */
+int32_t sdv_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV_H */

@@ -1,0 +1,111 @@
+"""ctypes declarations of libsdv.so (the C ABI in include/sdv.h).
+
+Loading fails loudly when the library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdv.so")
+
+SDV_OK = 0
+SDV_ERR_NULL_POINTER = 1
+SDV_ERR_DTYPE = 2
+SDV_ERR_GEOMETRY = 3
+SDV_ERR_SHAPE = 4
+SDV_ERR_WORKSPACE = 5
+SDV_ERR_HIP = 6
+
+SDV_F32 = 0
+SDV_BF16 = 1
+SDV_FP8_E4M3 = 2
+
+DEVERR_QO_LEN = 1
+DEVERR_KV_CAPACITY = 2
+DEVERR_PAGE_RANGE = 4
+DEVERR_TOPK_INDEX = 8
+
+
+class SubpageGeom(C.Structure):
+    _fields_ = [
+        ("phys_page", C.c_int32), ("sub_page", C.c_int32), ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("slot_stride", C.c_int32), ("kv_offset", C.c_int32),
+        ("num_layers", C.c_int32), ("num_slots", C.c_int32), ("pool_index_scale", C.c_int32),
+        ("kv_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+        ("k_root", C.c_void_p),
+    ]
+
+
+class SubpageView(C.Structure):
+    _fields_ = [
+        ("k_root", C.c_void_p), ("kv_dtype", C.c_int32), ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("index_scale", C.c_int32), ("num_slots", C.c_int32),
+        ("k_scale", C.c_float), ("v_scale", C.c_float), ("num_sub_pages", C.c_int64),
+    ]
+
+
+class PagedKV(C.Structure):
+    _fields_ = [
+        ("k", C.c_void_p), ("v", C.c_void_p), ("page_stride", C.c_int64),
+        ("num_pages", C.c_int32), ("page_size", C.c_int32), ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("kv_dtype", C.c_int32), ("k_scale", C.c_float),
+        ("v_scale", C.c_float),
+    ]
+
+
+_P = C.c_void_p
+_I = C.c_int32
+_F = C.c_float
+_S = C.c_size_t
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "kv_subpage_view_init": (_I, [C.POINTER(SubpageGeom), _P, _I, _I, _I, _P,
+                                  C.POINTER(SubpageView), _P, _P]),
+    "verify_attention_dense": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(SubpageView), _P, _I,
+                                    _F, _I, _P, _S, _P, _I, _P, _P]),
+    "proxy_page_scores": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I, _P,
+                               _P, _P]),
+    "ladder_topk_pages": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "verify_attention_sparse": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I,
+                                     _P, _I, _F, _I, _P, _S, _P, _I, _P, _P]),
+    "lse_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
+    "sdv_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "sdv_status_string": (C.c_char_p, [_I]),
+    "sdv_last_error": (C.c_char_p, []),
+    "sdv_set_kernel_family": (_I, [_I]),
+    "sdv_fill_u32": (_I, [_P, _S, C.c_uint32, _P]),
+}
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc, gfx950); there is no fallback implementation")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class SdvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sdv status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def check(status: int) -> None:
+    if status != SDV_OK:
+        lib = load()
+        raise SdvError(status, lib.sdv_last_error().decode() or lib.sdv_status_string(status).decode())

@@ -1,0 +1,235 @@
+"""PyTorch-facing binding of the verify-attention library.
+
+Argument marshalling only: each function turns tensors into pointers, sizes and a
+stream handle and calls the C entry point of the same name; every step of the path
+runs in the HIP kernels.  PyTorch supplies device memory and the current stream.
+Output tensors may be passed in (no allocation, e.g. in timed loops) or are allocated
+here.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.SDV_F32, torch.bfloat16: L.SDV_BF16, torch.float8_e4m3fn: L.SDV_FP8_E4M3}
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, contiguous=True):
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class SubpageView:
+    """A validated non-owning P32 view (keeps the pool tensor alive)."""
+    c: L.SubpageView
+    pool: torch.Tensor
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.c.num_kv_heads
+
+    @property
+    def head_dim(self) -> int:
+        return self.c.head_dim
+
+
+def kv_subpage_view_init(k_root: torch.Tensor, block_table: torch.Tensor, *, num_kv_heads: int,
+                         head_dim: int, slot_stride: int, num_slots: int,
+                         k_scale: float = 1.0, v_scale: float = 1.0, pool_index_scale: int = 0,
+                         kv_offset: int = 1, num_layers: int = 1, phys_page: int = 128,
+                         sub_page: int = 32, max_blocks: Optional[int] = None,
+                         sub_offsets: Optional[torch.Tensor] = None,
+                         dev_err: Optional[torch.Tensor] = None):
+    """k_root: tensor whose first element is slot 0's draft-layer K page.
+    block_table: int32 [B, W] P128 slot ids.  Returns (SubpageView, sub_offsets
+    int32 [B, 2, 4 * max_blocks])."""
+    _need(block_table, "block_table", torch.int32, contiguous=False)
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    B, W = block_table.shape
+    mb = W if max_blocks is None else max_blocks
+    if sub_offsets is None:
+        sub_offsets = torch.empty((B, 2, 4 * mb), dtype=torch.int32, device=block_table.device)
+    _need(sub_offsets, "sub_offsets", torch.int32)
+    geom = L.SubpageGeom(phys_page, sub_page, num_kv_heads, head_dim, slot_stride, kv_offset,
+                         num_layers, num_slots, pool_index_scale, dtype_code(k_root.dtype),
+                         k_scale, v_scale, k_root.data_ptr())
+    view = L.SubpageView()
+    L.check(L.load().kv_subpage_view_init(C.byref(geom), _ptr(block_table), B, mb,
+                                          block_table.stride(0), _ptr(sub_offsets),
+                                          C.byref(view), _ptr(dev_err),
+                                          _stream(block_table.device)))
+    return SubpageView(view, k_root), sub_offsets
+
+
+def workspace_bytes(q_rows_cap: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(L.load().sdv_workspace_bytes(q_rows_cap, num_q_heads, head_dim, num_splits))
+
+
+def alloc_workspace(q_rows_cap: int, num_q_heads: int, head_dim: int, num_splits: int, device):
+    n = workspace_bytes(q_rows_cap, num_q_heads, head_dim, num_splits)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _out(out, q, rows_cap, out_dtype):
+    if out is None:
+        out = torch.empty((rows_cap, q.shape[1], q.shape[2]), dtype=out_dtype or q.dtype,
+                          device=q.device)
+    _need(out, "out")
+    return out
+
+
+def verify_attention_dense(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
+                           view: SubpageView, sub_offsets: torch.Tensor, *, max_qo_len: int,
+                           softmax_scale: float, num_splits: int = 1,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, out_dtype=None,
+                           dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q [rows, Hq, d]; returns out [B * max_qo_len, Hq, d] (rows of each request at
+    qo_indptr[r] ..)."""
+    _need(q, "q")
+    _need(qo_indptr, "qo_indptr", torch.int32)
+    _need(kv_len, "kv_len", torch.int32)
+    _need(sub_offsets, "sub_offsets", torch.int32)
+    B = kv_len.numel()
+    rows_cap = B * max_qo_len
+    out = _out(out, q, rows_cap, out_dtype)
+    if workspace is None and num_splits > 1:
+        workspace = alloc_workspace(rows_cap, q.shape[1], q.shape[2], num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().verify_attention_dense(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(view.c), _ptr(sub_offsets), sub_offsets.shape[-1], softmax_scale, num_splits,
+        _ptr(workspace), ws_bytes, _ptr(out), dtype_code(out.dtype), _ptr(dev_err),
+        _stream(q.device)))
+    return out
+
+
+@dataclass
+class PagedKV:
+    """Head-major P128 page arrays k/v [num_pages, Hkv, 128, d] (non-owning view)."""
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    def c(self) -> L.PagedKV:
+        if self.k.shape != self.v.shape or self.k.dtype != self.v.dtype:
+            raise ValueError("k and v pools must match in shape and dtype")
+        if not (self.k.is_contiguous() and self.v.is_contiguous()):
+            raise ValueError("k and v pools must be contiguous")
+        n, H, P, d = self.k.shape
+        return L.PagedKV(self.k.data_ptr(), self.v.data_ptr(), H * P * d, n, P, H, d,
+                         dtype_code(self.k.dtype), self.k_scale, self.v_scale)
+
+
+def proxy_page_scores(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
+                      kv: PagedKV, block_table: torch.Tensor, *, max_qo_len: int,
+                      scores: Optional[torch.Tensor] = None,
+                      dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Returns scores float32 [B * max_qo_len, Hkv, max_pages]."""
+    _need(q, "q")
+    _need(block_table, "block_table", torch.int32, contiguous=False)
+    B = kv_len.numel()
+    max_pages = block_table.shape[1]
+    ckv = kv.c()
+    if scores is None:
+        scores = torch.empty((B * max_qo_len, ckv.num_kv_heads, max_pages), dtype=torch.float32,
+                             device=q.device)
+    _need(scores, "scores", torch.float32)
+    L.check(L.load().proxy_page_scores(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(ckv), _ptr(block_table), max_pages, block_table.stride(0), _ptr(scores),
+        _ptr(dev_err), _stream(q.device)))
+    return scores
+
+
+def ladder_topk_pages(scores: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor, *,
+                      max_qo_len: int, top_k: int, page_size: int = 128,
+                      topk_idx: Optional[torch.Tensor] = None,
+                      topk_cnt: Optional[torch.Tensor] = None, want_count: bool = False,
+                      dev_err: Optional[torch.Tensor] = None):
+    """Returns topk_idx int32 [B * max_qo_len, Hkv, top_k] (and counts if asked)."""
+    _need(scores, "scores", torch.float32)
+    B = kv_len.numel()
+    rows, Hkv, max_pages = scores.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((rows, Hkv, top_k), dtype=torch.int32, device=scores.device)
+    if topk_cnt is None and want_count:
+        topk_cnt = torch.empty((rows, Hkv), dtype=torch.int32, device=scores.device)
+    L.check(L.load().ladder_topk_pages(
+        _ptr(scores), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, Hkv, max_pages, page_size,
+        top_k, _ptr(topk_idx), _ptr(topk_cnt), _ptr(dev_err), _stream(scores.device)))
+    return (topk_idx, topk_cnt) if want_count or topk_cnt is not None else topk_idx
+
+
+def verify_attention_sparse(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
+                            kv: PagedKV, block_table: torch.Tensor, topk_idx: torch.Tensor, *,
+                            max_qo_len: int, softmax_scale: float, num_splits: int = 1,
+                            workspace: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, out_dtype=None,
+                            dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(q, "q")
+    _need(topk_idx, "topk_idx", torch.int32)
+    B = kv_len.numel()
+    rows_cap = B * max_qo_len
+    out = _out(out, q, rows_cap, out_dtype)
+    if workspace is None and num_splits > 1:
+        workspace = alloc_workspace(rows_cap, q.shape[1], q.shape[2], num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ckv = kv.c()
+    L.check(L.load().verify_attention_sparse(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(ckv), _ptr(block_table), block_table.shape[1], block_table.stride(0),
+        _ptr(topk_idx), topk_idx.shape[-1], softmax_scale, num_splits, _ptr(workspace), ws_bytes,
+        _ptr(out), dtype_code(out.dtype), _ptr(dev_err), _stream(q.device)))
+    return out
+
+
+def lse_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, *, out_dtype=torch.float32,
+                out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                want_lse: bool = False):
+    """partial_out [S, rows, H, d] float32, partial_lse [S, rows, H] float32."""
+    _need(partial_out, "partial_out", torch.float32)
+    _need(partial_lse, "partial_lse", torch.float32)
+    S, rows, H, d = partial_out.shape
+    if out is None:
+        out = torch.empty((rows, H, d), dtype=out_dtype, device=partial_out.device)
+    if lse_out is None and want_lse:
+        lse_out = torch.empty((rows, H), dtype=torch.float32, device=partial_out.device)
+    L.check(L.load().lse_combine(_ptr(partial_out), _ptr(partial_lse), S, rows, H, d, _ptr(out),
+                                 dtype_code(out.dtype), _ptr(lse_out),
+                                 _stream(partial_out.device)))
+    return (out, lse_out) if want_lse else out
+
+
+def set_kernel_family(family: int) -> int:
+    """0 = automatic (matrix-core kernels where supported), 1 = vector-ALU kernels."""
+    return int(L.load().sdv_set_kernel_family(family))
+
+
+def fill_u32(dst: torch.Tensor, pattern: int = 0) -> None:
+    L.check(L.load().sdv_fill_u32(_ptr(dst), dst.numel() * dst.element_size(), pattern,
+                                  _stream(dst.device)))

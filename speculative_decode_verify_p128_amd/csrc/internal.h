@@ -1,0 +1,87 @@
+// Internal launch interface between the C-ABI layer (sdv_api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sdv.h"
+
+namespace sdv {
+
+// Where a (request, KV head)'s 32-token K/V blocks live.
+struct DenseSource {            // P32 sub-page view
+  const void* root;             // element 0 of P32 page 0
+  const int32_t* sub_offsets;   // [B][2][max_sub_pages]
+  int32_t max_sub_pages;
+  int64_t num_sub_pages;        // valid P32 page range from root
+};
+
+struct SparseSource {           // head-major P128 pages + selected page lists
+  const void* k;
+  const void* v;
+  int64_t page_stride;          // elements
+  int32_t num_pages;
+  const int32_t* block_table;   // [B][bt_stride]
+  int32_t bt_stride;
+  int32_t max_pages;
+  const int32_t* topk_idx;      // [rows][Hkv][top_k]
+  int32_t top_k;
+};
+
+struct AttnArgs {
+  const void* q;
+  int32_t q_dt;
+  const int32_t* qo_indptr;
+  const int32_t* kv_len;
+  int32_t B;
+  int32_t max_qo_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dt;
+  float k_scale;
+  float v_scale;
+  float softmax_scale;
+  int32_t num_splits;
+  float* part_o;                // [splits][rows_cap][Hq][d] when num_splits > 1
+  float* part_lse;              // [splits][rows_cap][Hq]
+  void* out;
+  int32_t out_dt;
+  int32_t* dev_err;
+};
+
+hipError_t launch_subpage_offsets(const int32_t* block_table, int32_t B, int32_t max_blocks,
+                                  int32_t bt_stride, int32_t slot_stride, int32_t num_slots,
+                                  int32_t* sub_offsets, int32_t* dev_err, hipStream_t s);
+
+hipError_t launch_proxy_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_paged_kv& kv,
+                               const int32_t* block_table, int32_t max_pages,
+                               int32_t bt_stride, float* scores, int32_t* dev_err,
+                               hipStream_t s);
+
+hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int32_t* kv_len,
+                       int32_t B, int32_t max_qo_len, int32_t num_kv_heads,
+                       int32_t max_pages, int32_t top_k, int32_t* topk_idx,
+                       int32_t* topk_cnt, int32_t* dev_err, hipStream_t s);
+
+// Vector-ALU attention kernels (any supported dtype).
+hipError_t launch_attn_dense_valu(const AttnArgs& a, const DenseSource& src, hipStream_t s);
+hipError_t launch_attn_sparse_valu(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+
+// Matrix-core attention kernels (bf16 Q; bf16 or fp8 K/V; head_dim 64/128).
+bool mfma_supported(const AttnArgs& a);
+hipError_t launch_attn_dense_mfma(const AttnArgs& a, const DenseSource& src, hipStream_t s);
+hipError_t launch_attn_sparse_mfma(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+
+// Rows [*row_begin_dev, *row_end_dev) are combined (all rows_cap rows when null).
+hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t num_splits,
+                          int32_t rows_cap, const int32_t* row_begin_dev,
+                          const int32_t* row_end_dev, int32_t num_heads, int32_t head_dim,
+                          void* out, int32_t out_dt, float* lse_out, hipStream_t s);
+
+hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s);
+
+}  // namespace sdv

@@ -1,0 +1,314 @@
+// Verify attention on the vector ALUs (any supported element type).
+//
+// Dense: token t of request r attends its request's positions j < bound(r,t) =
+// kv_len - qo_len + t + 1, read through the P32 sub-page view ("[None][perf] Default
+// Minimax-m3 to unified draft-target kv manager ...", Description and item 2).
+// Sparse: token t, KV head h attends positions j < bound(r,t) whose page j / 128 it
+// selected ("[TRTLLM-14093][feat] Eagle3 for M3 MSA path + CUDA graphs
+// compatibility", MSA verify commit).  Unlike the pages' row-expanded kernel, every
+// (request, KV head) reads the union of its tokens' pages once and applies each
+// token's own page set as a per-row mask.
+//
+// One workgroup (256 threads) per (request, KV head, split).  Query rows are the G x
+// qo (token, head) pairs, row = t * G + g, at most 64.  Keys and values pass through
+// LDS in 16-token tiles as float; scores, online-softmax state and the output
+// accumulators are float32; exponentials in base 2 with log2(e) folded into the
+// query scale.
+#include "device.h"
+#include "internal.h"
+
+namespace sdv {
+
+constexpr int kMaxRows = 64;
+constexpr int kTile = 16;
+constexpr int kMaxUnion = 512;
+constexpr int kMaxWords = 512;   // max_pages <= 16384
+
+template <int D>
+struct ValuSmem {
+  float qs[kMaxRows][D];
+  float ks[kTile][D + 1];
+  float vs[kTile][D];
+  float ps[kMaxRows][kTile];
+  float row_m[kMaxRows];
+  float row_l[kMaxRows];
+  float row_a[kMaxRows];
+  uint32_t bitmap[kMaxWords];
+  int32_t word_prefix[kMaxWords];
+  int32_t upage[kMaxUnion];
+  int32_t umask[kMaxUnion];
+  int32_t scan[256];
+  int32_t bad;
+  int32_t n_union;
+};
+
+// Builds the sorted union of the pages the request's tokens selected for KV head h,
+// with a bit mask of the selecting tokens per page.  Returns the union size.
+template <int D>
+__device__ int build_union(ValuSmem<D>& sm, const SparseSource& ss, int r, int h, int Hkv,
+                           int row0, int qo, int kv, int32_t* dev_err) {
+  const int tid = threadIdx.x;
+  const int words = (ss.max_pages + 31) / 32;
+  for (int w = tid; w < words; w += blockDim.x) sm.bitmap[w] = 0u;
+  if (tid == 0) sm.bad = 0;
+  __syncthreads();
+  const int n_el = qo * ss.top_k;
+  for (int e = tid; e < n_el; e += blockDim.x) {
+    const int t = e / ss.top_k;
+    const int k = e - t * ss.top_k;
+    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+    if (p < 0) continue;
+    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
+    if (p >= nvalid) {
+      set_err(dev_err, SDV_DEVERR_TOPK_INDEX);
+      continue;
+    }
+    atomicOr(&sm.bitmap[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // exclusive prefix of popcounts over words: each thread owns two words
+  const int w0 = 2 * tid;
+  int c0 = (w0 < words) ? __popc(sm.bitmap[w0]) : 0;
+  int c1 = (w0 + 1 < words) ? __popc(sm.bitmap[w0 + 1]) : 0;
+  sm.scan[tid] = c0 + c1;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? sm.scan[tid - off] : 0;
+    __syncthreads();
+    sm.scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = sm.scan[tid] - (c0 + c1);
+  if (w0 < words) sm.word_prefix[w0] = excl;
+  if (w0 + 1 < words) sm.word_prefix[w0 + 1] = excl + c0;
+  const int total = sm.scan[255];
+  __syncthreads();
+  for (int w = tid; w < words; w += blockDim.x) {
+    uint32_t bits = sm.bitmap[w];
+    int idx = sm.word_prefix[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      sm.upage[idx] = w * 32 + b;
+      sm.umask[idx] = 0;
+      ++idx;
+      bits &= bits - 1;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < n_el; e += blockDim.x) {
+    const int t = e / ss.top_k;
+    const int k = e - t * ss.top_k;
+    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
+    if (p < 0 || p >= nvalid) continue;
+    const int w = p >> 5;
+    const int idx = sm.word_prefix[w] + __popc(sm.bitmap[w] & ((1u << (p & 31)) - 1u));
+    atomicOr(&sm.umask[idx], 1 << t);
+  }
+  __syncthreads();
+  return total;
+}
+
+template <int D, bool SPARSE>
+__global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSource ds,
+                                                           SparseSource ss) {
+  __shared__ ValuSmem<D> sm;
+  constexpr int NE = kMaxRows * D / 256;   // accumulators per thread
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
+                                : static_cast<int64_t>(ds.max_sub_pages) * kSub;
+  const int row0 = a.qo_indptr[r];
+  const int qo = a.qo_indptr[r + 1] - row0;
+  const int kv = a.kv_len[r];
+  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
+  const bool bad_cap = !bad_len && kv > kv_cap;
+  if (bad_len || bad_cap) {
+    if (tid == 0 && split == 0 && h == 0)
+      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  const int R = qo * G;
+  const float qscale = a.softmax_scale * a.k_scale * kLog2e;
+
+  // Query rows, scaled into the base-2 score domain.
+  for (int i = tid; i < R * D; i += 256) {
+    const int row = i / D;
+    const int c = i - row * D;
+    const int t = row / G;
+    const int g = row - t * G;
+    const int64_t src = (static_cast<int64_t>(row0 + t) * a.num_q_heads + h * G + g) * D + c;
+    sm.qs[row][c] = load_elem(a.q, src, a.q_dt) * qscale;
+  }
+  if (tid < kMaxRows) {
+    sm.row_m[tid] = -INFINITY;
+    sm.row_l[tid] = 0.f;
+  }
+
+  // This split's work: a range of 32-token blocks.
+  int blk_lo, blk_hi;     // dense: sub-pages; sparse: union entries (each 4 blocks)
+  int n_union = 0;
+  if constexpr (SPARSE) {
+    n_union = build_union<D>(sm, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
+    const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
+    blk_lo = split * chunk;
+    blk_hi = min(n_union, blk_lo + chunk);
+  } else {
+    const int chunk = (ds.max_sub_pages + a.num_splits - 1) / a.num_splits;
+    const int nb = (kv + kSub - 1) / kSub;
+    blk_lo = split * chunk;
+    blk_hi = min(nb, blk_lo + chunk);
+  }
+  __syncthreads();
+
+  float o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] = 0.f;
+
+  const int n_sub = SPARSE ? 4 : 1;    // 32-token blocks per work item
+  for (int item = blk_lo; item < blk_hi; ++item) {
+    int mask = ~0;
+    const void* kb = nullptr;
+    const void* vb = nullptr;
+    int64_t kofs = 0, vofs = 0;     // element offset of token 0 of the 32-token block
+    int pos_base;
+    bool ok = true;
+    if constexpr (SPARSE) {
+      const int p = sm.upage[item];
+      mask = sm.umask[item];
+      const int phys = ss.block_table[static_cast<int64_t>(r) * ss.bt_stride + p];
+      if (phys < 0 || phys >= ss.num_pages) ok = false;
+      kb = ss.k;
+      vb = ss.v;
+      kofs = (static_cast<int64_t>(phys) * ss.page_stride + static_cast<int64_t>(h) * kPage * D);
+      vofs = kofs;
+      pos_base = p * kPage;
+    } else {
+      const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
+      const int64_t xk = offs[item];
+      const int64_t xv = offs[ds.max_sub_pages + item];
+      if (xk < 0 || xk >= ds.num_sub_pages || xv < 0 || xv >= ds.num_sub_pages) ok = false;
+      kb = ds.root;
+      vb = ds.root;
+      kofs = (xk * Hkv + h) * kSub * D;
+      vofs = (xv * Hkv + h) * kSub * D;
+      pos_base = item * kSub;
+    }
+    if (!ok) {
+      if (tid == 0) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+      continue;
+    }
+    for (int sb = 0; sb < n_sub; ++sb) {
+      const int blk_pos = pos_base + sb * kSub;
+      if (blk_pos >= kv) break;
+      const int64_t kb_ofs = kofs + (SPARSE ? static_cast<int64_t>(sb) * kSub * D : 0);
+      const int64_t vb_ofs = vofs + (SPARSE ? static_cast<int64_t>(sb) * kSub * D : 0);
+      for (int half = 0; half < kSub / kTile; ++half) {
+        const int tile_pos = blk_pos + half * kTile;
+        if (tile_pos >= kv) break;
+        for (int i = tid; i < kTile * D; i += 256) {
+          const int jj = i / D;
+          const int c = i - jj * D;
+          const bool live = tile_pos + jj < kv;
+          const int64_t off = static_cast<int64_t>(half * kTile + jj) * D + c;
+          sm.ks[jj][c] = live ? load_elem(kb, kb_ofs + off, a.kv_dt) : 0.f;
+          sm.vs[jj][c] = live ? load_elem(vb, vb_ofs + off, a.kv_dt) : 0.f;
+        }
+        __syncthreads();
+        for (int i = tid; i < R * kTile; i += 256) {
+          const int row = i / kTile;
+          const int jj = i - row * kTile;
+          const int t = row / G;
+          const int pos = tile_pos + jj;
+          const bool allowed = pos < kv - qo + t + 1 && ((mask >> t) & 1);
+          float s = 0.f;
+#pragma unroll 8
+          for (int c = 0; c < D; ++c) s += sm.qs[row][c] * sm.ks[jj][c];
+          sm.ps[row][jj] = allowed ? s : -INFINITY;
+        }
+        __syncthreads();
+        if (tid < R) {
+          const float m_old = sm.row_m[tid];
+          float mx = m_old;
+          for (int jj = 0; jj < kTile; ++jj) mx = fmaxf(mx, sm.ps[tid][jj]);
+          float alpha = 1.f, lsum = 0.f;
+          if (mx != -INFINITY) {
+            alpha = exp2f(m_old - mx);
+            for (int jj = 0; jj < kTile; ++jj) {
+              const float pv = exp2f(sm.ps[tid][jj] - mx);
+              sm.ps[tid][jj] = pv;
+              lsum += pv;
+            }
+          } else {
+            for (int jj = 0; jj < kTile; ++jj) sm.ps[tid][jj] = 0.f;
+          }
+          sm.row_a[tid] = alpha;
+          sm.row_m[tid] = mx;
+          sm.row_l[tid] = sm.row_l[tid] * alpha + lsum;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const int idx = tid + 256 * e;
+          const int row = idx / D;
+          const int c = idx - row * D;
+          if (row < R) {
+            float acc = o[e] * sm.row_a[row];
+            for (int jj = 0; jj < kTile; ++jj) acc += sm.ps[row][jj] * sm.vs[jj][c];
+            o[e] = acc;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  // Write the (partial) result.
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int idx = tid + 256 * e;
+    const int row = idx / D;
+    const int c = idx - row * D;
+    if (row >= R) continue;
+    const int t = row / G;
+    const int g = row - t * G;
+    const int64_t qrow = row0 + t;
+    const int hq = h * G + g;
+    const float l = sm.row_l[row];
+    const float val = l > 0.f ? o[e] * a.v_scale / l : 0.f;
+    if (a.num_splits == 1) {
+      store_out(a.out, (qrow * a.num_q_heads + hq) * D + c, val, a.out_dt);
+    } else {
+      const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
+      const int64_t unit = (static_cast<int64_t>(split) * rows_cap + qrow) * a.num_q_heads + hq;
+      a.part_o[unit * D + c] = val;
+      if (c == 0) a.part_lse[unit] = l > 0.f ? (sm.row_m[row] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <bool SPARSE>
+static hipError_t launch_valu(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
+                              hipStream_t s) {
+  dim3 grid(a.num_splits, a.num_kv_heads, a.B);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((sdv_attn_valu_kernel<128, SPARSE>), grid, dim3(256), 0, s, a, ds, ss);
+  else
+    hipLaunchKernelGGL((sdv_attn_valu_kernel<64, SPARSE>), grid, dim3(256), 0, s, a, ds, ss);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_dense_valu(const AttnArgs& a, const DenseSource& src, hipStream_t s) {
+  return launch_valu<false>(a, src, SparseSource{}, s);
+}
+
+hipError_t launch_attn_sparse_valu(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
+  return launch_valu<true>(a, DenseSource{}, src, s);
+}
+
+}  // namespace sdv

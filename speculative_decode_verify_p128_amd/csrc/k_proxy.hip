@@ -1,0 +1,193 @@
+// Proxy page scores of the block-sparse target layer.
+//
+// "[TRTLLM-14093][feat] Eagle3 for M3 MSA path + CUDA graphs compatibility", MSA
+// multi-token verify commit: the proxy ("OnlyScore") pass runs natively multi-token
+// under the inclusive causal bound with offset kv_len - qo_len, so token t sees
+// kv_len - qo_len + t + 1 positions.  The pages give no formula; this library scores
+//   score(t, h, p) = max_{hq in group h} q[t, hq] . ksum(t, h, p),
+//   ksum(t, h, p)  = sum of K[j, h, :] over positions j of page p with j < bound_t,
+// in a fixed float32 order so that the ranking is reproducible bit for bit:
+//   1. ksum accumulated one position at a time, ascending, from 0;
+//   2. products q[c] * ksum[c] rounded separately (no fused multiply-add);
+//   3. recursive halving over channels: u[c] += u[c + n/2] for n = d, d/2, ..., 2;
+//   4. maximum over the G query heads; -0 becomes +0.
+//
+// Design (HBM-bound; K of every valid page is read exactly once for all tokens):
+//   one workgroup = 4 waves per (request, KV head, run of pages); within a wave a
+//   group of LPR lanes owns one page, each lane a contiguous 16-byte slice of every
+//   key row (8 bf16, 16 fp8 or 4 f32 channels), so each wave load instruction reads
+//   64/LPR full page rows.  A lane keeps its channels' running sums in registers and
+//   scores a token as soon as the running sum reaches that token's bound; the
+//   tokens' bounds differ by one position, so every token shares one pass.
+//   The halving tree first pairs channels c and c + d/2, which live in different
+//   lanes of the group (xor shuffles), and ends inside the lane.
+#include "device.h"
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace sdv {
+
+template <int KDT, int D>
+__global__ void __launch_bounds__(256) sdv_proxy_scores_kernel(
+    const void* __restrict__ q, int32_t q_dt, const int32_t* __restrict__ qo_indptr,
+    const int32_t* __restrict__ kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+    int32_t G, const void* __restrict__ kbase, int64_t page_stride, int32_t num_pages,
+    const int32_t* __restrict__ block_table, int32_t bt_stride, int32_t max_pages,
+    float* __restrict__ scores, int32_t* dev_err) {
+  using V16 = Vec16<KDT>;
+  constexpr int V = V16::N;          // channels per lane
+  constexpr int LPR = D / V;         // lanes per page
+  constexpr int PPW = kWave / LPR;   // pages per wave
+  constexpr int PPB = PPW * 4;       // pages per workgroup
+  constexpr int EB = elem_bytes<KDT>();
+  constexpr int U = 8;               // positions per unrolled step
+  extern __shared__ float q_lds[];   // [qo][G][D] float
+
+  const int r = blockIdx.z;
+  const int h = blockIdx.y;
+  const int Hkv = gridDim.y;
+  const int row0 = qo_indptr[r];
+  const int qo = qo_indptr[r + 1] - row0;
+  const int kv = kv_len[r];
+  const bool bad_len = qo < 1 || qo > max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(B) * max_qo_len;
+  const bool bad_cap = !bad_len && static_cast<int64_t>(kv) > static_cast<int64_t>(max_pages) * kPage;
+  if (bad_len || bad_cap) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0)
+      set_err(dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  const int n_pages_r = (kv + kPage - 1) / kPage;
+  const int p_first = blockIdx.x * PPB;
+  if (p_first >= n_pages_r) return;
+
+  // Stage this request's queries of KV head h as float: q_lds[(t * G + g) * D + c].
+  for (int i = threadIdx.x; i < qo * G * D; i += blockDim.x) {
+    const int t = i / (G * D);
+    const int rem = i - t * (G * D);
+    const int g = rem / D;
+    const int c = rem - g * D;
+    const int64_t src = (static_cast<int64_t>(row0 + t) * num_q_heads + h * G + g) * D + c;
+    q_lds[i] = q_dt == SDV_F32 ? reinterpret_cast<const float*>(q)[src]
+                               : __uint_as_float(static_cast<uint32_t>(
+                                     reinterpret_cast<const uint16_t*>(q)[src]) << 16);
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = lane / LPR;
+  const int sub = lane - grp * LPR;
+  const int p = p_first + wave * PPW + grp;
+  bool active = p < n_pages_r;
+  int32_t phys = 0;
+  if (active) {
+    phys = block_table[static_cast<int64_t>(r) * bt_stride + p];
+    if (phys < 0 || phys >= num_pages) {
+      set_err(dev_err, SDV_DEVERR_PAGE_RANGE);
+      active = false;
+      phys = 0;
+    }
+  }
+  const char* kp = reinterpret_cast<const char*>(kbase) +
+                   (static_cast<int64_t>(phys) * page_stride + static_cast<int64_t>(h) * kPage * D) * EB +
+                   sub * 16;
+  constexpr int ROW_BYTES = D * EB;
+
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  int j = 0;
+  float* out_rows = scores + (static_cast<int64_t>(row0) * Hkv + h) * max_pages + p;
+
+  for (int t = 0; t < qo; ++t) {
+    const int bound = kv - qo + t + 1;
+    int L = active ? bound - p * kPage : 0;
+    L = L < 0 ? 0 : (L > kPage ? kPage : L);
+    // Step 1: extend the running sums to the first L positions of the page.
+    for (; j + U <= L; j += U) {
+      uint4 w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        w[u] = *reinterpret_cast<const uint4*>(kp + static_cast<int64_t>(j + u) * ROW_BYTES);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[V];
+        V16::decode(w[u], x);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
+      }
+    }
+    for (; j < L; ++j) {
+      const uint4 w = *reinterpret_cast<const uint4*>(kp + static_cast<int64_t>(j) * ROW_BYTES);
+      float x[V];
+      V16::decode(w, x);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
+    }
+    // Steps 2-4 for every query head of the group.
+    float best = -INFINITY;
+    for (int g = 0; g < G; ++g) {
+      const float* qv = q_lds + (t * G + g) * D + sub * V;
+      float u[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) u[e] = qv[e] * acc[e];
+      // channel c pairs with c + n/2: across lanes while n/2 >= V ...
+#pragma unroll
+      for (int off = LPR / 2; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) u[e] = u[e] + __shfl_xor(u[e], off, kWave);
+      }
+      // ... then inside the lane.
+#pragma unroll
+      for (int n = V; n >= 2; n >>= 1) {
+#pragma unroll
+        for (int e = 0; e < n / 2; ++e) u[e] = u[e] + u[e + n / 2];
+      }
+      best = fmaxf(best, u[0]);
+    }
+    if (active && sub == 0) {
+      const float s = L > 0 ? best + 0.0f : -INFINITY;
+      out_rows[static_cast<int64_t>(t) * Hkv * max_pages] = s;
+    }
+  }
+}
+
+template <int KDT, int D>
+static hipError_t launch_proxy_t(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                 const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                 int32_t num_q_heads, const sdv_paged_kv& kv,
+                                 const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                                 float* scores, int32_t* dev_err, hipStream_t s) {
+  constexpr int V = Vec16<KDT>::N;
+  constexpr int PPB = (kWave / (D / V)) * 4;
+  const int G = num_q_heads / kv.num_kv_heads;
+  const size_t lds = static_cast<size_t>(max_qo_len) * G * D * sizeof(float);
+  dim3 grid((max_pages + PPB - 1) / PPB, kv.num_kv_heads, B);
+  hipLaunchKernelGGL((sdv_proxy_scores_kernel<KDT, D>), grid, dim3(256), lds, s, q, q_dt,
+                     qo_indptr, kv_len, B, max_qo_len, num_q_heads, G, kv.k, kv.page_stride,
+                     kv.num_pages, block_table, bt_stride, max_pages, scores, dev_err);
+  return hipGetLastError();
+}
+
+hipError_t launch_proxy_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_paged_kv& kv,
+                               const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                               float* scores, int32_t* dev_err, hipStream_t s) {
+#define SDV_PROXY_CASE(KDT, D)                                                               \
+  if (kv.kv_dtype == KDT && kv.head_dim == D)                                                \
+    return launch_proxy_t<KDT, D>(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, \
+                                  block_table, max_pages, bt_stride, scores, dev_err, s);
+  SDV_PROXY_CASE(SDV_F32, 64)
+  SDV_PROXY_CASE(SDV_F32, 128)
+  SDV_PROXY_CASE(SDV_BF16, 64)
+  SDV_PROXY_CASE(SDV_BF16, 128)
+  SDV_PROXY_CASE(SDV_FP8_E4M3, 64)
+  SDV_PROXY_CASE(SDV_FP8_E4M3, 128)
+#undef SDV_PROXY_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdv

@@ -1,0 +1,384 @@
+// C ABI of the verify-attention library: argument validation (host only, before any
+// HIP call), workspace layout, kernel-family dispatch and status reporting.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int32_t> g_family{0};
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return SDV_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SDV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_dtype(int32_t dt) { return dt == SDV_F32 || dt == SDV_BF16 || dt == SDV_FP8_E4M3; }
+bool valid_out_dtype(int32_t dt) { return dt == SDV_F32 || dt == SDV_BF16; }
+bool valid_head_dim(int32_t d) { return d == 64 || d == 128; }
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// q/kv element-type pairs the attention kernels implement.
+bool attn_dtype_pair(int32_t q_dt, int32_t kv_dt) {
+  return (q_dt == SDV_F32 && kv_dt == SDV_F32) ||
+         (q_dt == SDV_BF16 && (kv_dt == SDV_BF16 || kv_dt == SDV_FP8_E4M3));
+}
+
+// Shared checks of the query-side arguments of every attention / score call.
+int32_t check_query_side(const void* q, const int32_t* qo_indptr, const int32_t* kv_len,
+                         int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+                         int32_t num_kv_heads) {
+  if (B < 0) return fail(SDV_ERR_SHAPE, "batch %d < 0", B);
+  if (max_qo_len < 1) return fail(SDV_ERR_SHAPE, "max_qo_len %d < 1", max_qo_len);
+  if (num_kv_heads < 1) return fail(SDV_ERR_SHAPE, "num_kv_heads %d < 1", num_kv_heads);
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(SDV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (B > 0 && (!q || !qo_indptr || !kv_len))
+    return fail(SDV_ERR_NULL_POINTER, "q, qo_indptr and kv_len must be non-null");
+  return SDV_OK;
+}
+
+int32_t check_workspace(void* workspace, size_t workspace_bytes, int64_t rows_cap,
+                        int32_t num_q_heads, int32_t head_dim, int32_t num_splits) {
+  if (num_splits < 1 || num_splits > 4096)
+    return fail(SDV_ERR_SHAPE, "num_splits %d outside [1, 4096]", num_splits);
+  const size_t need = sdv_workspace_bytes(static_cast<int32_t>(rows_cap), num_q_heads, head_dim,
+                                          num_splits);
+  if (need > 0) {
+    if (!workspace) return fail(SDV_ERR_WORKSPACE, "workspace of %zu bytes required, got null", need);
+    if (workspace_bytes < need)
+      return fail(SDV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(SDV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  return SDV_OK;
+}
+
+void split_workspace(void* workspace, int64_t rows_cap, int32_t num_q_heads, int32_t head_dim,
+                     int32_t num_splits, float** part_o, float** part_lse) {
+  if (num_splits <= 1) {
+    *part_o = nullptr;
+    *part_lse = nullptr;
+    return;
+  }
+  const size_t o_bytes = align256(static_cast<size_t>(num_splits) * rows_cap * num_q_heads *
+                                  head_dim * sizeof(float));
+  *part_o = reinterpret_cast<float*>(workspace);
+  *part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdv_workspace_bytes(int32_t q_rows_cap, int32_t num_q_heads, int32_t head_dim,
+                           int32_t num_splits) {
+  if (num_splits <= 1 || q_rows_cap <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const size_t units = static_cast<size_t>(num_splits) * q_rows_cap * num_q_heads;
+  return align256(units * head_dim * sizeof(float)) + align256(units * sizeof(float));
+}
+
+const char* sdv_status_string(int32_t status) {
+  switch (status) {
+    case SDV_OK: return "ok";
+    case SDV_ERR_NULL_POINTER: return "null pointer";
+    case SDV_ERR_DTYPE: return "unsupported dtype";
+    case SDV_ERR_GEOMETRY: return "unsupported geometry (native P128 draft view unavailable)";
+    case SDV_ERR_SHAPE: return "bad shape";
+    case SDV_ERR_WORKSPACE: return "workspace too small";
+    case SDV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* sdv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sdv_set_kernel_family(int32_t family) { return g_family.exchange(family ? 1 : 0); }
+
+int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_table,
+                             int32_t B, int32_t max_blocks, int32_t bt_stride,
+                             int32_t* sub_offsets, sdv_subpage_view* view_out,
+                             int32_t* dev_err, hipStream_t stream) {
+  if (!geom || !view_out) return fail(SDV_ERR_NULL_POINTER, "geom and view_out must be non-null");
+  const sdv_subpage_geom& g = *geom;
+  const char* why = nullptr;
+  char buf[160];
+  if (g.phys_page != SDV_PHYS_PAGE) {
+    snprintf(buf, sizeof buf, "physical page is %d tokens, the view needs 128", g.phys_page);
+    why = buf;
+  } else if (g.sub_page != SDV_SUB_PAGE) {
+    snprintf(buf, sizeof buf, "sub-page is %d tokens, the view needs 32", g.sub_page);
+    why = buf;
+  } else if (g.num_layers != 1) {
+    snprintf(buf, sizeof buf, "view spans %d layers, it must be single-layer", g.num_layers);
+    why = buf;
+  } else if (g.kv_offset != 1) {
+    snprintf(buf, sizeof buf, "kv_offset is %d, V must be the page after K (1)", g.kv_offset);
+    why = buf;
+  } else if (g.slot_stride < 2) {
+    snprintf(buf, sizeof buf, "slot stride %d cannot hold a K and a V page", g.slot_stride);
+    why = buf;
+  } else if (g.num_kv_heads < 1) {
+    snprintf(buf, sizeof buf, "num_kv_heads %d < 1", g.num_kv_heads);
+    why = buf;
+  } else if (!valid_head_dim(g.head_dim)) {
+    snprintf(buf, sizeof buf, "head_dim %d (supported: 64, 128)", g.head_dim);
+    why = buf;
+  } else if (g.num_slots < 1 ||
+             static_cast<int64_t>(g.num_slots) * g.slot_stride * 4 >= (1ll << 31)) {
+    snprintf(buf, sizeof buf, "num_slots %d with stride %d exceeds the 32-bit P32 index range",
+             g.num_slots, g.slot_stride);
+    why = buf;
+  }
+  if (why) return fail(SDV_ERR_GEOMETRY, "native P128 draft view unavailable: %s", why);
+  if (!valid_dtype(g.kv_dtype)) return fail(SDV_ERR_DTYPE, "kv_dtype %d", g.kv_dtype);
+  if (!valid_scale(g.k_scale) || !valid_scale(g.v_scale))
+    return fail(SDV_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  if (!g.k_root) return fail(SDV_ERR_NULL_POINTER, "k_root must be non-null");
+  if (reinterpret_cast<uintptr_t>(g.k_root) % 16 != 0)
+    return fail(SDV_ERR_GEOMETRY, "native P128 draft view unavailable: k_root not 16-byte aligned");
+  if (B < 0 || max_blocks < 0 || bt_stride < max_blocks)
+    return fail(SDV_ERR_SHAPE, "B %d, max_blocks %d, bt_stride %d", B, max_blocks, bt_stride);
+  if (B > 0 && max_blocks > 0 && (!block_table || !sub_offsets))
+    return fail(SDV_ERR_NULL_POINTER, "block_table and sub_offsets must be non-null");
+
+  view_out->k_root = g.k_root;
+  view_out->kv_dtype = g.kv_dtype;
+  view_out->num_kv_heads = g.num_kv_heads;
+  view_out->head_dim = g.head_dim;
+  view_out->index_scale = g.slot_stride;
+  view_out->num_slots = g.num_slots;
+  view_out->k_scale = g.k_scale;
+  view_out->v_scale = g.v_scale;
+  // P32 pages from the root up to and including the last slot's V page.
+  view_out->num_sub_pages = 4ll * ((static_cast<int64_t>(g.num_slots) - 1) * g.slot_stride + 2);
+  if (B == 0 || max_blocks == 0) return ok();
+  return hip_status(sdv::launch_subpage_offsets(block_table, B, max_blocks, bt_stride,
+                                                g.slot_stride, g.num_slots, sub_offsets,
+                                                dev_err, stream),
+                    "kv_subpage_view_init launch");
+}
+
+int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_subpage_view* view,
+                               const int32_t* sub_offsets, int32_t max_sub_pages,
+                               float softmax_scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* out, int32_t out_dt,
+                               int32_t* dev_err, hipStream_t stream) {
+  if (!view) return fail(SDV_ERR_NULL_POINTER, "view must be non-null");
+  const sdv_subpage_view& v = *view;
+  int32_t st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, v.num_kv_heads);
+  if (st) return st;
+  if (!attn_dtype_pair(q_dt, v.kv_dtype))
+    return fail(SDV_ERR_DTYPE, "q dtype %d with kv dtype %d", q_dt, v.kv_dtype);
+  if (!valid_out_dtype(out_dt)) return fail(SDV_ERR_DTYPE, "out dtype %d", out_dt);
+  if (!valid_head_dim(v.head_dim)) return fail(SDV_ERR_SHAPE, "head_dim %d", v.head_dim);
+  const int32_t G = num_q_heads / v.num_kv_heads;
+  if (static_cast<int64_t>(G) * max_qo_len > 64)
+    return fail(SDV_ERR_SHAPE, "group %d x max_qo_len %d exceeds 64 query rows", G, max_qo_len);
+  if (max_sub_pages < 1) return fail(SDV_ERR_SHAPE, "max_sub_pages %d < 1", max_sub_pages);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (!valid_scale(v.k_scale) || !valid_scale(v.v_scale) || !v.k_root || v.num_sub_pages < 8)
+    return fail(SDV_ERR_GEOMETRY, "native P128 draft view unavailable: view not initialised");
+  const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
+  if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
+  st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, v.head_dim, num_splits);
+  if (st) return st;
+  if (B > 0 && (!sub_offsets || !out))
+    return fail(SDV_ERR_NULL_POINTER, "sub_offsets and out must be non-null");
+  if (B == 0) return ok();
+
+  sdv::AttnArgs a{};
+  a.q = q; a.q_dt = q_dt; a.qo_indptr = qo_indptr; a.kv_len = kv_len; a.B = B;
+  a.max_qo_len = max_qo_len; a.num_q_heads = num_q_heads; a.num_kv_heads = v.num_kv_heads;
+  a.head_dim = v.head_dim; a.kv_dt = v.kv_dtype; a.k_scale = v.k_scale; a.v_scale = v.v_scale;
+  a.softmax_scale = softmax_scale; a.num_splits = num_splits; a.out = out; a.out_dt = out_dt;
+  a.dev_err = dev_err;
+  split_workspace(workspace, rows_cap, num_q_heads, v.head_dim, num_splits, &a.part_o, &a.part_lse);
+  sdv::DenseSource src{v.k_root, sub_offsets, max_sub_pages, v.num_sub_pages};
+  hipError_t e = (g_family.load() == 0 && sdv::mfma_supported(a))
+                     ? sdv::launch_attn_dense_mfma(a, src, stream)
+                     : sdv::launch_attn_dense_valu(a, src, stream);
+  if (e != hipSuccess) return hip_status(e, "verify_attention_dense launch");
+  if (num_splits > 1) {
+    e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
+                            qo_indptr, qo_indptr + B, num_q_heads, v.head_dim, out, out_dt,
+                            nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, "verify_attention_dense combine launch");
+  }
+  return ok();
+}
+
+static int32_t check_paged_kv(const sdv_paged_kv* kv) {
+  if (!kv) return fail(SDV_ERR_NULL_POINTER, "kv must be non-null");
+  if (kv->page_size != SDV_PHYS_PAGE)
+    return fail(SDV_ERR_GEOMETRY, "page_size %d (supported: 128)", kv->page_size);
+  if (kv->num_kv_heads < 1) return fail(SDV_ERR_SHAPE, "num_kv_heads %d", kv->num_kv_heads);
+  if (!valid_head_dim(kv->head_dim)) return fail(SDV_ERR_SHAPE, "head_dim %d", kv->head_dim);
+  if (!valid_dtype(kv->kv_dtype)) return fail(SDV_ERR_DTYPE, "kv dtype %d", kv->kv_dtype);
+  if (kv->num_pages < 1) return fail(SDV_ERR_SHAPE, "num_pages %d", kv->num_pages);
+  if (kv->page_stride < static_cast<int64_t>(kv->num_kv_heads) * SDV_PHYS_PAGE * kv->head_dim)
+    return fail(SDV_ERR_SHAPE, "page_stride %lld smaller than one page",
+                static_cast<long long>(kv->page_stride));
+  const int eb = kv->kv_dtype == SDV_F32 ? 4 : (kv->kv_dtype == SDV_BF16 ? 2 : 1);
+  if ((kv->page_stride * eb) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "page stride must be a multiple of 16 bytes");
+  if (!kv->k || !kv->v) return fail(SDV_ERR_NULL_POINTER, "kv.k and kv.v must be non-null");
+  if ((reinterpret_cast<uintptr_t>(kv->k) | reinterpret_cast<uintptr_t>(kv->v)) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "K and V pools must be 16-byte aligned");
+  if (!valid_scale(kv->k_scale) || !valid_scale(kv->v_scale))
+    return fail(SDV_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  return SDV_OK;
+}
+
+int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                          const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                          int32_t num_q_heads, const sdv_paged_kv* kv,
+                          const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                          float* scores, int32_t* dev_err, hipStream_t stream) {
+  int32_t st = check_paged_kv(kv);
+  if (st) return st;
+  st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv->num_kv_heads);
+  if (st) return st;
+  if (q_dt != SDV_F32 && q_dt != SDV_BF16) return fail(SDV_ERR_DTYPE, "q dtype %d", q_dt);
+  const int32_t G = num_q_heads / kv->num_kv_heads;
+  if (static_cast<int64_t>(max_qo_len) * G * kv->head_dim > 16384)
+    return fail(SDV_ERR_SHAPE, "max_qo_len x group x head_dim exceeds 16384");
+  if (max_pages < 1 || bt_stride < max_pages)
+    return fail(SDV_ERR_SHAPE, "max_pages %d, bt_stride %d", max_pages, bt_stride);
+  if (B > 0 && (!block_table || !scores))
+    return fail(SDV_ERR_NULL_POINTER, "block_table and scores must be non-null");
+  if (B == 0) return ok();
+  return hip_status(sdv::launch_proxy_scores(q, q_dt, qo_indptr, kv_len, B, max_qo_len,
+                                             num_q_heads, *kv, block_table, max_pages, bt_stride,
+                                             scores, dev_err, stream),
+                    "proxy_page_scores launch");
+}
+
+int32_t ladder_topk_pages(const float* scores, const int32_t* qo_indptr, const int32_t* kv_len,
+                          int32_t B, int32_t max_qo_len, int32_t num_kv_heads, int32_t max_pages,
+                          int32_t page_size, int32_t top_k, int32_t* topk_idx,
+                          int32_t* topk_cnt, int32_t* dev_err, hipStream_t stream) {
+  if (page_size != SDV_PHYS_PAGE)
+    return fail(SDV_ERR_GEOMETRY, "page_size %d (supported: 128)", page_size);
+  if (B < 0 || max_qo_len < 1 || num_kv_heads < 1)
+    return fail(SDV_ERR_SHAPE, "B %d, max_qo_len %d, num_kv_heads %d", B, max_qo_len, num_kv_heads);
+  if (top_k < 1 || top_k > 1024) return fail(SDV_ERR_SHAPE, "top_k %d outside [1, 1024]", top_k);
+  if (max_pages < 1 || max_pages > 4096)
+    return fail(SDV_ERR_SHAPE, "max_pages %d outside [1, 4096]", max_pages);
+  if (B > 0 && (!scores || !qo_indptr || !kv_len || !topk_idx))
+    return fail(SDV_ERR_NULL_POINTER, "scores, qo_indptr, kv_len and topk_idx must be non-null");
+  if (B == 0) return ok();
+  return hip_status(sdv::launch_topk(scores, qo_indptr, kv_len, B, max_qo_len, num_kv_heads,
+                                     max_pages, top_k, topk_idx, topk_cnt, dev_err, stream),
+                    "ladder_topk_pages launch");
+}
+
+int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                int32_t num_q_heads, const sdv_paged_kv* kv,
+                                const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                                const int32_t* topk_idx, int32_t top_k, float softmax_scale,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                void* out, int32_t out_dt, int32_t* dev_err,
+                                hipStream_t stream) {
+  int32_t st = check_paged_kv(kv);
+  if (st) return st;
+  st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv->num_kv_heads);
+  if (st) return st;
+  if (!attn_dtype_pair(q_dt, kv->kv_dtype))
+    return fail(SDV_ERR_DTYPE, "q dtype %d with kv dtype %d", q_dt, kv->kv_dtype);
+  if (!valid_out_dtype(out_dt)) return fail(SDV_ERR_DTYPE, "out dtype %d", out_dt);
+  const int32_t G = num_q_heads / kv->num_kv_heads;
+  if (static_cast<int64_t>(G) * max_qo_len > 64)
+    return fail(SDV_ERR_SHAPE, "group %d x max_qo_len %d exceeds 64 query rows", G, max_qo_len);
+  if (max_qo_len > 32) return fail(SDV_ERR_SHAPE, "max_qo_len %d > 32", max_qo_len);
+  if (top_k < 1 || static_cast<int64_t>(top_k) * max_qo_len > 512)
+    return fail(SDV_ERR_SHAPE, "top_k %d x max_qo_len %d outside [1, 512]", top_k, max_qo_len);
+  if (max_pages < 1 || max_pages > 16384 || bt_stride < max_pages)
+    return fail(SDV_ERR_SHAPE, "max_pages %d (<= 16384), bt_stride %d", max_pages, bt_stride);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
+  if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
+  st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, kv->head_dim, num_splits);
+  if (st) return st;
+  if (B > 0 && (!block_table || !topk_idx || !out))
+    return fail(SDV_ERR_NULL_POINTER, "block_table, topk_idx and out must be non-null");
+  if (B == 0) return ok();
+
+  sdv::AttnArgs a{};
+  a.q = q; a.q_dt = q_dt; a.qo_indptr = qo_indptr; a.kv_len = kv_len; a.B = B;
+  a.max_qo_len = max_qo_len; a.num_q_heads = num_q_heads; a.num_kv_heads = kv->num_kv_heads;
+  a.head_dim = kv->head_dim; a.kv_dt = kv->kv_dtype; a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale; a.softmax_scale = softmax_scale; a.num_splits = num_splits;
+  a.out = out; a.out_dt = out_dt; a.dev_err = dev_err;
+  split_workspace(workspace, rows_cap, num_q_heads, kv->head_dim, num_splits, &a.part_o, &a.part_lse);
+  sdv::SparseSource src{kv->k, kv->v, kv->page_stride, kv->num_pages, block_table, bt_stride,
+                        max_pages, topk_idx, top_k};
+  hipError_t e = (g_family.load() == 0 && sdv::mfma_supported(a))
+                     ? sdv::launch_attn_sparse_mfma(a, src, stream)
+                     : sdv::launch_attn_sparse_valu(a, src, stream);
+  if (e != hipSuccess) return hip_status(e, "verify_attention_sparse launch");
+  if (num_splits > 1) {
+    e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
+                            qo_indptr, qo_indptr + B, num_q_heads, kv->head_dim, out, out_dt,
+                            nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, "verify_attention_sparse combine launch");
+  }
+  return ok();
+}
+
+int32_t lse_combine(const float* partial_out, const float* partial_lse, int32_t num_splits,
+                    int32_t num_rows, int32_t num_heads, int32_t head_dim, void* out,
+                    int32_t out_dt, float* lse_out, hipStream_t stream) {
+  if (num_splits < 1 || num_rows < 0 || num_heads < 1)
+    return fail(SDV_ERR_SHAPE, "num_splits %d, num_rows %d, num_heads %d", num_splits, num_rows,
+                num_heads);
+  if (!valid_head_dim(head_dim)) return fail(SDV_ERR_SHAPE, "head_dim %d", head_dim);
+  if (!valid_out_dtype(out_dt)) return fail(SDV_ERR_DTYPE, "out dtype %d", out_dt);
+  if (num_rows > 0 && (!partial_out || !partial_lse || !out))
+    return fail(SDV_ERR_NULL_POINTER, "partial_out, partial_lse and out must be non-null");
+  if (num_rows == 0) return ok();
+  return hip_status(sdv::launch_combine(partial_out, partial_lse, num_splits, num_rows, nullptr,
+                                        nullptr, num_heads, head_dim, out, out_dt, lse_out,
+                                        stream),
+                    "lse_combine launch");
+}
+
+int32_t sdv_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t stream) {
+  if (bytes == 0) return ok();
+  if (!dst) return fail(SDV_ERR_NULL_POINTER, "dst must be non-null");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "fill needs 16-byte aligned size and address");
+  return hip_status(sdv::launch_fill_u32(dst, bytes, pattern, stream), "sdv_fill_u32 launch");
+}
+
+}  // extern "C"
