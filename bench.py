@@ -1,0 +1,315 @@
+"""Benchmark of the verify path on one MI355X.
+
+A step is one pass of the block-sparse target-layer verify path over one batch:
+proxy page scores -> ladder top-k -> sparse verify attention (+ split-KV combine),
+on the sparse bf16 workload (batch 64, qo_len 4, 16/4 heads, head_dim 128, kv_len
+uniform in [4096, 32768], top-k 16).  Inputs are generated on the GPU from a seed and
+are resident in HBM before timing starts.  The dense draft-layer path (P32 view
+offsets + dense verify attention, batch 32, qo_len 4, 64/4 heads, kv_len uniform in
+[1024, 8192]) is timed in the same run and reported under "dense".
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on the
+launch stream around every kernel inside the timed loop.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify tokens/sec + achieved HBM GB/s (% of peak), sparse paged GQA qo_len=4"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--splits", type=int, default=None, help="override sparse num_splits")
+    p.add_argument("--dense-splits", type=int, default=None)
+    p.add_argument("--family", type=int, default=0, help="0 auto, 1 vector-ALU kernels")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle sample")
+    return p.parse_args()
+
+
+def sparse_algorithmic_bytes(case, idx_np):
+    """Bytes each sparse-path kernel must move (no re-reads, no partials)."""
+    w = case.w
+    e = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    eq = {"f32": 4, "bf16": 2}[w.q_dtype]
+    d, Hq, Hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
+    qo, kv = case.lengths.qo, case.lengths.kv
+    ind = case.lengths.qo_indptr
+    rows = int(qo.sum())
+    q_bytes = rows * Hq * d * eq
+    n_pages = -(-kv // 128)
+    # proxy: every valid K row once, Q, the block table, the written scores
+    proxy = int(kv.sum()) * Hkv * d * e + q_bytes + int(n_pages.sum()) * 4 + \
+        int((qo * n_pages).sum()) * Hkv * 4
+    # top-k: valid score entries read, indices written
+    nv_sum = 0
+    for r in range(len(kv)):
+        b = kv[r] - qo[r] + np.arange(qo[r]) + 1
+        nv_sum += int((-(-b // 128)).sum())
+    topk = nv_sum * Hkv * 4 + rows * Hkv * w.top_k * 4
+    # sparse: valid K and V rows of the distinct pages any token of (r, h) selected
+    kv_rows = 0
+    for r in range(len(kv)):
+        sel = idx_np[ind[r]:ind[r + 1]]                      # [qo, Hkv, K]
+        for h in range(Hkv):
+            pages = np.unique(sel[:, h, :])
+            pages = pages[pages >= 0]
+            kv_rows += int(np.minimum(128, kv[r] - 128 * pages).sum())
+    sparse = kv_rows * d * e * 2 + q_bytes + rows * Hq * d * eq + rows * Hkv * w.top_k * 4 + \
+        int(n_pages.sum()) * 4
+    rowexp = 0
+    for r in range(len(kv)):
+        sel = idx_np[ind[r]:ind[r + 1]]
+        for t in range(qo[r]):
+            for h in range(Hkv):
+                pages = sel[t, h][sel[t, h] >= 0]
+                rowexp += int(np.minimum(128, kv[r] - 128 * pages).sum())
+    return {"proxy": proxy, "topk": topk, "sparse": sparse,
+            "sparse_row_expanded_kv": rowexp * d * e * 2}
+
+
+def dense_algorithmic_bytes(case):
+    w = case.w
+    e = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    eq = {"f32": 4, "bf16": 2}[w.q_dtype]
+    rows = case.lengths.total_q
+    kv = case.lengths.kv
+    return int(kv.sum()) * w.num_kv_heads * w.head_dim * e * 2 + \
+        2 * rows * w.num_q_heads * w.head_dim * eq + int((-(-kv // 32)).sum()) * 2 * 4
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "speculative_decode_verify_p128_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src_hash, launches_bytes):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_steps(step_fns, steps, warmup, torch):
+    """Runs warmup + timed steps; events around each kernel on the current stream."""
+    for _ in range(warmup):
+        for _, fn in step_fns:
+            fn()
+    torch.cuda.synchronize()
+    n = len(step_fns)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, (_, fn) in enumerate(step_fns):
+            fn()
+            ev[s][i + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    per = {}
+    for i, (name, _) in enumerate(step_fns):
+        ts = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]
+        per[name] = {"avg_us": 1e3 * float(np.mean(ts)), "min_us": 1e3 * float(np.min(ts)),
+                     "p50_us": 1e3 * float(np.median(ts))}
+    return total_ms / steps, per, wall
+
+
+def cpu_baseline(case, n_req):
+    """The oracle, untuned, on a bounded sample of the same workload, one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from workloads import raw_numpy
+    w = case.w
+    req = list(range(min(n_req, w.batch)))
+    q_raw = raw_numpy(case.q)
+    kp, vp = raw_numpy(case.k_pool), raw_numpy(case.v_pool)
+    bt = case.block_table.cpu().numpy()
+    ind = case.qo_indptr.cpu().numpy()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.sparse_verify_case(q_raw, w.q_dtype, ind, case.lengths.kv, kp, vp, w.kv_dtype, bt,
+                                  case.k_scale, case.v_scale, w.top_k, case.softmax_scale,
+                                  w.max_pages(), requests=req)
+        dt = time.perf_counter() - t0
+    toks = int(sum(case.lengths.qo[r] for r in req))
+    kvs = [int(case.lengths.kv[r]) for r in req]
+    return {"value": toks / dt, "unit": "verify tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(req)} of {w.batch} requests ({toks} verify tokens, kv_len {kvs}) "
+                      f"through proxy scores, top-k and sparse attention; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify path "
+              "here is a single-GPU kernel library with no cross-GPU step.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import speculative_decode_verify_p128_amd as sdv
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    sdv.set_kernel_family(args.family)
+
+    # ---- sparse target-layer path (the headline workload) ----
+    w = W.SPARSE_BF16
+    splits = args.splits or w.num_splits
+    c = W.make_sparse_case(w, device=dev)
+    kv = sdv.PagedKV(c.k_pool, c.v_pool, c.k_scale, c.v_scale)
+    rows_cap = w.batch * w.max_qo()
+    scores = torch.empty((rows_cap, w.num_kv_heads, w.max_pages()), dtype=torch.float32, device=dev)
+    idx = torch.empty((rows_cap, w.num_kv_heads, w.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((rows_cap, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, splits, dev)
+    mq = w.max_qo()
+
+    def k_proxy():
+        sdv.proxy_page_scores(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, max_qo_len=mq,
+                              scores=scores)
+
+    def k_topk():
+        sdv.ladder_topk_pages(scores, c.qo_indptr, c.kv_len, max_qo_len=mq, top_k=w.top_k,
+                              topk_idx=idx)
+
+    def k_sparse():
+        sdv.verify_attention_sparse(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, idx,
+                                    max_qo_len=mq, softmax_scale=c.softmax_scale,
+                                    num_splits=splits, workspace=ws, out=out)
+
+    fns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
+           ("verify_attention_sparse", k_sparse)]
+    ms, per, wall = time_steps(fns, args.steps, args.warmup, torch)
+    tokens = c.lengths.total_q
+    idx_np = idx.cpu().numpy()
+    ab = sparse_algorithmic_bytes(c, idx_np)
+    path_bytes = ab["proxy"] + ab["topk"] + ab["sparse"]
+    kern = {}
+    for name, key in (("proxy_page_scores", "proxy"), ("ladder_topk_pages", "topk"),
+                      ("verify_attention_sparse", "sparse")):
+        gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
+        kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
+                      "frac_of_peak": gbs / HBM_PEAK_GBS}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    src = {"proxy_page_scores": ("k_proxy.hip",), "ladder_topk_pages": ("k_topk.hip",),
+           "verify_attention_sparse": ("k_attn_mfma.hip", "k_attn_valu.hip", "k_small.hip")}[dom]
+    traffic = load_traffic(dom, w.name, source_hash(*src), None)
+    path_gbs = path_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "verify tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "sparse_bf16: block-sparse target-layer verify, batch 64, "
+                               "qo_len 4, 16 q / 4 kv heads, head_dim 128, kv_len U[4096, 32768], "
+                               "128-token pages, top-k 16",
+                   "batch": w.batch, "qo_len": 4, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "top_k": w.top_k,
+                   "num_splits": splits, "seed": W.seed_for(w), "verify_tokens": tokens,
+                   "kv_tokens": int(c.lengths.kv.sum())},
+        "gb_per_s": path_gbs,
+        "frac_of_peak": path_gbs / HBM_PEAK_GBS,
+        "path_algorithmic_bytes": path_bytes,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "kernels": kern,
+        "sparse_row_expanded_kv_bytes": ab["sparse_row_expanded_kv"],
+        "wall_s_timed": wall,
+    }
+    del scores, ws
+
+    # ---- dense draft-layer path ----
+    if not args.no_dense:
+        wd = W.DENSE_BF16
+        dsplits = args.dense_splits or wd.num_splits
+        d = W.make_dense_case(wd, device=dev)
+        rows_d = wd.batch * wd.max_qo()
+        outd = torch.empty((rows_d, wd.num_q_heads, wd.head_dim), dtype=torch.bfloat16, device=dev)
+        wsd = sdv.alloc_workspace(rows_d, wd.num_q_heads, wd.head_dim, dsplits, dev)
+        offs = torch.empty((wd.batch, 2, 4 * wd.max_pages()), dtype=torch.int32, device=dev)
+        holder = {}
+
+        def k_view():
+            holder["view"], _ = sdv.kv_subpage_view_init(
+                d.pool[wd.root_page], d.block_table, num_kv_heads=wd.num_kv_heads,
+                head_dim=wd.head_dim, slot_stride=wd.slot_stride, num_slots=d.num_slots,
+                pool_index_scale=wd.pool_index_scale, sub_offsets=offs)
+
+        k_view()
+
+        def k_dense():
+            sdv.verify_attention_dense(d.q, d.qo_indptr, d.kv_len, holder["view"], offs,
+                                       max_qo_len=wd.max_qo(), softmax_scale=d.softmax_scale,
+                                       num_splits=dsplits, workspace=wsd, out=outd)
+
+        msd, perd, _ = time_steps([("kv_subpage_view_init", k_view),
+                                   ("verify_attention_dense", k_dense)],
+                                  args.steps, args.warmup, torch)
+        db = dense_algorithmic_bytes(d)
+        gbs = db / (perd["verify_attention_dense"]["avg_us"] * 1e-6) / 1e9
+        result["dense"] = {
+            "workload": "dense_bf16: draft-layer verify through the P32 view, batch 32, qo_len 4, "
+                        "64 q / 4 kv heads, head_dim 128, kv_len U[1024, 8192], slot stride 8",
+            "value": d.lengths.total_q / (msd * 1e-3), "unit": "verify tokens/s",
+            "ms_per_step": msd, "num_splits": dsplits, "algorithmic_bytes": db,
+            "kernels": perd,
+            "roofline": {"bound": "hbm", "kernel": "verify_attention_dense", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": load_traffic("verify_attention_dense", wd.name,
+                                                 source_hash("k_attn_mfma.hip", "k_attn_valu.hip",
+                                                             "k_small.hip"), None)},
+        }
+        del d, outd, wsd
+
+    if not args.no_cpu_baseline:
+        c_cpu = W.SparseCase(**{**c.__dict__})
+        result["cpu_baseline"] = cpu_baseline(c_cpu, args.cpu_sample)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -16,13 +16,12 @@
 // query scale.
 #include "device.h"
 #include "internal.h"
+#include "sparse_union.h"
 
 namespace sdv {
 
 constexpr int kMaxRows = 64;
 constexpr int kTile = 16;
-constexpr int kMaxUnion = 512;
-constexpr int kMaxWords = 512;   // max_pages <= 16384
 
 template <int D>
 struct ValuSmem {
@@ -33,81 +32,8 @@ struct ValuSmem {
   float row_m[kMaxRows];
   float row_l[kMaxRows];
   float row_a[kMaxRows];
-  uint32_t bitmap[kMaxWords];
-  int32_t word_prefix[kMaxWords];
-  int32_t upage[kMaxUnion];
-  int32_t umask[kMaxUnion];
-  int32_t scan[256];
-  int32_t bad;
-  int32_t n_union;
+  UnionLds u;
 };
-
-// Builds the sorted union of the pages the request's tokens selected for KV head h,
-// with a bit mask of the selecting tokens per page.  Returns the union size.
-template <int D>
-__device__ int build_union(ValuSmem<D>& sm, const SparseSource& ss, int r, int h, int Hkv,
-                           int row0, int qo, int kv, int32_t* dev_err) {
-  const int tid = threadIdx.x;
-  const int words = (ss.max_pages + 31) / 32;
-  for (int w = tid; w < words; w += blockDim.x) sm.bitmap[w] = 0u;
-  if (tid == 0) sm.bad = 0;
-  __syncthreads();
-  const int n_el = qo * ss.top_k;
-  for (int e = tid; e < n_el; e += blockDim.x) {
-    const int t = e / ss.top_k;
-    const int k = e - t * ss.top_k;
-    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
-    if (p < 0) continue;
-    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
-    if (p >= nvalid) {
-      set_err(dev_err, SDV_DEVERR_TOPK_INDEX);
-      continue;
-    }
-    atomicOr(&sm.bitmap[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
-  // exclusive prefix of popcounts over words: each thread owns two words
-  const int w0 = 2 * tid;
-  int c0 = (w0 < words) ? __popc(sm.bitmap[w0]) : 0;
-  int c1 = (w0 + 1 < words) ? __popc(sm.bitmap[w0 + 1]) : 0;
-  sm.scan[tid] = c0 + c1;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = tid >= off ? sm.scan[tid - off] : 0;
-    __syncthreads();
-    sm.scan[tid] += v;
-    __syncthreads();
-  }
-  const int excl = sm.scan[tid] - (c0 + c1);
-  if (w0 < words) sm.word_prefix[w0] = excl;
-  if (w0 + 1 < words) sm.word_prefix[w0 + 1] = excl + c0;
-  const int total = sm.scan[255];
-  __syncthreads();
-  for (int w = tid; w < words; w += blockDim.x) {
-    uint32_t bits = sm.bitmap[w];
-    int idx = sm.word_prefix[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      sm.upage[idx] = w * 32 + b;
-      sm.umask[idx] = 0;
-      ++idx;
-      bits &= bits - 1;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < n_el; e += blockDim.x) {
-    const int t = e / ss.top_k;
-    const int k = e - t * ss.top_k;
-    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
-    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
-    if (p < 0 || p >= nvalid) continue;
-    const int w = p >> 5;
-    const int idx = sm.word_prefix[w] + __popc(sm.bitmap[w] & ((1u << (p & 31)) - 1u));
-    atomicOr(&sm.umask[idx], 1 << t);
-  }
-  __syncthreads();
-  return total;
-}
 
 template <int D, bool SPARSE>
 __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSource ds,
@@ -154,7 +80,7 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
   int blk_lo, blk_hi;     // dense: sub-pages; sparse: union entries (each 4 blocks)
   int n_union = 0;
   if constexpr (SPARSE) {
-    n_union = build_union<D>(sm, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
+    n_union = build_union(sm.u, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
     const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
     blk_lo = split * chunk;
     blk_hi = min(n_union, blk_lo + chunk);
@@ -179,8 +105,8 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
     int pos_base;
     bool ok = true;
     if constexpr (SPARSE) {
-      const int p = sm.upage[item];
-      mask = sm.umask[item];
+      const int p = sm.u.upage[item];
+      mask = sm.u.umask[item];
       const int phys = ss.block_table[static_cast<int64_t>(r) * ss.bt_stride + p];
       if (phys < 0 || phys >= ss.num_pages) ok = false;
       kb = ss.k;

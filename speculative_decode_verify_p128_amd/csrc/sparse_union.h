@@ -1,0 +1,91 @@
+// Union of the pages a request's verify tokens selected for one KV head, built in LDS
+// by a 256-thread workgroup.
+//
+// Each (request, KV head) reads every page that any of its tokens selected once; a
+// per-page bit mask records which tokens selected it, and each token's rows attend
+// only the pages whose bit is set (plus its ladder bound).  The list is sorted by
+// request-local page number, which makes split-KV partitioning deterministic.
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+namespace sdv {
+
+constexpr int kMaxUnion = 512;   // max_qo_len * top_k
+constexpr int kMaxWords = 512;   // max_pages <= 16384
+
+struct UnionLds {
+  uint32_t bitmap[kMaxWords];
+  int32_t word_prefix[kMaxWords];
+  int32_t upage[kMaxUnion];
+  int32_t umask[kMaxUnion];
+  int32_t scan[256];
+};
+
+// All 256 threads must call.  Returns the number of distinct selected pages; flags
+// (and ignores) indices at or beyond a token's valid-page count.
+__device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, int h, int Hkv,
+                                  int row0, int qo, int kv, int32_t* dev_err) {
+  const int tid = threadIdx.x;
+  const int words = (ss.max_pages + 31) / 32;
+  for (int w = tid; w < words; w += 256) u.bitmap[w] = 0u;
+  __syncthreads();
+  const int n_el = qo * ss.top_k;
+  for (int e = tid; e < n_el; e += 256) {
+    const int t = e / ss.top_k;
+    const int k = e - t * ss.top_k;
+    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+    if (p < 0) continue;
+    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
+    if (p >= nvalid) {
+      set_err(dev_err, SDV_DEVERR_TOPK_INDEX);
+      continue;
+    }
+    atomicOr(&u.bitmap[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // exclusive prefix of per-word popcounts; each thread owns two consecutive words
+  const int w0 = 2 * tid;
+  const int c0 = (w0 < words) ? __popc(u.bitmap[w0]) : 0;
+  const int c1 = (w0 + 1 < words) ? __popc(u.bitmap[w0 + 1]) : 0;
+  u.scan[tid] = c0 + c1;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? u.scan[tid - off] : 0;
+    __syncthreads();
+    u.scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = u.scan[tid] - (c0 + c1);
+  if (w0 < words) u.word_prefix[w0] = excl;
+  if (w0 + 1 < words) u.word_prefix[w0 + 1] = excl + c0;
+  const int total = u.scan[255];
+  __syncthreads();
+  for (int w = tid; w < words; w += 256) {
+    uint32_t bits = u.bitmap[w];
+    int idx = u.word_prefix[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      u.upage[idx] = w * 32 + b;
+      u.umask[idx] = 0;
+      ++idx;
+      bits &= bits - 1;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < n_el; e += 256) {
+    const int t = e / ss.top_k;
+    const int k = e - t * ss.top_k;
+    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
+    if (p < 0 || p >= nvalid) continue;
+    const int w = p >> 5;
+    const int idx = u.word_prefix[w] + __popc(u.bitmap[w] & ((1u << (p & 31)) - 1u));
+    atomicOr(&u.umask[idx], 1 << t);
+  }
+  __syncthreads();
+  return total;
+}
+
+}  // namespace sdv
