@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a 1 GiB device copy (for memory-counter calibration)")
+    p.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     return p.parse_args()
 
 
@@ -165,8 +168,40 @@ def cpu_baseline(case, n_req):
     toks = int(sum(case.lengths.qo[r] for r in req))
     kvs = [int(case.lengths.kv[r]) for r in req]
     return {"value": toks / dt, "unit": "verify tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(req)} of {w.batch} requests ({toks} verify tokens, kv_len {kvs}) "
-                      f"through proxy scores, top-k and sparse attention; {dt:.1f} s"}
+            "sample": f"{len(req)} of {w.batch} requests ({toks} verify tokens, {sum(kvs)} kv "
+                      f"tokens, kv_len {min(kvs)}..{max(kvs)}) through proxy scores, top-k and "
+                      f"sparse attention, one thread; {dt:.1f} s"}
+
+
+def attainable_read_gbs(torch, sdv, dev, gib=4):
+    """Best rate of the streaming-read probe over a buffer far larger than the caches."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+        sdv.read_probe(buf, sink, blocks)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(5):
+            sdv.read_probe(buf, sink, blocks)
+        e.record()
+        torch.cuda.synchronize()
+        best = max(best, 5 * buf.numel() / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def calibrate_copy(torch, mib=1024, reps=3):
+    """A plain device copy of known size, for scaling the memory counters."""
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": mib << 20, "copy_bytes_written": mib << 20,
+                      "reps": reps}))
 
 
 def main():
@@ -182,6 +217,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     sdv.set_kernel_family(args.family)
 
     # ---- sparse target-layer path (the headline workload) ----
@@ -303,6 +341,8 @@ def main():
         }
         del d, outd, wsd
 
+    if not args.no_probe:
+        result["attainable_read_GB_s"] = attainable_read_gbs(torch, sdv, dev)
     if not args.no_cpu_baseline:
         c_cpu = W.SparseCase(**{**c.__dict__})
         result["cpu_baseline"] = cpu_baseline(c_cpu, args.cpu_sample)

@@ -215,7 +215,7 @@ typedef struct sdv_paged_kv {
  *         p < ceil(kv_len[r] / 128) of each request are written, others untouched.
  * block_table device int32 [B][bt_stride], request-local page p -> physical page.
  * Supported: q F32 or BF16; K F32, BF16 or FP8; head_dim 64 or 128;
- * max_qo_len * G * head_dim <= 16384.
+ * max_qo_len * G * head_dim <= 8192.
  */
 int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                           const int32_t* kv_len, int32_t B, int32_t max_qo_len,
@@ -285,13 +285,22 @@ const char* sdv_status_string(int32_t status);
 /* Message of the calling thread's most recent failed call ("" if none). */
 const char* sdv_last_error(void);
 
-/* Kernel family selection, for cross-checking: 0 = automatic (matrix-core kernels
- * where supported), 1 = force the vector-ALU kernels.  Returns the previous value. */
+/* Kernel family selection, for cross-checking: 0 = automatic (matrix-core kernels fed
+ * by the LDS block ring where supported), 1 = the vector-ALU kernels, 2 = the
+ * matrix-core kernels that stream K/V through registers.  Process-wide; returns the
+ * previous value. */
 int32_t sdv_set_kernel_family(int32_t family);
 
 /* Measurement helper: fill `bytes` (multiple of 16) of device memory with a 32-bit
  * pattern — used to evict caches between timed runs. */
 int32_t sdv_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t stream);
+
+/* Measurement helper: read `bytes` (multiple of 16) of device memory once with 16-byte
+ * loads using `blocks` workgroups of 256 threads; sink (device, >= blocks words) gets
+ * an XOR fold so the reads are kept.  Its rate is the attainable streaming-read
+ * bandwidth that the HBM-bound kernels are compared with. */
+int32_t sdv_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -77,6 +77,7 @@ SIGNATURES = {
     "sdv_last_error": (C.c_char_p, []),
     "sdv_set_kernel_family": (_I, [_I]),
     "sdv_fill_u32": (_I, [_P, _S, C.c_uint32, _P]),
+    "sdv_read_probe": (_I, [_P, _S, _P, _I, _P]),
 }
 
 _lib = None

@@ -226,10 +226,17 @@ def lse_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, *, out_dty
 
 
 def set_kernel_family(family: int) -> int:
-    """0 = automatic (matrix-core kernels where supported), 1 = vector-ALU kernels."""
+    """0 = automatic (LDS-ring matrix-core kernels), 1 = vector-ALU kernels,
+    2 = register-streaming matrix-core kernels."""
     return int(L.load().sdv_set_kernel_family(family))
 
 
 def fill_u32(dst: torch.Tensor, pattern: int = 0) -> None:
     L.check(L.load().sdv_fill_u32(_ptr(dst), dst.numel() * dst.element_size(), pattern,
                                   _stream(dst.device)))
+
+
+def read_probe(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
+    """Streaming read of all of src (measurement helper); sink: int32 [>= blocks]."""
+    L.check(L.load().sdv_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                    blocks, _stream(src.device)))

@@ -76,6 +76,12 @@ bool mfma_supported(const AttnArgs& a);
 hipError_t launch_attn_dense_mfma(const AttnArgs& a, const DenseSource& src, hipStream_t s);
 hipError_t launch_attn_sparse_mfma(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 
+// Matrix-core attention with an LDS block ring fed by asynchronous global->LDS copies
+// (same support as the kernels above; dense needs at most 1024 blocks per split).
+constexpr int kStreamMaxDenseBlocks = 1024;
+hipError_t launch_attn_dense_stream(const AttnArgs& a, const DenseSource& src, hipStream_t s);
+hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+
 // Rows [*row_begin_dev, *row_end_dev) are combined (all rows_cap rows when null).
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t num_splits,
                           int32_t rows_cap, const int32_t* row_begin_dev,
@@ -83,5 +89,7 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t nu
                           void* out, int32_t out_dt, float* lse_out, hipStream_t s);
 
 hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                             hipStream_t s);
 
 }  // namespace sdv

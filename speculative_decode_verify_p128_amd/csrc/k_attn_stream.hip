@@ -1,0 +1,546 @@
+// Verify attention on the CDNA4 matrix cores with an LDS block ring (bf16 queries;
+// bf16 or fp8 K/V).
+//
+// What is computed: token t of request r, query head hq of KV head h attends the
+// positions j < bound(r,t) = kv_len - qo_len + t + 1 ("[TRTLLM-14093][feat] Eagle3
+// for M3 MSA path + CUDA graphs compatibility", MSA verify commit); dense keys come
+// through the P32 sub-page view of the draft layer's P128 pages ("[None][perf]
+// Default Minimax-m3 to unified draft-target kv manager ...", Description and item 2
+// Grouped-HND), sparse keys only from the pages the token selected.  Float32
+// accumulation; probabilities enter the value product as bf16.
+//
+// Work layout (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
+//   * One workgroup (4 waves) per (request, KV head, split).  Its query rows are the
+//     G x qo (token, head) pairs, row = t * G + g, in RT tiles of 16 (RT = 1, 2, 4).
+//     Wave w owns row tile w % RT and the output channel part w / RT of 4 / RT parts,
+//     so every wave works on every 32-token block of the split: with 64 rows the waves
+//     split the rows, with 16 rows they split the value product's output channels
+//     (and compute the same scores).
+//   * Each 32-token K/V block is copied once from HBM into an LDS ring by the
+//     asynchronous global->LDS loads (global_load_lds_dwordx4): each wave instruction
+//     reads one contiguous KiB of K or V.  STAGES - 1 blocks are in flight while one is
+//     computed; no registers hold in-flight data.  The 16-byte chunks of a row land
+//     XOR-swizzled by the row number, so the MFMA operand reads (16 rows, same column)
+//     and the value reads (one row, all columns) are free of LDS bank conflicts.
+//   * Scores are computed transposed, S^T = K Q^T (K the A operand, Q^T the B operand
+//     held in registers); lane l then holds query row l % 16 for tokens 4(l/16)..+3 of
+//     each 16-token tile — the B-operand layout of O^T = V^T P^T — so the probabilities
+//     feed the value product with no data exchange, and each query row's online-softmax
+//     rescale is a per-lane multiply.  Channels within a 32-channel step are permuted
+//     (lane group q takes channels q*d/4 .. q*d/4 + d/4 - 1 across the steps), the same
+//     for K and Q, which leaves the dot products unchanged.
+//   * Output goes through LDS to coalesced stores: the final rows, or a normalised
+//     partial with its log-sum-exp for the split-KV combine.
+#include <type_traits>
+
+#include "device.h"
+#include "internal.h"
+#include "sparse_union.h"
+
+namespace sdv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kRescaleLog2 = 8.f;
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Workgroup barrier for the block ring without a memory fence.  __syncthreads() also
+// releases all of the wave's outstanding memory operations, which would drain every
+// asynchronous copy in flight; here the waits are explicit (vmcnt for the copies of the
+// block about to be read, lgkmcnt for the reads of a slot about to be refilled) and
+// only the compiler is kept from moving LDS accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Geometry of one 32-token block of one head in LDS.
+template <int D, int KDT>
+struct Geo {
+  static constexpr int EB = elem_bytes<KDT>();
+  static constexpr int ROWB = D * EB;               // bytes per token row
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;              // rows per wave load instruction
+  static constexpr int HALF = 32 * ROWB;            // K (or V) bytes of one block
+  static constexpr int BLOCK = 2 * HALF;            // K then V
+  static constexpr int LPT = (2 * 32 / RPI) / 4;    // load instructions per wave per block
+  static constexpr int STEPS = D / 32;              // 32-channel MFMA steps
+  static constexpr int NT = D / 16;                 // 16-channel output tiles
+  static_assert(LPT >= 1, "block too small for four waves");
+  // byte offset in a block's K or V half of (row, byte-in-row)
+  __device__ static __forceinline__ int at(int row, int byte) {
+    const int chunk = byte >> 4;
+    return row * ROWB + (((chunk ^ row) & (CPR - 1)) << 4) + (byte & 15);
+  }
+};
+
+// Each wave issues LPT asynchronous loads that together copy one block (K then V) into
+// the ring slot; lane l of instruction n lands at slot + (n * 64 + l) * 16.
+template <int D, int KDT>
+__device__ __forceinline__ void issue_block(const char* kp, const char* vp, char* slot, int wave,
+                                            int lane) {
+  using Gm = Geo<D, KDT>;
+#pragma unroll
+  for (int n = 0; n < Gm::LPT; ++n) {
+    const int ins = wave * Gm::LPT + n;                 // 0 .. 2 * 32 / RPI - 1
+    const int half = ins / (32 / Gm::RPI);              // 0 = K, 1 = V
+    const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
+    const int lchunk = lane % Gm::CPR;
+    const int gchunk = (lchunk ^ row) & (Gm::CPR - 1);
+    const char* src = (half == 0 ? kp : vp) + row * Gm::ROWB + gchunk * 16;
+    char* dst = slot + half * Gm::HALF + ((ins % (32 / Gm::RPI)) * 64) * 16;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(dst))));
+    // Issued as inline assembly so that the compiler's wait insertion, which cannot
+    // tell ring slots apart, does not drain the copies in flight before every LDS read;
+    // the ring's own vmcnt waits and barriers order the copies and the reads.  M0 (the
+    // LDS base of the copy) is reserved by the compiler, which uses it in this kernel
+    // for nothing else; the clobber documents that it is overwritten.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void lds_read(const char* p, uint32_t* w) {
+  if constexpr (NB == 16) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else if constexpr (NB == 8) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x; w[1] = x.y;
+  } else if constexpr (NB == 4) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (NB == 2) {
+    w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else {
+    w[0] = *reinterpret_cast<const uint8_t*>(p);
+  }
+}
+
+// Token of the 32-token block that element e (0..7) of lane group q stands for in the
+// value product: the score tile of tokens 0-15 gives e < 4, the one of 16-31 e >= 4.
+__device__ __forceinline__ int ptok(int q, int e) { return e < 4 ? 4 * q + e : 12 + 4 * q + e; }
+
+template <int D, int KDT>
+__device__ __forceinline__ bf16x8 k_operand(const char* kb, int tt, int s, int i, int q) {
+  using Gm = Geo<D, KDT>;
+  const int row = tt * 16 + i;
+  const int byte = (q * (D / 4) + s * 8) * Gm::EB;
+  uint32_t w[4];
+  if constexpr (KDT == SDV_BF16) {
+    lds_read<16>(kb + Gm::at(row, byte), w);
+  } else {
+    uint32_t r8[2];
+    lds_read<8>(kb + Gm::at(row, byte), r8);
+    float f[8];
+    fp8x2_to_f32<false>(r8[0], f[0], f[1]);
+    fp8x2_to_f32<true>(r8[0], f[2], f[3]);
+    fp8x2_to_f32<false>(r8[1], f[4], f[5]);
+    fp8x2_to_f32<true>(r8[1], f[6], f[7]);
+    w[0] = pack2_bf16(f[0], f[1]);
+    w[1] = pack2_bf16(f[2], f[3]);
+    w[2] = pack2_bf16(f[4], f[5]);
+    w[3] = pack2_bf16(f[6], f[7]);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// A operands of O^T += V^T P^T for this wave's output tiles n0 .. n0 + NTW - 1: element
+// e of tile n is V[ptok(q, e)][NT * i + n0 + n].  v_runs reads, for each of the lane's 8
+// tokens, its run of NTW channels (positions past kv_len read as 0: stale storage must
+// not reach P * V); v_operand interleaves bf16 runs into an operand with byte
+// permutes, or widens fp8 runs exactly to bf16.
+template <int D, int KDT, int NTW>
+__device__ __forceinline__ void v_runs(const char* vb, int i, int q, int n0, int pos0, int kv,
+                                       uint32_t (&raw)[8][4]) {
+  using Gm = Geo<D, KDT>;
+  constexpr int NBYTES = NTW * Gm::EB;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int tok = ptok(q, e);
+    const int byte = (Gm::NT * i + n0) * Gm::EB;
+    raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
+    lds_read<NBYTES>(vb + Gm::at(tok, byte), raw[e]);
+    if (pos0 + tok >= kv) raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
+  }
+}
+
+template <int KDT>
+__device__ __forceinline__ bf16x8 v_operand(const uint32_t (&raw)[8][4], int n) {
+  uint32_t w[4];
+  if constexpr (KDT == SDV_BF16) {
+    const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      w[m] = __builtin_amdgcn_perm(raw[2 * m + 1][n >> 1], raw[2 * m][n >> 1], sel);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float a0, a1, b0, b1;
+      const uint32_t wa = raw[2 * m][n >> 2];
+      const uint32_t wb = raw[2 * m + 1][n >> 2];
+      if ((n & 2) == 0) {
+        fp8x2_to_f32<false>(wa, a0, a1);
+        fp8x2_to_f32<false>(wb, b0, b1);
+      } else {
+        fp8x2_to_f32<true>(wa, a0, a1);
+        fp8x2_to_f32<true>(wb, b0, b1);
+      }
+      w[m] = (n & 1) ? pack2_bf16(a1, b1) : pack2_bf16(a0, b0);
+    }
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+constexpr int kMaxDenseBlocks = 1024;   // 32-token blocks per dense split
+
+struct NoUnion {};
+
+// P32 page index of the K sub-page of a dense split's blocks; -1 marks an index outside
+// the pool.  The view's geometry puts V one P128 page (four P32 pages) after K.
+struct DenseMeta {
+  int32_t xk[kMaxDenseBlocks];
+};
+
+template <int RT, int D, int KDT, bool SPARSE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RT >= 4 ? 3 : 2, 8)))
+sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
+                                                             SparseSource ss) {
+  using Gm = Geo<D, KDT>;
+  constexpr int STEPS = Gm::STEPS;
+  constexpr int NT = Gm::NT;
+  constexpr int NCP = 4 / RT;          // output-channel parts
+  constexpr int NTW = NT / NCP;        // output tiles per wave
+  constexpr int ROWS = RT * 16;
+  constexpr int OPAD = D + 4;
+  // Ring depth: with 64 rows three stages let three workgroups share a CU.
+  constexpr int kStages = RT >= 4 ? 3 : 4;
+  static_assert(NTW >= 1, "tiles per wave");
+
+  // The block ring; after the last block the same bytes stage the output rows.
+  constexpr int RING = kStages * Gm::BLOCK;
+  constexpr int OUTB = ROWS * OPAD * 4;
+  __shared__ __attribute__((aligned(16))) char ring[RING > OUTB ? RING : OUTB];
+  float (*o_lds)[OPAD] = reinterpret_cast<float (*)[OPAD]>(ring);
+  __shared__ float L_lds[ROWS];
+  __shared__ float M_lds[ROWS];
+  __shared__ typename std::conditional<SPARSE, UnionLds, DenseMeta>::type ul;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int i = lane & 15;
+  const int q = lane >> 4;
+  const int rt = wave % RT;
+  const int cp = wave / RT;
+  const int n0 = cp * NTW;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+
+  const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
+                                : static_cast<int64_t>(ds.max_sub_pages) * kSub;
+  const int row0 = a.qo_indptr[r];
+  const int qo = a.qo_indptr[r + 1] - row0;
+  const int kv = a.kv_len[r];
+  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
+  const bool bad_cap = !bad_len && kv > kv_cap;
+  if (bad_len || bad_cap) {
+    if (tid == 0 && split == 0 && h == 0)
+      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  const int nrows = qo * G;
+
+  // This wave's query row (lane i of row tile rt), its token and its ladder bound.
+  const int row = rt * 16 + i;
+  const bool row_live = row < nrows;
+  const int t_row = row_live ? row / G : 0;
+  const int g_row = row_live ? row - t_row * G : 0;
+  const int bound_row = row_live ? kv - qo + t_row + 1 : 0;
+  bf16x8 qb[STEPS];
+  {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(row0 + t_row) * a.num_q_heads + h * G + g_row) * D +
+                      q * (D / 4)) * 2;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const uint4 w = row_live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  // Q is complete before any copy is issued, so no wait inside the block loop has to
+  // account for it (the compiler does not see the copies).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
+
+  // This split's blocks and their addresses, staged in LDS before the copy pipeline
+  // starts: a vector load of block metadata inside the loop would wait behind every
+  // asynchronous copy in flight.
+  int nblk, base;
+  if constexpr (SPARSE) {
+    const int n_union = build_union(ul, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
+    const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
+    base = split * chunk;
+    nblk = 4 * max(0, min(n_union, base + chunk) - base);
+  } else {
+    const int chunk = (ds.max_sub_pages + a.num_splits - 1) / a.num_splits;
+    const int nb = (kv + kSub - 1) / kSub;
+    base = split * chunk;
+    nblk = max(0, min(nb, base + chunk) - base);
+    const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
+    for (int b = tid; b < nblk; b += 256) {
+      const int32_t xk = offs[base + b];
+      const int32_t xv = offs[ds.max_sub_pages + base + b];
+      const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
+      if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+      ul.xk[b] = ok ? xk : -1;
+    }
+    __syncthreads();
+  }
+
+  // Block b of the split: K and V source pointers, first position, selecting tokens.
+  auto locate = [&](int b, const char*& kp, const char*& vp, int& pos0, int& mask) {
+    if constexpr (SPARSE) {
+      const int e = base + (b >> 2);
+      const int quarter = b & 3;
+      const int p = ul.upage[e];
+      mask = ul.umask[e];
+      pos0 = p * kPage + quarter * kSub;
+      const int64_t off = (static_cast<int64_t>(ul.uphys[e]) * ss.page_stride +
+                           (static_cast<int64_t>(h) * kPage + quarter * kSub) * D) * Gm::EB;
+      kp = reinterpret_cast<const char*>(ss.k) + off;
+      vp = reinterpret_cast<const char*>(ss.v) + off;
+    } else {
+      int64_t xk = ul.xk[b];
+      mask = xk < 0 ? 0 : ~0;       // an index outside the pool reads page 0, masked out
+      xk = xk < 0 ? 0 : xk;
+      const int64_t xv = xk + 4;
+      pos0 = (base + b) * kSub;
+      kp = reinterpret_cast<const char*>(ds.root) + (xk * Hkv + h) * kSub * D * Gm::EB;
+      vp = reinterpret_cast<const char*>(ds.root) + (xv * Hkv + h) * kSub * D * Gm::EB;
+    }
+  };
+
+  f32x4 o[NTW];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Prologue: blocks 0 .. kStages - 2 in flight.
+#pragma unroll
+  for (int b = 0; b < kStages - 1; ++b) {
+    if (b < nblk) {
+      const char *kp, *vp;
+      int p0, mk;
+      locate(b, kp, vp, p0, mk);
+      issue_block<D, KDT>(kp, vp, ring + b * Gm::BLOCK, wave, lane);
+    }
+  }
+
+  for (int b = 0; b < nblk; ++b) {
+    const int bn = b + kStages - 1;
+    if (bn < nblk) {
+      const char *kp, *vp;
+      int p0, mk;
+      locate(bn, kp, vp, p0, mk);
+      issue_block<D, KDT>(kp, vp, ring + (bn % kStages) * Gm::BLOCK, wave, lane);
+    }
+    // Wait for this wave's copies of block b; the barrier makes all waves' copies visible.
+    const int after = min(nblk - 1 - b, kStages - 1);   // blocks issued after b
+    if (after >= 3) wait_vmcnt<(kStages >= 4 ? 3 : 0) * Gm::LPT>();
+    else if (after == 2) wait_vmcnt<2 * Gm::LPT>();
+    else if (after == 1) wait_vmcnt<Gm::LPT>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+
+    const char* kb = ring + (b % kStages) * Gm::BLOCK;
+    const char* vb = kb + Gm::HALF;
+    const char *kp_unused, *vp_unused;
+    int pos0, mask;
+    locate(b, kp_unused, vp_unused, pos0, mask);
+
+    // scores S^T for this wave's row tile
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s)
+        sacc[tt] = mfma16(k_operand<D, KDT>(kb, tt, s, i, q), qb[s], sacc[tt]);
+    }
+    const int bnd = ((mask >> t_row) & 1) ? bound_row : 0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = pos0 + tt * 16 + 4 * q + e;
+        const float sv = pos < bnd ? sacc[tt][e] * qk_scale : -INFINITY;
+        sacc[tt][e] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // The row's reference maximum moves only when a score exceeds it by more than 2^8
+    // (probabilities then stay <= 256); l and O always share the reference, so the
+    // normalised result is unchanged and most blocks skip the rescale.
+    if (mx > m_run + kRescaleLog2) {
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NTW; ++n) o[n] *= alpha;
+      m_run = mx;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[0][e] - m_run);
+      p[e + 4] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[1][e] - m_run);
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ls += p[e];
+    l_run += ls;
+    const bf16x8 pb = __builtin_bit_cast(
+        bf16x8, make_uint4(pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
+                           pack2_bf16(p[6], p[7])));
+    // value product for this wave's output tiles
+    uint32_t vraw[8][4];
+    v_runs<D, KDT, NTW>(vb, i, q, n0, pos0, kv, vraw);
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) o[n] = mfma16(v_operand<KDT>(vraw, n), pb, o[n]);
+    // The slot of block b is refilled next iteration: every wave's reads of it are done.
+    wait_lgkmcnt0();
+    ring_barrier();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- normalise and write (waves of one row tile hold identical m, l) ----
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (cp == 0 && q == 0) {
+    L_lds[row] = l_run;
+    M_lds[row] = m_run;
+  }
+#pragma unroll
+  for (int n = 0; n < NTW; ++n)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o_lds[row][NT * (4 * q + e) + n0 + n] = o[n][e];
+  __syncthreads();
+
+  const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
+  for (int item = tid; item < nrows * (D / 8); item += 256) {
+    const int orow = item / (D / 8);
+    const int c0 = (item - orow * (D / 8)) * 8;
+    const int t = orow / G;
+    const int g = orow - t * G;
+    const int hq = h * G + g;
+    const int64_t qrow = row0 + t;
+    const float L = L_lds[orow];
+    const float inv = L > 0.f ? a.v_scale / L : 0.f;
+    float v8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v8[e] = o_lds[orow][c0 + e] * inv;
+    if (a.num_splits == 1) {
+      const int64_t idx = (qrow * a.num_q_heads + hq) * D + c0;
+      if (a.out_dt == SDV_BF16) {
+        const uint4 w = make_uint4(pack2_bf16(v8[0], v8[1]), pack2_bf16(v8[2], v8[3]),
+                                   pack2_bf16(v8[4], v8[5]), pack2_bf16(v8[6], v8[7]));
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + idx) = w;
+      } else {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx);
+        dst[0] = make_float4(v8[0], v8[1], v8[2], v8[3]);
+        dst[1] = make_float4(v8[4], v8[5], v8[6], v8[7]);
+      }
+    } else {
+      const int64_t unit = (static_cast<int64_t>(split) * rows_cap + qrow) * a.num_q_heads + hq;
+      float4* dst = reinterpret_cast<float4*>(a.part_o + unit * D + c0);
+      dst[0] = make_float4(v8[0], v8[1], v8[2], v8[3]);
+      dst[1] = make_float4(v8[4], v8[5], v8[6], v8[7]);
+      if (c0 == 0)
+        a.part_lse[unit] = L > 0.f ? (M_lds[orow] + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int RT, int D, int KDT, bool SPARSE>
+hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
+                    hipStream_t s) {
+  dim3 grid(a.num_splits, a.num_kv_heads, a.B);
+  hipLaunchKernelGGL((sdv_attn_stream_kernel<RT, D, KDT, SPARSE>), grid, dim3(256), 0, s, a, ds, ss);
+  return hipGetLastError();
+}
+
+template <bool SPARSE>
+hipError_t dispatch(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
+                    hipStream_t s) {
+  const int rows = a.max_qo_len * (a.num_q_heads / a.num_kv_heads);
+  const int rt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+#define SDV_STREAM_CASE(RTV, DV, KDTV)                                                 \
+  if (rt == RTV && a.head_dim == DV && a.kv_dt == KDTV)                                \
+    return launch_t<RTV, DV, KDTV, SPARSE>(a, ds, ss, s);
+  SDV_STREAM_CASE(1, 128, SDV_BF16)
+  SDV_STREAM_CASE(2, 128, SDV_BF16)
+  SDV_STREAM_CASE(4, 128, SDV_BF16)
+  SDV_STREAM_CASE(1, 64, SDV_BF16)
+  SDV_STREAM_CASE(2, 64, SDV_BF16)
+  SDV_STREAM_CASE(4, 64, SDV_BF16)
+  SDV_STREAM_CASE(1, 128, SDV_FP8_E4M3)
+  SDV_STREAM_CASE(2, 128, SDV_FP8_E4M3)
+  SDV_STREAM_CASE(4, 128, SDV_FP8_E4M3)
+  SDV_STREAM_CASE(1, 64, SDV_FP8_E4M3)
+  SDV_STREAM_CASE(2, 64, SDV_FP8_E4M3)
+  SDV_STREAM_CASE(4, 64, SDV_FP8_E4M3)
+#undef SDV_STREAM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_dense_stream(const AttnArgs& a, const DenseSource& src, hipStream_t s) {
+  return dispatch<false>(a, src, SparseSource{}, s);
+}
+
+hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
+  return dispatch<true>(a, DenseSource{}, src, s);
+}
+
+}  // namespace sdv

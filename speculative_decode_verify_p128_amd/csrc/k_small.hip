@@ -109,6 +109,34 @@ __global__ void __launch_bounds__(256) sdv_fill_kernel(uint4* __restrict__ dst, 
     dst[i] = v;
 }
 
+// Streaming-read probe: every byte of src read once with 16-byte loads (4 in flight
+// per lane), folded into one word per workgroup so the loads cannot be elided.
+__global__ void __launch_bounds__(256) sdv_read_probe_kernel(const uint4* __restrict__ src,
+                                                             int64_t n16, uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicXor(sink + blockIdx.x, acc);
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                             hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(sdv_read_probe_kernel, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(src), n16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s) {
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
   if (n16 == 0) return hipSuccess;

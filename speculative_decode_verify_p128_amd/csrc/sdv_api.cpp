@@ -118,7 +118,9 @@ const char* sdv_status_string(int32_t status) {
 
 const char* sdv_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sdv_set_kernel_family(int32_t family) { return g_family.exchange(family ? 1 : 0); }
+int32_t sdv_set_kernel_family(int32_t family) {
+  return g_family.exchange(family >= 0 && family <= 2 ? family : 0);
+}
 
 int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_table,
                              int32_t B, int32_t max_blocks, int32_t bt_stride,
@@ -223,9 +225,13 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   a.dev_err = dev_err;
   split_workspace(workspace, rows_cap, num_q_heads, v.head_dim, num_splits, &a.part_o, &a.part_lse);
   sdv::DenseSource src{v.k_root, sub_offsets, max_sub_pages, v.num_sub_pages};
-  hipError_t e = (g_family.load() == 0 && sdv::mfma_supported(a))
-                     ? sdv::launch_attn_dense_mfma(a, src, stream)
-                     : sdv::launch_attn_dense_valu(a, src, stream);
+  const int32_t fam = g_family.load();
+  const bool stream_ok =
+      (max_sub_pages + num_splits - 1) / num_splits <= sdv::kStreamMaxDenseBlocks;
+  hipError_t e;
+  if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_dense_valu(a, src, stream);
+  else if (fam == 2 || !stream_ok) e = sdv::launch_attn_dense_mfma(a, src, stream);
+  else e = sdv::launch_attn_dense_stream(a, src, stream);
   if (e != hipSuccess) return hip_status(e, "verify_attention_dense launch");
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
@@ -269,8 +275,8 @@ int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
   if (st) return st;
   if (q_dt != SDV_F32 && q_dt != SDV_BF16) return fail(SDV_ERR_DTYPE, "q dtype %d", q_dt);
   const int32_t G = num_q_heads / kv->num_kv_heads;
-  if (static_cast<int64_t>(max_qo_len) * G * kv->head_dim > 16384)
-    return fail(SDV_ERR_SHAPE, "max_qo_len x group x head_dim exceeds 16384");
+  if (static_cast<int64_t>(max_qo_len) * G * kv->head_dim > 8192)
+    return fail(SDV_ERR_SHAPE, "max_qo_len x group x head_dim exceeds 8192");
   if (max_pages < 1 || bt_stride < max_pages)
     return fail(SDV_ERR_SHAPE, "max_pages %d, bt_stride %d", max_pages, bt_stride);
   if (B > 0 && (!block_table || !scores))
@@ -343,9 +349,11 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
   split_workspace(workspace, rows_cap, num_q_heads, kv->head_dim, num_splits, &a.part_o, &a.part_lse);
   sdv::SparseSource src{kv->k, kv->v, kv->page_stride, kv->num_pages, block_table, bt_stride,
                         max_pages, topk_idx, top_k};
-  hipError_t e = (g_family.load() == 0 && sdv::mfma_supported(a))
-                     ? sdv::launch_attn_sparse_mfma(a, src, stream)
-                     : sdv::launch_attn_sparse_valu(a, src, stream);
+  const int32_t fam = g_family.load();
+  hipError_t e;
+  if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_sparse_valu(a, src, stream);
+  else if (fam == 2) e = sdv::launch_attn_sparse_mfma(a, src, stream);
+  else e = sdv::launch_attn_sparse_stream(a, src, stream);
   if (e != hipSuccess) return hip_status(e, "verify_attention_sparse launch");
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
@@ -379,6 +387,17 @@ int32_t sdv_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t stre
   if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
     return fail(SDV_ERR_SHAPE, "fill needs 16-byte aligned size and address");
   return hip_status(sdv::launch_fill_u32(dst, bytes, pattern, stream), "sdv_fill_u32 launch");
+}
+
+int32_t sdv_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                       hipStream_t stream) {
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(SDV_ERR_NULL_POINTER, "src and sink must be non-null");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "probe needs 16-byte aligned size and address");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(SDV_ERR_SHAPE, "blocks %d", blocks);
+  return hip_status(sdv::launch_read_probe(src, bytes, sink, blocks, stream),
+                    "sdv_read_probe launch");
 }
 
 }  // extern "C"

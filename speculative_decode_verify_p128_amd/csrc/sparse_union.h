@@ -18,8 +18,9 @@ constexpr int kMaxWords = 512;   // max_pages <= 16384
 struct UnionLds {
   uint32_t bitmap[kMaxWords];
   int32_t word_prefix[kMaxWords];
-  int32_t upage[kMaxUnion];
-  int32_t umask[kMaxUnion];
+  int32_t upage[kMaxUnion];     // request-local page number
+  int32_t uphys[kMaxUnion];     // physical page (0 when out of range, then umask = 0)
+  int32_t umask[kMaxUnion];     // bit t: verify token t selected the page
   int32_t scan[256];
 };
 
@@ -67,7 +68,14 @@ __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, in
     int idx = u.word_prefix[w];
     while (bits) {
       const int b = __ffs(bits) - 1;
-      u.upage[idx] = w * 32 + b;
+      const int p = w * 32 + b;
+      int phys = ss.block_table[static_cast<int64_t>(r) * ss.bt_stride + p];
+      if (phys < 0 || phys >= ss.num_pages) {
+        set_err(dev_err, SDV_DEVERR_PAGE_RANGE);
+        phys = -1;
+      }
+      u.upage[idx] = p;
+      u.uphys[idx] = phys;
       u.umask[idx] = 0;
       ++idx;
       bits &= bits - 1;
@@ -82,8 +90,13 @@ __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, in
     if (p < 0 || p >= nvalid) continue;
     const int w = p >> 5;
     const int idx = u.word_prefix[w] + __popc(u.bitmap[w] & ((1u << (p & 31)) - 1u));
-    atomicOr(&u.umask[idx], 1 << t);
+    if (u.uphys[idx] >= 0) atomicOr(&u.umask[idx], 1 << t);
   }
+  __syncthreads();
+  // Pages outside the pool keep an empty token mask and read page 0 (in bounds); the
+  // request is flagged.
+  for (int e = tid; e < total; e += 256)
+    if (u.uphys[e] < 0) u.uphys[e] = 0;
   __syncthreads();
   return total;
 }
