@@ -99,36 +99,57 @@ struct Geo {
   }
 };
 
-// Each wave issues LPT asynchronous loads that together copy one block (K then V) into
-// the ring slot; lane l of instruction n lands at slot + (n * 64 + l) * 16.
+// A wave's share of one block copy: LPT asynchronous 16-byte-per-lane loads that
+// together copy one block (K then V) into a ring slot; lane l of instruction n lands at
+// slot + (n * 64 + l) * 16.  The per-lane source offsets inside the block's K or V run
+// and the LDS offsets inside the slot do not change from block to block, so a copy is
+// a scalar block base, a constant 32-bit lane offset and M0.
 template <int D, int KDT>
-__device__ __forceinline__ void issue_block(const char* kp, const char* vp, char* slot, int wave,
-                                            int lane) {
+struct BlockCopier {
   using Gm = Geo<D, KDT>;
+  uint32_t off[Gm::LPT];      // lane's byte offset in the K or V run of the block
+  uint32_t lds[Gm::LPT];      // LDS byte offset of the instruction in the slot (uniform)
+  bool is_v[Gm::LPT];         // copies V rather than K (uniform)
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int n = 0; n < Gm::LPT; ++n) {
-    const int ins = wave * Gm::LPT + n;                 // 0 .. 2 * 32 / RPI - 1
-    const int half = ins / (32 / Gm::RPI);              // 0 = K, 1 = V
-    const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
-    const int lchunk = lane % Gm::CPR;
-    const int gchunk = (lchunk ^ row) & (Gm::CPR - 1);
-    const char* src = (half == 0 ? kp : vp) + row * Gm::ROWB + gchunk * 16;
-    char* dst = slot + half * Gm::HALF + ((ins % (32 / Gm::RPI)) * 64) * 16;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(dst))));
-    // Issued as inline assembly so that the compiler's wait insertion, which cannot
-    // tell ring slots apart, does not drain the copies in flight before every LDS read;
-    // the ring's own vmcnt waits and barriers order the copies and the reads.  M0 (the
-    // LDS base of the copy) is reserved by the compiler, which uses it in this kernel
-    // for nothing else; the clobber documents that it is overwritten.
+    for (int n = 0; n < Gm::LPT; ++n) {
+      const int ins = wave * Gm::LPT + n;               // 0 .. 2 * 32 / RPI - 1
+      const int half = ins / (32 / Gm::RPI);            // 0 = K, 1 = V
+      const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
+      const int gchunk = ((lane % Gm::CPR) ^ row) & (Gm::CPR - 1);
+      off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
+      lds[n] = static_cast<uint32_t>(half * Gm::HALF + (ins % (32 / Gm::RPI)) * 64 * 16);
+      is_v[n] = half != 0;
+    }
+  }
+
+  // kbase, vbase: first byte of the block's K and V runs; slot_lds: LDS address of the
+  // ring slot.  All three are wave-uniform.
+  __device__ __forceinline__ void issue(uint64_t kbase, uint64_t vbase, uint32_t slot_lds) const {
+#pragma unroll
+    for (int n = 0; n < Gm::LPT; ++n) {
+      const uint64_t base = is_v[n] ? vbase : kbase;
+      const uint32_t m0 = slot_lds + lds[n];
+      // Inline assembly, so that the compiler's wait insertion, which cannot tell ring
+      // slots apart, does not drain the copies in flight before every LDS read; the
+      // ring's own vmcnt waits and barriers order copies and reads.  M0 (the copy's
+      // LDS base) is reserved by the compiler, which uses it in this kernel for
+      // nothing else; the clobber records that it is overwritten.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds), "v"(src)
-                 : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(m0), "v"(off[n]), "s"(base)
+                   : "memory", "m0");
 #pragma clang diagnostic pop
+    }
   }
+};
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
 template <int NB>
@@ -181,7 +202,7 @@ __device__ __forceinline__ bf16x8 k_operand(const char* kb, int tt, int s, int i
 // tokens, its run of NTW channels (positions past kv_len read as 0: stale storage must
 // not reach P * V); v_operand interleaves bf16 runs into an operand with byte
 // permutes, or widens fp8 runs exactly to bf16.
-template <int D, int KDT, int NTW>
+template <int D, int KDT, int NTW, bool TAIL>
 __device__ __forceinline__ void v_runs(const char* vb, int i, int q, int n0, int pos0, int kv,
                                        uint32_t (&raw)[8][4]) {
   using Gm = Geo<D, KDT>;
@@ -192,7 +213,7 @@ __device__ __forceinline__ void v_runs(const char* vb, int i, int q, int n0, int
     const int byte = (Gm::NT * i + n0) * Gm::EB;
     raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
     lds_read<NBYTES>(vb + Gm::at(tok, byte), raw[e]);
-    if (pos0 + tok >= kv) raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
+    if (TAIL && pos0 + tok >= kv) raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
   }
 }
 
@@ -335,28 +356,39 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     __syncthreads();
   }
 
-  // Block b of the split: K and V source pointers, first position, selecting tokens.
-  auto locate = [&](int b, const char*& kp, const char*& vp, int& pos0, int& mask) {
+  // Block b of the split: K and V byte addresses (wave-uniform), first position and the
+  // verify tokens that selected it.
+  auto locate = [&](int b, uint64_t& kbase, uint64_t& vbase, int& pos0, int& mask) {
     if constexpr (SPARSE) {
       const int e = base + (b >> 2);
       const int quarter = b & 3;
-      const int p = ul.upage[e];
-      mask = ul.umask[e];
+      const int p = __builtin_amdgcn_readfirstlane(ul.upage[e]);
+      mask = __builtin_amdgcn_readfirstlane(ul.umask[e]);
+      const int phys = __builtin_amdgcn_readfirstlane(ul.uphys[e]);
       pos0 = p * kPage + quarter * kSub;
-      const int64_t off = (static_cast<int64_t>(ul.uphys[e]) * ss.page_stride +
-                           (static_cast<int64_t>(h) * kPage + quarter * kSub) * D) * Gm::EB;
-      kp = reinterpret_cast<const char*>(ss.k) + off;
-      vp = reinterpret_cast<const char*>(ss.v) + off;
+      const uint64_t off = static_cast<uint64_t>(
+          (static_cast<int64_t>(phys) * ss.page_stride +
+           (static_cast<int64_t>(h) * kPage + quarter * kSub) * D) * Gm::EB);
+      kbase = reinterpret_cast<uint64_t>(ss.k) + off;
+      vbase = reinterpret_cast<uint64_t>(ss.v) + off;
     } else {
-      int64_t xk = ul.xk[b];
+      int64_t xk = __builtin_amdgcn_readfirstlane(ul.xk[b]);
       mask = xk < 0 ? 0 : ~0;       // an index outside the pool reads page 0, masked out
       xk = xk < 0 ? 0 : xk;
       const int64_t xv = xk + 4;
       pos0 = (base + b) * kSub;
-      kp = reinterpret_cast<const char*>(ds.root) + (xk * Hkv + h) * kSub * D * Gm::EB;
-      vp = reinterpret_cast<const char*>(ds.root) + (xv * Hkv + h) * kSub * D * Gm::EB;
+      kbase = reinterpret_cast<uint64_t>(ds.root) + static_cast<uint64_t>((xk * Hkv + h) * kSub * D * Gm::EB);
+      vbase = reinterpret_cast<uint64_t>(ds.root) + static_cast<uint64_t>((xv * Hkv + h) * kSub * D * Gm::EB);
     }
   };
+
+  BlockCopier<D, KDT> copier;
+  copier.init(__builtin_amdgcn_readfirstlane(wave), lane);
+  const uint32_t ring_lds = lds_address(ring);
+  // Blocks wholly inside every row's ladder bound and chosen by every token need no
+  // masking: the common case, tested once per block for the whole workgroup.
+  const int all_tokens = qo >= 32 ? ~0 : (1 << qo) - 1;
+  const int first_bound = kv - qo + 1;
 
   f32x4 o[NTW];
 #pragma unroll
@@ -367,20 +399,20 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
 #pragma unroll
   for (int b = 0; b < kStages - 1; ++b) {
     if (b < nblk) {
-      const char *kp, *vp;
+      uint64_t kb, vb;
       int p0, mk;
-      locate(b, kp, vp, p0, mk);
-      issue_block<D, KDT>(kp, vp, ring + b * Gm::BLOCK, wave, lane);
+      locate(b, kb, vb, p0, mk);
+      copier.issue(kb, vb, ring_lds + b * Gm::BLOCK);
     }
   }
 
   for (int b = 0; b < nblk; ++b) {
     const int bn = b + kStages - 1;
     if (bn < nblk) {
-      const char *kp, *vp;
+      uint64_t kbn, vbn;
       int p0, mk;
-      locate(bn, kp, vp, p0, mk);
-      issue_block<D, KDT>(kp, vp, ring + (bn % kStages) * Gm::BLOCK, wave, lane);
+      locate(bn, kbn, vbn, p0, mk);
+      copier.issue(kbn, vbn, ring_lds + (bn % kStages) * Gm::BLOCK);
     }
     // Wait for this wave's copies of block b; the barrier makes all waves' copies visible.
     const int after = min(nblk - 1 - b, kStages - 1);   // blocks issued after b
@@ -392,11 +424,12 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
 
     const char* kb = ring + (b % kStages) * Gm::BLOCK;
     const char* vb = kb + Gm::HALF;
-    const char *kp_unused, *vp_unused;
+    uint64_t kb_unused, vb_unused;
     int pos0, mask;
-    locate(b, kp_unused, vp_unused, pos0, mask);
+    locate(b, kb_unused, vb_unused, pos0, mask);
+    const bool inside = pos0 + kSub <= first_bound && (mask & all_tokens) == all_tokens;
 
-    // scores S^T for this wave's row tile
+    // scores S^T for this wave's row tile (unscaled)
     f32x4 sacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -405,34 +438,50 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
       for (int s = 0; s < STEPS; ++s)
         sacc[tt] = mfma16(k_operand<D, KDT>(kb, tt, s, i, q), qb[s], sacc[tt]);
     }
-    const int bnd = ((mask >> t_row) & 1) ? bound_row : 0;
     float mx = -INFINITY;
+    if (inside) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = pos0 + tt * 16 + 4 * q + e;
-        const float sv = pos < bnd ? sacc[tt][e] * qk_scale : -INFINITY;
-        sacc[tt][e] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    // The row's reference maximum moves only when a score exceeds it by more than 2^8
-    // (probabilities then stay <= 256); l and O always share the reference, so the
-    // normalised result is unchanged and most blocks skip the rescale.
-    if (mx > m_run + kRescaleLog2) {
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
-      l_run *= alpha;
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[tt][e]);
+    } else {
+      const int bnd = ((mask >> t_row) & 1) ? bound_row : 0;
 #pragma unroll
-      for (int n = 0; n < NTW; ++n) o[n] *= alpha;
-      m_run = mx;
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = pos0 + tt * 16 + 4 * q + e;
+          const float sv = pos < bnd ? sacc[tt][e] : -INFINITY;
+          sacc[tt][e] = sv;
+          mx = fmaxf(mx, sv);
+        }
     }
+    // The scale is positive, so scaling the maximum equals the maximum of the scaled
+    // scores.  The row's reference maximum moves only when a score exceeds it by more
+    // than 2^8 (probabilities then stay <= 256); l and O always share the reference, so
+    // the normalised result is unchanged and most blocks skip the rescale.  A row's
+    // maximum can pass the threshold only if one of its four lanes' partial maxima does,
+    // so the cross-lane reduction runs only when some lane of the wave votes for it.
+    const float mx_scaled = mx * qk_scale;
+    if (__any(mx_scaled > m_run + kRescaleLog2)) {
+      float mr = fmaxf(mx_scaled, __shfl_xor(mx_scaled, 16, kWave));
+      mr = fmaxf(mr, __shfl_xor(mr, 32, kWave));
+      if (mr > m_run + kRescaleLog2) {
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mr);
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) o[n] *= alpha;
+        m_run = mr;
+      }
+    }
+    // Masked scores are -inf and give 0; a row with no live score yet keeps m = -inf and
+    // has only masked scores here.
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float p[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p[e] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[0][e] - m_run);
-      p[e + 4] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[1][e] - m_run);
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][e], qk_scale, -m_use));
+      p[e + 4] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][e], qk_scale, -m_use));
     }
     float ls = 0.f;
 #pragma unroll
@@ -443,7 +492,10 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
                            pack2_bf16(p[6], p[7])));
     // value product for this wave's output tiles
     uint32_t vraw[8][4];
-    v_runs<D, KDT, NTW>(vb, i, q, n0, pos0, kv, vraw);
+    if (pos0 + kSub <= kv)
+      v_runs<D, KDT, NTW, false>(vb, i, q, n0, pos0, kv, vraw);
+    else
+      v_runs<D, KDT, NTW, true>(vb, i, q, n0, pos0, kv, vraw);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) o[n] = mfma16(v_operand<KDT>(vraw, n), pb, o[n]);
     // The slot of block b is refilled next iteration: every wave's reads of it are done.
