@@ -97,6 +97,17 @@ def dense_algorithmic_bytes(case):
         2 * rows * w.num_q_heads * w.head_dim * eq + int((-(-kv // 32)).sum()) * 2 * 4
 
 
+# Sources that decide each timed kernel's memory traffic: a counter summary taken on
+# other sources no longer describes the kernel.
+KERNEL_SOURCES = {
+    "proxy_page_scores": ("k_proxy.hip", "device.h"),
+    "ladder_topk_pages": ("k_topk.hip", "device.h"),
+    "verify_attention_sparse": ("k_attn_stream.hip", "sparse_union.h", "k_small.hip", "device.h",
+                                "sdv_api.cpp"),
+    "verify_attention_dense": ("k_attn_stream.hip", "k_small.hip", "device.h", "sdv_api.cpp"),
+}
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -105,7 +116,7 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload, src_hash, launches_bytes):
+def load_traffic(kernel, workload, src_hash):
     """HBM bytes per launch from a committed counter summary, if it was taken on the
     current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
@@ -261,9 +272,7 @@ def main():
         kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
                       "frac_of_peak": gbs / HBM_PEAK_GBS}
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    src = {"proxy_page_scores": ("k_proxy.hip",), "ladder_topk_pages": ("k_topk.hip",),
-           "verify_attention_sparse": ("k_attn_mfma.hip", "k_attn_valu.hip", "k_small.hip")}[dom]
-    traffic = load_traffic(dom, w.name, source_hash(*src), None)
+    traffic = load_traffic(dom, w.name, source_hash(*KERNEL_SOURCES[dom]))
     path_gbs = path_bytes / (ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -336,8 +345,7 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "verify_attention_dense", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": load_traffic("verify_attention_dense", wd.name,
-                                                 source_hash("k_attn_mfma.hip", "k_attn_valu.hip",
-                                                             "k_small.hip"), None)},
+                                                 source_hash(*KERNEL_SOURCES["verify_attention_dense"]))},
         }
         del d, outd, wsd
 

@@ -135,10 +135,11 @@ struct BlockCopier {
       // slots apart, does not drain the copies in flight before every LDS read; the
       // ring's own vmcnt waits and barriers order copies and reads.  M0 (the copy's
       // LDS base) is reserved by the compiler, which uses it in this kernel for
-      // nothing else; the clobber records that it is overwritten.
+      // nothing else; the clobber records that it is overwritten.  The copies are
+      // non-temporal: every K/V byte is read once.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                    :
                    : "s"(m0), "v"(off[n]), "s"(base)
                    : "memory", "m0");

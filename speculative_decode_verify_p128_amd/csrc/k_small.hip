@@ -109,19 +109,26 @@ __global__ void __launch_bounds__(256) sdv_fill_kernel(uint4* __restrict__ dst, 
     dst[i] = v;
 }
 
-// Streaming-read probe: every byte of src read once with 16-byte loads (4 in flight
-// per lane), folded into one word per workgroup so the loads cannot be elided.
+typedef unsigned int u32x4_probe __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 probe_load(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_probe*>(p)));
+}
+
+// Streaming-read probe: every byte of src read once with non-temporal 16-byte loads (4
+// in flight per lane), folded into one word per workgroup so the loads cannot be elided.
 __global__ void __launch_bounds__(256) sdv_read_probe_kernel(const uint4* __restrict__ src,
                                                              int64_t n16, uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const uint4 a = probe_load(src + i), b = probe_load(src + i + stride),
+                c = probe_load(src + i + 2 * stride), d = probe_load(src + i + 3 * stride);
     acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
   for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+    const uint4 a = probe_load(src + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);

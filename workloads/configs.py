@@ -88,14 +88,14 @@ TINY_FP32 = VerifyWorkload(
 DENSE_BF16 = VerifyWorkload(
     name="dense_bf16", batch=32, qo=4, kv=("uniform", 1024, 8192),
     num_q_heads=64, num_kv_heads=4, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
-    values="normal", top_k=16, num_splits=8, slot_stride=8, root_page=6,
+    values="normal", top_k=16, num_splits=4, slot_stride=8, root_page=6,
     pool_index_scale=8)
 
 # 3. Block-sparse target layer, bf16.
 SPARSE_BF16 = VerifyWorkload(
     name="sparse_bf16", batch=64, qo=4, kv=("uniform", 4096, 32768),
     num_q_heads=16, num_kv_heads=4, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
-    values="normal", top_k=16, num_splits=4)
+    values="normal", top_k=16, num_splits=2)
 
 # 4. Long-context sparse verify with fp8 e4m3 K/V and a 16-way split-KV.
 LONG_FP8 = VerifyWorkload(
