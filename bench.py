@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--splits", type=int, default=None, help="override sparse num_splits")
     p.add_argument("--dense-splits", type=int, default=None)
@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a 1 GiB device copy (for memory-counter calibration)")
     p.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
+    p.add_argument("--warm", action="store_true",
+                   help="no cache-evicting fill between steps (warm-cache numbers)")
     return p.parse_args()
 
 
@@ -129,9 +131,13 @@ def load_traffic(kernel, workload, src_hash):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_steps(step_fns, steps, warmup, torch):
-    """Runs warmup + timed steps; events around each kernel on the current stream."""
+def time_steps(step_fns, steps, warmup, torch, flush=None):
+    """Runs warmup + timed steps; events around each kernel on the current stream.  With
+    `flush`, a cache-evicting fill runs before every step outside the timed span (the
+    step time is the event span from the step's first kernel to its last)."""
     for _ in range(warmup):
+        if flush:
+            flush()
         for _, fn in step_fns:
             fn()
     torch.cuda.synchronize()
@@ -139,24 +145,24 @@ def time_steps(step_fns, steps, warmup, torch):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
     for s in range(steps):
+        if flush:
+            flush()
         ev[s][0].record()
         for i, (_, fn) in enumerate(step_fns):
             fn()
             ev[s][i + 1].record()
-    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
+    step_ms = [ev[s][0].elapsed_time(ev[s][n]) for s in range(steps)]
     per = {}
     for i, (name, _) in enumerate(step_fns):
         ts = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]
         per[name] = {"avg_us": 1e3 * float(np.mean(ts)), "min_us": 1e3 * float(np.min(ts)),
-                     "p50_us": 1e3 * float(np.median(ts))}
-    return total_ms / steps, per, wall
+                     "p10_us": 1e3 * float(np.percentile(ts, 10)),
+                     "p50_us": 1e3 * float(np.median(ts)),
+                     "p90_us": 1e3 * float(np.percentile(ts, 90))}
+    return float(np.mean(step_ms)), per, wall
 
 
 def cpu_baseline(case, n_req):
@@ -232,6 +238,12 @@ def main():
         calibrate_copy(torch)
         return
     sdv.set_kernel_family(args.family)
+    flush = None
+    if not args.warm:
+        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+        def flush():
+            sdv.fill_u32(flush_buf, 0x5A5A5A5A)
 
     # ---- sparse target-layer path (the headline workload) ----
     w = W.SPARSE_BF16
@@ -260,7 +272,7 @@ def main():
 
     fns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
            ("verify_attention_sparse", k_sparse)]
-    ms, per, wall = time_steps(fns, args.steps, args.warmup, torch)
+    ms, per, wall = time_steps(fns, args.steps, args.warmup, torch, flush)
     tokens = c.lengths.total_q
     idx_np = idx.cpu().numpy()
     ab = sparse_algorithmic_bytes(c, idx_np)
@@ -304,6 +316,8 @@ def main():
         "kernels": kern,
         "sparse_row_expanded_kv_bytes": ab["sparse_row_expanded_kv"],
         "wall_s_timed": wall,
+        "cache": ("warm: consecutive steps, no eviction" if args.warm else
+                  "cold: a 1 GiB fill before every step (untimed) evicts L2 and the Infinity Cache"),
     }
     del scores, ws
 
@@ -333,7 +347,7 @@ def main():
 
         msd, perd, _ = time_steps([("kv_subpage_view_init", k_view),
                                    ("verify_attention_dense", k_dense)],
-                                  args.steps, args.warmup, torch)
+                                  args.steps, args.warmup, torch, flush)
         db = dense_algorithmic_bytes(d)
         gbs = db / (perd["verify_attention_dense"]["avg_us"] * 1e-6) / 1e9
         result["dense"] = {

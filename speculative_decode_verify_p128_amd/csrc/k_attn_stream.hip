@@ -247,6 +247,36 @@ __device__ __forceinline__ bf16x8 v_operand(const uint32_t (&raw)[8][4], int n) 
 
 constexpr int kMaxDenseBlocks = 1024;   // 32-token blocks per dense split
 
+// Ring depth (blocks) per row-tile count: STAGES - 1 blocks are in flight while one is
+// computed, so a deeper ring hides more memory latency per workgroup, at the price of
+// LDS and so of workgroups per CU.
+template <int RT>
+constexpr int ring_stages() { return 4; }
+
+// f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Waits until at most `after` blocks' copies (LPT instructions each) of this wave are
+// still in flight, for after in [0, MAXA].
+template <int LPT, int MAXA>
+__device__ __forceinline__ void wait_blocks(int after) {
+  if constexpr (MAXA > 0) {
+    if (after >= MAXA) {
+      wait_vmcnt<MAXA * LPT>();
+      return;
+    }
+    wait_blocks<LPT, MAXA - 1>(after);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 struct NoUnion {};
 
 // P32 page index of the K sub-page of a dense split's blocks; -1 marks an index outside
@@ -256,7 +286,7 @@ struct DenseMeta {
 };
 
 template <int RT, int D, int KDT, bool SPARSE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RT >= 4 ? 3 : 2, 8)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
                                                              SparseSource ss) {
   using Gm = Geo<D, KDT>;
@@ -266,8 +296,7 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   constexpr int NTW = NT / NCP;        // output tiles per wave
   constexpr int ROWS = RT * 16;
   constexpr int OPAD = D + 4;
-  // Ring depth: with 64 rows three stages let three workgroups share a CU.
-  constexpr int kStages = RT >= 4 ? 3 : 4;
+  constexpr int kStages = ring_stages<RT>();
   static_assert(NTW >= 1, "tiles per wave");
 
   // The block ring; after the last block the same bytes stage the output rows.
@@ -287,10 +316,14 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   const int rt = wave % RT;
   const int cp = wave / RT;
   const int n0 = cp * NTW;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int r = blockIdx.z;
+  // Grid x = (request, KV head), y = split: consecutive workgroups, which the hardware
+  // deals round-robin to the eight XCDs, are different (request, head) pairs of the same
+  // split, so long and short requests spread evenly over the XCDs, and the high splits
+  // (empty for short requests) are dispatched last.
   const int Hkv = a.num_kv_heads;
+  const int split = blockIdx.y;
+  const int h = blockIdx.x % Hkv;
+  const int r = blockIdx.x / Hkv;
   const int G = a.num_q_heads / Hkv;
 
   const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
@@ -357,15 +390,33 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     __syncthreads();
   }
 
-  // Block b of the split: K and V byte addresses (wave-uniform), first position and the
-  // verify tokens that selected it.
-  auto locate = [&](int b, uint64_t& kbase, uint64_t& vbase, int& pos0, int& mask) {
+  // Metadata of block b as stored in LDS (wave-uniform values, still in vector registers).
+  // It is fetched one block ahead of its use, so the read's latency hides under compute.
+  struct RawMeta {
+    int a, b, c;
+  };
+  auto fetch = [&](int b) {
+    RawMeta m;
     if constexpr (SPARSE) {
       const int e = base + (b >> 2);
+      m.a = ul.upage[e];
+      m.b = ul.uphys[e];
+      m.c = ul.umask[e];
+    } else {
+      m.a = ul.xk[b];
+      m.b = m.c = 0;
+    }
+    return m;
+  };
+  // Block b's K and V byte addresses, first position and the verify tokens that selected
+  // it, all in scalar registers.
+  auto resolve = [&](const RawMeta& m, int b, uint64_t& kbase, uint64_t& vbase, int& pos0,
+                     int& mask) {
+    if constexpr (SPARSE) {
       const int quarter = b & 3;
-      const int p = __builtin_amdgcn_readfirstlane(ul.upage[e]);
-      mask = __builtin_amdgcn_readfirstlane(ul.umask[e]);
-      const int phys = __builtin_amdgcn_readfirstlane(ul.uphys[e]);
+      const int p = __builtin_amdgcn_readfirstlane(m.a);
+      const int phys = __builtin_amdgcn_readfirstlane(m.b);
+      mask = __builtin_amdgcn_readfirstlane(m.c);
       pos0 = p * kPage + quarter * kSub;
       const uint64_t off = static_cast<uint64_t>(
           (static_cast<int64_t>(phys) * ss.page_stride +
@@ -373,13 +424,15 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
       kbase = reinterpret_cast<uint64_t>(ss.k) + off;
       vbase = reinterpret_cast<uint64_t>(ss.v) + off;
     } else {
-      int64_t xk = __builtin_amdgcn_readfirstlane(ul.xk[b]);
+      int64_t xk = __builtin_amdgcn_readfirstlane(m.a);
       mask = xk < 0 ? 0 : ~0;       // an index outside the pool reads page 0, masked out
       xk = xk < 0 ? 0 : xk;
       const int64_t xv = xk + 4;
       pos0 = (base + b) * kSub;
-      kbase = reinterpret_cast<uint64_t>(ds.root) + static_cast<uint64_t>((xk * Hkv + h) * kSub * D * Gm::EB);
-      vbase = reinterpret_cast<uint64_t>(ds.root) + static_cast<uint64_t>((xv * Hkv + h) * kSub * D * Gm::EB);
+      kbase = reinterpret_cast<uint64_t>(ds.root) +
+              static_cast<uint64_t>((xk * Hkv + h) * kSub * D * Gm::EB);
+      vbase = reinterpret_cast<uint64_t>(ds.root) +
+              static_cast<uint64_t>((xv * Hkv + h) * kSub * D * Gm::EB);
     }
   };
 
@@ -396,38 +449,45 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   for (int n = 0; n < NTW; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // First position and selecting tokens of the block each ring slot holds.
+  int slot_pos[kStages], slot_mask[kStages];
+#pragma unroll
+  for (int j = 0; j < kStages; ++j) slot_pos[j] = slot_mask[j] = 0;
+
   // Prologue: blocks 0 .. kStages - 2 in flight.
 #pragma unroll
-  for (int b = 0; b < kStages - 1; ++b) {
-    if (b < nblk) {
+  for (int j = 0; j < kStages - 1; ++j) {
+    if (j < nblk) {
       uint64_t kb, vb;
-      int p0, mk;
-      locate(b, kb, vb, p0, mk);
-      copier.issue(kb, vb, ring_lds + b * Gm::BLOCK);
+      resolve(fetch(j), j, kb, vb, slot_pos[j], slot_mask[j]);
+      copier.issue(kb, vb, ring_lds + j * Gm::BLOCK);
     }
   }
+  RawMeta next{0, 0, 0};
+  if (kStages - 1 < nblk) next = fetch(kStages - 1);
 
-  for (int b = 0; b < nblk; ++b) {
+  // Block b lives in slot b % kStages; the loop runs kStages blocks per trip so that every
+  // slot offset and slot register index is a compile-time constant.
+  auto step = [&](auto slot_c, int b) {
+    constexpr int u = decltype(slot_c)::value;
+    constexpr int un = (u + kStages - 1) % kStages;   // slot of block b - 1 = of b + kStages - 1
+    // This wave's LDS reads of block b - 1 and the metadata fetch are complete and its
+    // copies of block b have landed; the barrier extends both facts to every wave.
+    wait_lgkmcnt0();
+    wait_blocks<Gm::LPT, kStages - 2>(min(nblk - 1 - b, kStages - 2));
+    ring_barrier();
     const int bn = b + kStages - 1;
     if (bn < nblk) {
       uint64_t kbn, vbn;
-      int p0, mk;
-      locate(bn, kbn, vbn, p0, mk);
-      copier.issue(kbn, vbn, ring_lds + (bn % kStages) * Gm::BLOCK);
+      resolve(next, bn, kbn, vbn, slot_pos[un], slot_mask[un]);
+      copier.issue(kbn, vbn, ring_lds + un * Gm::BLOCK);
+      if (bn + 1 < nblk) next = fetch(bn + 1);
     }
-    // Wait for this wave's copies of block b; the barrier makes all waves' copies visible.
-    const int after = min(nblk - 1 - b, kStages - 1);   // blocks issued after b
-    if (after >= 3) wait_vmcnt<(kStages >= 4 ? 3 : 0) * Gm::LPT>();
-    else if (after == 2) wait_vmcnt<2 * Gm::LPT>();
-    else if (after == 1) wait_vmcnt<Gm::LPT>();
-    else wait_vmcnt<0>();
-    ring_barrier();
 
-    const char* kb = ring + (b % kStages) * Gm::BLOCK;
+    const char* kb = ring + u * Gm::BLOCK;
     const char* vb = kb + Gm::HALF;
-    uint64_t kb_unused, vb_unused;
-    int pos0, mask;
-    locate(b, kb_unused, vb_unused, pos0, mask);
+    const int pos0 = slot_pos[u];
+    const int mask = slot_mask[u];
     const bool inside = pos0 + kSub <= first_bound && (mask & all_tokens) == all_tokens;
 
     // scores S^T for this wave's row tile (unscaled)
@@ -499,9 +559,13 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
       v_runs<D, KDT, NTW, true>(vb, i, q, n0, pos0, kv, vraw);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) o[n] = mfma16(v_operand<KDT>(vraw, n), pb, o[n]);
-    // The slot of block b is refilled next iteration: every wave's reads of it are done.
-    wait_lgkmcnt0();
-    ring_barrier();
+  };
+
+  for (int b0 = 0; b0 < nblk; b0 += kStages) {
+    static_for<kStages>([&](auto slot_c) {
+      const int b = b0 + decltype(slot_c)::value;
+      if (b < nblk) step(slot_c, b);
+    });
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -557,7 +621,7 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
 template <int RT, int D, int KDT, bool SPARSE>
 hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
                     hipStream_t s) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.B);
+  dim3 grid(a.num_kv_heads * a.B, a.num_splits);
   hipLaunchKernelGGL((sdv_attn_stream_kernel<RT, D, KDT, SPARSE>), grid, dim3(256), 0, s, a, ds, ss);
   return hipGetLastError();
 }

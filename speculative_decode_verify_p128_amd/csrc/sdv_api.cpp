@@ -58,6 +58,10 @@ int32_t check_query_side(const void* q, const int32_t* qo_indptr, const int32_t*
   if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
     return fail(SDV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 num_q_heads, num_kv_heads);
+  if (static_cast<int64_t>(B) * num_q_heads > INT32_MAX ||
+      static_cast<int64_t>(B) * max_qo_len > INT32_MAX)
+    return fail(SDV_ERR_SHAPE, "batch %d too large for %d heads and max_qo_len %d", B,
+                num_q_heads, max_qo_len);
   if (B > 0 && (!q || !qo_indptr || !kv_len))
     return fail(SDV_ERR_NULL_POINTER, "q, qo_indptr and kv_len must be non-null");
   return SDV_OK;
