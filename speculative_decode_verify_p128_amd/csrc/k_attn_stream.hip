@@ -200,11 +200,11 @@ __device__ __forceinline__ bf16x8 k_operand(const char* kb, int tt, int s, int i
 
 // A operands of O^T += V^T P^T for this wave's output tiles n0 .. n0 + NTW - 1: element
 // e of tile n is V[ptok(q, e)][NT * i + n0 + n].  v_runs reads, for each of the lane's 8
-// tokens, its run of NTW channels (positions past kv_len read as 0: stale storage must
-// not reach P * V); v_operand interleaves bf16 runs into an operand with byte
-// permutes, or widens fp8 runs exactly to bf16.
-template <int D, int KDT, int NTW, bool TAIL>
-__device__ __forceinline__ void v_runs(const char* vb, int i, int q, int n0, int pos0, int kv,
+// tokens, its run of NTW channels; v_zero_tail clears the runs of positions past kv_len;
+// v_operand interleaves bf16 runs into an operand with byte permutes, or widens fp8 runs
+// exactly to bf16.
+template <int D, int KDT, int NTW>
+__device__ __forceinline__ void v_runs(const char* vb, int i, int q, int n0,
                                        uint32_t (&raw)[8][4]) {
   using Gm = Geo<D, KDT>;
   constexpr int NBYTES = NTW * Gm::EB;
@@ -214,8 +214,13 @@ __device__ __forceinline__ void v_runs(const char* vb, int i, int q, int n0, int
     const int byte = (Gm::NT * i + n0) * Gm::EB;
     raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
     lds_read<NBYTES>(vb + Gm::at(tok, byte), raw[e]);
-    if (TAIL && pos0 + tok >= kv) raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
   }
+}
+
+__device__ __forceinline__ void v_zero_tail(int q, int pos0, int kv, uint32_t (&raw)[8][4]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (pos0 + ptok(q, e) >= kv) raw[e][0] = raw[e][1] = raw[e][2] = raw[e][3] = 0u;
 }
 
 template <int KDT>
@@ -476,6 +481,19 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     wait_lgkmcnt0();
     wait_blocks<Gm::LPT, kStages - 2>(min(nblk - 1 - b, kStages - 2));
     ring_barrier();
+
+    // All of this wave's reads of the block first, so their latency runs under the copy
+    // issue below and under the score products.
+    const char* kb = ring + u * Gm::BLOCK;
+    const char* vb = kb + Gm::HALF;
+    bf16x8 kop[2][STEPS];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) kop[tt][s] = k_operand<D, KDT>(kb, tt, s, i, q);
+    uint32_t vraw[8][4];
+    v_runs<D, KDT, NTW>(vb, i, q, n0, vraw);
+
     const int bn = b + kStages - 1;
     if (bn < nblk) {
       uint64_t kbn, vbn;
@@ -484,8 +502,6 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
       if (bn + 1 < nblk) next = fetch(bn + 1);
     }
 
-    const char* kb = ring + u * Gm::BLOCK;
-    const char* vb = kb + Gm::HALF;
     const int pos0 = slot_pos[u];
     const int mask = slot_mask[u];
     const bool inside = pos0 + kSub <= first_bound && (mask & all_tokens) == all_tokens;
@@ -496,8 +512,7 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     for (int tt = 0; tt < 2; ++tt) {
       sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s)
-        sacc[tt] = mfma16(k_operand<D, KDT>(kb, tt, s, i, q), qb[s], sacc[tt]);
+      for (int s = 0; s < STEPS; ++s) sacc[tt] = mfma16(kop[tt][s], qb[s], sacc[tt]);
     }
     float mx = -INFINITY;
     if (inside) {
@@ -551,12 +566,9 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     const bf16x8 pb = __builtin_bit_cast(
         bf16x8, make_uint4(pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
                            pack2_bf16(p[6], p[7])));
-    // value product for this wave's output tiles
-    uint32_t vraw[8][4];
-    if (pos0 + kSub <= kv)
-      v_runs<D, KDT, NTW, false>(vb, i, q, n0, pos0, kv, vraw);
-    else
-      v_runs<D, KDT, NTW, true>(vb, i, q, n0, pos0, kv, vraw);
+    // value product for this wave's output tiles; positions past kv_len read as 0 (stale
+    // storage must not reach P * V, even times a zero probability)
+    if (pos0 + kSub > kv) v_zero_tail(q, pos0, kv, vraw);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) o[n] = mfma16(v_operand<KDT>(vraw, n), pb, o[n]);
   };
