@@ -36,7 +36,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--splits", type=int, default=None, help="override sparse num_splits")
     p.add_argument("--dense-splits", type=int, default=None)
-    p.add_argument("--family", type=int, default=0, help="0 auto, 1 vector-ALU kernels")
+    p.add_argument("--family", type=int, default=0,
+                   help="attention kernels: 0 auto, 1 vector-ALU, 2 register-streaming MFMA, "
+                        "3 per-wave LDS stream, 4 workgroup LDS ring")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle sample")
@@ -104,9 +106,10 @@ def dense_algorithmic_bytes(case):
 KERNEL_SOURCES = {
     "proxy_page_scores": ("k_proxy.hip", "device.h"),
     "ladder_topk_pages": ("k_topk.hip", "device.h"),
-    "verify_attention_sparse": ("k_attn_stream.hip", "sparse_union.h", "k_small.hip", "device.h",
-                                "sdv_api.cpp"),
-    "verify_attention_dense": ("k_attn_stream.hip", "k_small.hip", "device.h", "sdv_api.cpp"),
+    "verify_attention_sparse": ("k_attn_waves.hip", "mfma_attn.h", "sparse_union.h", "k_small.hip",
+                                "device.h", "internal.h", "sdv_api.cpp"),
+    "verify_attention_dense": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
+                               "internal.h", "sdv_api.cpp"),
 }
 
 

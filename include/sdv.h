@@ -162,10 +162,16 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
  * qo_indptr    device int32 [B+1];  kv_len device int32 [B].
  * view         host: from kv_subpage_view_init.
  * sub_offsets  device int32 [B][2][max_sub_pages]; kv_len[r] <= 32 * max_sub_pages.
- * num_splits   >= 1: each (request, KV head) splits the sub-page capacity
- *              [0, max_sub_pages) into num_splits equal contiguous chunks (trailing
- *              chunks of short requests are empty); partials are merged by the
- *              log-sum-exp combine.  num_splits = 1 needs no workspace.
+ * num_splits   >= 1: the most partial results per (request, KV head).  Each request's
+ *              sub-pages are cut into contiguous chunks of one length C for the whole
+ *              call, chunk s being split s; partials are merged by the log-sum-exp
+ *              combine.  The matrix-core kernels take C = about the call's total
+ *              sub-pages over all (request, KV head) pairs divided by the workgroups
+ *              the GPU holds at once (so long and short requests balance), at least
+ *              ceil(longest request's sub-pages / num_splits) and at most 1024; the
+ *              other kernels take C = ceil(max_sub_pages / num_splits).
+ *              Trailing splits of short requests are empty.  num_splits = 1 needs no
+ *              workspace.
  * workspace    device, >= sdv_workspace_bytes(B*max_qo_len, num_q_heads, head_dim,
  *              num_splits) bytes (nullable when that is 0).
  * out          device [rows][num_q_heads][head_dim], out_dt (F32 or BF16).
@@ -285,10 +291,12 @@ const char* sdv_status_string(int32_t status);
 /* Message of the calling thread's most recent failed call ("" if none). */
 const char* sdv_last_error(void);
 
-/* Kernel family selection, for cross-checking: 0 = automatic (matrix-core kernels fed
- * by the LDS block ring where supported), 1 = the vector-ALU kernels, 2 = the
- * matrix-core kernels that stream K/V through registers.  Process-wide; returns the
- * previous value. */
+/* Kernel family selection, for cross-checking: 0 = automatic (matrix-core kernels:
+ * one LDS block stream per wave for sparse attention, the workgroup-shared LDS block
+ * ring for dense attention; vector-ALU kernels for fp32), 1 = the vector-ALU kernels,
+ * 2 = the matrix-core kernels that stream K/V through registers, 3 = the per-wave
+ * LDS-stream kernels for both, 4 = the workgroup-shared LDS-ring kernels for both.
+ * Process-wide; returns the previous value. */
 int32_t sdv_set_kernel_family(int32_t family);
 
 /* Measurement helper: fill `bytes` (multiple of 16) of device memory with a 32-bit

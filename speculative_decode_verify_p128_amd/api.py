@@ -226,8 +226,8 @@ def lse_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, *, out_dty
 
 
 def set_kernel_family(family: int) -> int:
-    """0 = automatic (LDS-ring matrix-core kernels), 1 = vector-ALU kernels,
-    2 = register-streaming matrix-core kernels."""
+    """0 = automatic, 1 = vector-ALU kernels, 2 = register-streaming matrix-core
+    kernels, 3 = per-wave LDS-stream kernels, 4 = workgroup-shared LDS-ring kernels."""
     return int(L.load().sdv_set_kernel_family(family))
 
 

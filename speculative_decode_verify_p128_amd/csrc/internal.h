@@ -49,7 +49,31 @@ struct AttnArgs {
   void* out;
   int32_t out_dt;
   int32_t* dev_err;
+  int32_t target_wgs;           // workgroups the GPU holds at once for the chosen kernel
 };
+
+// Compute units of the current device (cached per device; 0 on error).
+inline int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev >= 64) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  }
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  return n;
+}
+
+// Workgroups of `kernel` (256 threads, static LDS only) one compute unit holds at once.
+template <typename K>
+int resident_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
 
 hipError_t launch_subpage_offsets(const int32_t* block_table, int32_t B, int32_t max_blocks,
                                   int32_t bt_stride, int32_t slot_stride, int32_t num_slots,
@@ -81,6 +105,11 @@ hipError_t launch_attn_sparse_mfma(const AttnArgs& a, const SparseSource& src, h
 constexpr int kStreamMaxDenseBlocks = 1024;
 hipError_t launch_attn_dense_stream(const AttnArgs& a, const DenseSource& src, hipStream_t s);
 hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+
+// Matrix-core attention with one block stream per wave (every wave holds all query rows
+// and takes every fourth block; same support as above, dense up to 1024 blocks per split).
+hipError_t launch_attn_dense_waves(const AttnArgs& a, const DenseSource& src, hipStream_t s);
+hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 
 // Rows [*row_begin_dev, *row_end_dev) are combined (all rows_cap rows when null).
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t num_splits,

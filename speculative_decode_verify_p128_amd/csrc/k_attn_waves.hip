@@ -1,0 +1,535 @@
+// Verify attention on the CDNA4 matrix cores, one block stream per wave (bf16 queries;
+// bf16 or fp8 K/V).
+//
+// What is computed: token t of request r, query head hq of KV head h attends the
+// positions j < bound(r,t) = kv_len - qo_len + t + 1 ("[TRTLLM-14093][feat] Eagle3
+// for M3 MSA path + CUDA graphs compatibility", MSA verify commit); dense keys come
+// through the P32 sub-page view of the draft layer's P128 pages ("[None][perf]
+// Default Minimax-m3 to unified draft-target kv manager ...", Description and item 2
+// Grouped-HND), sparse keys only from the pages the token selected.  Float32
+// accumulation; probabilities enter the value product as bf16.
+//
+// Work layout (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
+//   * One workgroup (4 waves) per (request, KV head, split).  Every wave holds all the
+//     query rows of the (request, KV head) — G x qo (token, head) pairs, row = t * G + g,
+//     in RT tiles of 16 — and takes every fourth 32-token block of the split.  Each K/V
+//     byte is therefore copied into LDS once and read from LDS once, by one wave, and a
+//     wave keeps its own online-softmax state; the waves never wait for each other until
+//     the end.
+//   * A wave streams its blocks through a private two-slot LDS ring with asynchronous
+//     global->LDS copies (global_load_lds_dwordx4, non-temporal): while a block is
+//     computed the next two are in flight.  Its waits are its own vmcnt / lgkmcnt waits;
+//     there is no workgroup barrier in the block loop.
+//   * Scores are computed transposed (S^T = K Q^T) for every row tile from one read of
+//     the K block, and one read and transpose of the V block serves the value product
+//     of every row tile (O^T += V^T P^T).
+//   * At the end the four waves' (max, sum, output) merge in a fixed order through LDS,
+//     and wave 0 writes the rows (or a normalised partial and its log-sum-exp for the
+//     split-KV combine) straight from registers: each lane holds a contiguous quarter of
+//     a row's channels.
+#include "mfma_attn.h"
+#include "sparse_union.h"
+
+namespace sdv {
+namespace {
+
+constexpr int kWaveSlots = 2;   // ring slots per wave
+
+// One wave's copy of a whole 32-token block (K then V) into a ring slot: 32 / RPI
+// asynchronous 16-byte-per-lane loads per half.  Lane l of instruction n lands at
+// half + (n * 64 + l) * 16, which is row n * RPI + l / CPR, chunk l % CPR of the
+// swizzled block; the lane reads the global chunk that belongs there.
+template <int D, int KDT>
+struct WaveCopier {
+  using Gm = Geo<D, KDT>;
+  static constexpr int PER_HALF = 32 / Gm::RPI;
+  static constexpr int NI = 2 * PER_HALF;        // loads per block
+  uint32_t off[PER_HALF];
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int n = 0; n < PER_HALF; ++n) {
+      const int row = n * Gm::RPI + lane / Gm::CPR;
+      const int gchunk = ((lane % Gm::CPR) ^ row) & (Gm::CPR - 1);
+      off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
+    }
+  }
+
+  // kbase, vbase: first byte of the block's K and V runs; slot_lds: LDS address of the
+  // slot.  All three are wave-uniform.
+  __device__ __forceinline__ void issue(uint64_t kbase, uint64_t vbase, uint32_t slot_lds) const {
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      const uint64_t base = hv ? vbase : kbase;
+#pragma unroll
+      for (int n = 0; n < PER_HALF; ++n) {
+        const uint32_t m0 = slot_lds + hv * Gm::HALF + n * 1024;
+        // Inline assembly, so that the compiler's wait insertion, which cannot tell ring
+        // slots apart, does not drain the copies in flight; this wave's own vmcnt waits
+        // order copies and reads.  M0 holds the copy's LDS base.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "s"(m0), "v"(off[n]), "s"(base)
+                     : "memory", "m0");
+#pragma clang diagnostic pop
+      }
+    }
+  }
+};
+
+// Merge buffer slot of (row, 16-byte piece k of the row): pieces are XOR-swizzled by the
+// row so that 16 lanes writing the same piece of 16 rows hit different banks.
+template <int D>
+__device__ __forceinline__ int merge_index(int row, int k) {
+  return row * (D / 4) + (k ^ (row & 15));
+}
+
+template <int RT, int D, int KDT, bool SPARSE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
+  using Gm = Geo<D, KDT>;
+  using Cp = WaveCopier<D, KDT>;
+  constexpr int STEPS = Gm::STEPS;
+  constexpr int NT = Gm::NT;
+  constexpr int ROWS = RT * 16;
+  constexpr int A = kWaveSlots;
+  constexpr int WAVE_RING = A * Gm::BLOCK;
+  constexpr int RING = 4 * WAVE_RING;
+  constexpr int MERGE = 2 * ROWS * D * 4;   // two regions of ROWS x D floats
+  static_assert(MERGE <= RING, "merge regions reuse the ring");
+  static_assert(D / 4 <= 32 && (D / 4) % 8 == 0, "a lane's quarter row");
+
+  __shared__ __attribute__((aligned(16))) char ring[RING];
+  __shared__ float M_lds[4][ROWS];
+  __shared__ float L_lds[4][ROWS];
+  __shared__ typename std::conditional<SPARSE, UnionLds, DenseMeta>::type ul;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i = lane & 15;
+  const int q = lane >> 4;
+  // Grid x = (request, KV head), y = split, so consecutive workgroups (dealt round-robin
+  // to the XCDs) are different (request, head) pairs of one split.
+  const int Hkv = a.num_kv_heads;
+  const int split = blockIdx.y;
+  const int h = blockIdx.x % Hkv;
+  const int r = blockIdx.x / Hkv;
+  const int G = a.num_q_heads / Hkv;
+
+  const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
+                                : static_cast<int64_t>(ds.max_sub_pages) * kSub;
+  const int row0 = a.qo_indptr[r];
+  const int qo = a.qo_indptr[r + 1] - row0;
+  const int kv = a.kv_len[r];
+  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
+  const bool bad_cap = !bad_len && kv > kv_cap;
+  if (bad_len || bad_cap) {
+    if (tid == 0 && split == 0 && h == 0)
+      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  const int nrows = qo * G;
+
+  // This lane's query row of every row tile (lane i of the tile), its token and bound.
+  int t_row[RT], bound_row[RT];
+  bf16x8 qb[RT][STEPS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + i;
+    const bool live = row < nrows;
+    t_row[rt] = live ? row / G : 0;
+    const int g_row = live ? row - t_row[rt] * G : 0;
+    bound_row[rt] = live ? kv - qo + t_row[rt] + 1 : 0;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(row0 + t_row[rt]) * a.num_q_heads + h * G + g_row) * D +
+                      q * (D / 4)) * 2;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const uint4 w = live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      qb[rt][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  // Q is complete before any copy is issued, so no wait inside the block loop has to
+  // account for it (the compiler does not see the copies).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
+
+  // This split's blocks, staged in LDS before any copy: a vector load of block metadata
+  // inside the loop would wait behind every copy in flight.
+  int nblk, base;
+  if constexpr (SPARSE) {
+    const int n_union = build_union(ul, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
+    const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
+    base = split * chunk;
+    nblk = 4 * max(0, min(n_union, base + chunk) - base);
+  } else {
+    __shared__ int chunk_lds;
+    const int chunk = dense_chunk(a, ds, &chunk_lds);
+    const int nb = (kv + kSub - 1) / kSub;
+    base = split * chunk;
+    nblk = max(0, min(nb, base + chunk) - base);
+    const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
+    for (int b = tid; b < nblk; b += 256) {
+      const int32_t xk = offs[base + b];
+      const int32_t xv = offs[ds.max_sub_pages + base + b];
+      const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
+      if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+      ul.xk[b] = ok ? xk : -1;
+    }
+    __syncthreads();
+  }
+  // This wave's blocks: split-local b = wave + 4 j, j < nbw.
+  const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;
+
+  struct RawMeta {
+    int a, b, c;
+  };
+  auto fetch = [&](int b) {
+    RawMeta m;
+    if constexpr (SPARSE) {
+      const int e = base + (b >> 2);
+      m.a = ul.upage[e];
+      m.b = ul.uphys[e];
+      m.c = ul.umask[e];
+    } else {
+      m.a = ul.xk[b];
+      m.b = m.c = 0;
+    }
+    return m;
+  };
+  auto resolve = [&](const RawMeta& m, int b, uint64_t& kbase, uint64_t& vbase, int& pos0,
+                     int& mask) {
+    if constexpr (SPARSE) {
+      const int quarter = b & 3;
+      const int p = __builtin_amdgcn_readfirstlane(m.a);
+      const int phys = __builtin_amdgcn_readfirstlane(m.b);
+      mask = __builtin_amdgcn_readfirstlane(m.c);
+      pos0 = p * kPage + quarter * kSub;
+      const uint64_t off = static_cast<uint64_t>(
+          (static_cast<int64_t>(phys) * ss.page_stride +
+           (static_cast<int64_t>(h) * kPage + quarter * kSub) * D) * Gm::EB);
+      kbase = reinterpret_cast<uint64_t>(ss.k) + off;
+      vbase = reinterpret_cast<uint64_t>(ss.v) + off;
+    } else {
+      int64_t xk = __builtin_amdgcn_readfirstlane(m.a);
+      mask = xk < 0 ? 0 : ~0;       // an index outside the pool reads page 0, masked out
+      xk = xk < 0 ? 0 : xk;
+      const int64_t xv = xk + 4;
+      pos0 = (base + b) * kSub;
+      kbase = reinterpret_cast<uint64_t>(ds.root) +
+              static_cast<uint64_t>((xk * Hkv + h) * kSub * D * Gm::EB);
+      vbase = reinterpret_cast<uint64_t>(ds.root) +
+              static_cast<uint64_t>((xv * Hkv + h) * kSub * D * Gm::EB);
+    }
+  };
+
+  Cp copier;
+  copier.init(lane);
+  char* wring = ring + wave * WAVE_RING;
+  const uint32_t wring_lds = lds_address(wring);
+  const int all_tokens = qo >= 32 ? ~0 : (1 << qo) - 1;
+  const int first_bound = kv - qo + 1;
+
+  f32x4 o[RT][NT];
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+  }
+
+  int slot_pos[A], slot_mask[A];
+#pragma unroll
+  for (int u = 0; u < A; ++u) {
+    slot_pos[u] = slot_mask[u] = 0;
+    if (u < nbw) {
+      uint64_t kb, vb;
+      resolve(fetch(wave + 4 * u), wave + 4 * u, kb, vb, slot_pos[u], slot_mask[u]);
+      copier.issue(kb, vb, wring_lds + u * Gm::BLOCK);
+    }
+  }
+  RawMeta next{0, 0, 0};
+  if (A < nbw) next = fetch(wave + 4 * A);
+
+  auto step = [&](auto slot_c, int j) {
+    constexpr int u = decltype(slot_c)::value;
+    // This wave's copies of block j have landed (those of later blocks may not have).
+    wait_blocks<Cp::NI, A - 1>(min(nbw - 1 - j, A - 1));
+    const char* kb = wring + u * Gm::BLOCK;
+    const char* vb = kb + Gm::HALF;
+    bf16x8 kop[2][STEPS];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) kop[tt][s] = k_operand<D, KDT>(kb, tt, s, i, q);
+    uint32_t vraw[8][4];
+    v_runs<D, KDT, NT>(vb, i, q, 0, vraw);
+    const int pos0 = slot_pos[u];
+    const int mask = slot_mask[u];
+    // The slot's reads have returned: refill it with block j + A.
+    wait_lgkmcnt0();
+    if (j + A < nbw) {
+      const int bn = wave + 4 * (j + A);
+      uint64_t kbn, vbn;
+      resolve(next, bn, kbn, vbn, slot_pos[u], slot_mask[u]);
+      copier.issue(kbn, vbn, wring_lds + u * Gm::BLOCK);
+      if (j + A + 1 < nbw) next = fetch(bn + 4);
+    }
+    const bool inside = pos0 + kSub <= first_bound && (mask & all_tokens) == all_tokens;
+
+    // Row tiles one at a time: scores S^T (unscaled), the lazy rescale and the
+    // probabilities, so that only one tile's scores are live.  A row's reference maximum
+    // moves only when a score passes it by more than 2^8 (probabilities stay <= 256); the
+    // cross-lane maximum runs only when some lane's partial maximum passed it.  The
+    // scale is positive, so it commutes with max.  Masked scores are -inf and give 0; a
+    // row with no live score yet keeps m = -inf and has only masked scores here.
+    bf16x8 pb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 sacc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mfma16(kop[tt][s], qb[rt][s], sacc[tt]);
+      float mx = -INFINITY;
+      if (inside) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[tt][e]);
+      } else {
+        const int bnd = ((mask >> t_row[rt]) & 1) ? bound_row[rt] : 0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int pos = pos0 + tt * 16 + 4 * q + e;
+            const float sv = pos < bnd ? sacc[tt][e] : -INFINITY;
+            sacc[tt][e] = sv;
+            mx = fmaxf(mx, sv);
+          }
+      }
+      const float ms = mx * qk_scale;
+      if (__any(ms > m_run[rt] + kRescaleLog2)) {
+        float mr = fmaxf(ms, __shfl_xor(ms, 16, kWave));
+        mr = fmaxf(mr, __shfl_xor(mr, 32, kWave));
+        if (mr > m_run[rt] + kRescaleLog2) {
+          const float alpha = m_run[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rt] - mr);
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) o[rt][n] *= alpha;
+          m_run[rt] = mr;
+        }
+      }
+      const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][e], qk_scale, -m_use));
+        p[e + 4] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][e], qk_scale, -m_use));
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ls += p[e];
+      l_run[rt] += ls;
+      pb[rt] = __builtin_bit_cast(
+          bf16x8, make_uint4(pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]),
+                             pack2_bf16(p[4], p[5]), pack2_bf16(p[6], p[7])));
+    }
+    // value product; positions past kv_len read as 0 (stale storage must not reach P * V)
+    if (pos0 + kSub > kv) v_zero_tail(q, pos0, kv, vraw);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const bf16x8 vop = v_operand<KDT>(vraw, n);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) o[rt][n] = mfma16(vop, pb[rt], o[rt][n]);
+    }
+  };
+
+  for (int j0 = 0; j0 < nbw; j0 += A) {
+    static_for<A>([&](auto slot_c) {
+      const int j = j0 + decltype(slot_c)::value;
+      if (j < nbw) step(slot_c, j);
+    });
+  }
+  wait_vmcnt<0>();
+
+  // ---- merge the four waves: reference max, sums, outputs (fixed order) ----
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    l_run[rt] += __shfl_xor(l_run[rt], 16, kWave);
+    l_run[rt] += __shfl_xor(l_run[rt], 32, kWave);
+    if (q == 0) {
+      M_lds[wave][rt * 16 + i] = m_run[rt];
+      L_lds[wave][rt * 16 + i] = l_run[rt];
+    }
+  }
+  __syncthreads();   // every wave is done with its ring; M and L are visible
+  float m_ref[RT], l_tot[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + i;
+    float mref = M_lds[0][row];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mref = fmaxf(mref, M_lds[w][row]);
+    float lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = M_lds[w][row];
+      lt += mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mref) * L_lds[w][row];
+    }
+    m_ref[rt] = mref;
+    l_tot[rt] = lt;
+    const float f = m_run[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rt] - mref);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[rt][n] *= f;
+  }
+  // Piece k = 4 n' ... of a lane: element e of tile n is channel NT * (4q + e) + n; the
+  // lane's 4 NT values form the contiguous channels q * D/4 .. q * D/4 + D/4 - 1, kept
+  // as D/16 pieces of 4 floats: piece k holds channels q * D/4 + 4k .. + 3.
+  float4* reg0 = reinterpret_cast<float4*>(ring);
+  float4* reg1 = reg0 + ROWS * D / 4;
+  auto lane_piece = [&](int rt, int k) {
+    // channels c = q*D/4 + 4k + c4, c4 = 0..3  ->  (e, n) with NT*(4q+e) + n = c
+    float4 v;
+    float* vv = reinterpret_cast<float*>(&v);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int c = 4 * k + c4;        // 0 .. D/4 - 1 within the lane's quarter
+      vv[c4] = o[rt][c % NT][c / NT];
+    }
+    return v;
+  };
+  auto add_piece = [&](int rt, int k, const float4& v) {
+    const float* vv = reinterpret_cast<const float*>(&v);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int c = 4 * k + c4;
+      o[rt][c % NT][c / NT] += vv[c4];
+    }
+  };
+  constexpr int KP = D / 16;   // pieces per lane per row
+  auto put = [&](float4* region) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int k = 0; k < KP; ++k)
+        region[merge_index<D>(rt * 16 + i, q * KP + k)] = lane_piece(rt, k);
+  };
+  auto take = [&](const float4* region) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int k = 0; k < KP; ++k) add_piece(rt, k, region[merge_index<D>(rt * 16 + i, q * KP + k)]);
+  };
+  // (w0 + w1) + (w2 + w3)
+  if (wave == 1) put(reg0);
+  if (wave == 3) put(reg1);
+  __syncthreads();
+  if (wave == 0) take(reg0);
+  if (wave == 2) take(reg1);
+  __syncthreads();
+  if (wave == 2) put(reg0);
+  __syncthreads();
+  if (wave != 0) return;
+  take(reg0);
+
+  // ---- wave 0 writes: its lane holds channels q*D/4 .. +D/4-1 of row rt*16 + i ----
+  const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + i;
+    if (row >= nrows) continue;
+    const int t = row / G;
+    const int g = row - t * G;
+    const int hq = h * G + g;
+    const int64_t qrow = row0 + t;
+    const float L = l_tot[rt];
+    const float inv = L > 0.f ? a.v_scale / L : 0.f;
+    float v[D / 4];
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) v[c] = o[rt][c % NT][c / NT] * inv;
+    const int c0 = q * (D / 4);
+    if (a.num_splits == 1) {
+      const int64_t idx = (qrow * a.num_q_heads + hq) * D + c0;
+      if (a.out_dt == SDV_BF16) {
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + idx);
+#pragma unroll
+        for (int c = 0; c < D / 4; c += 8)
+          dst[c / 8] = make_uint4(pack2_bf16(v[c], v[c + 1]), pack2_bf16(v[c + 2], v[c + 3]),
+                                  pack2_bf16(v[c + 4], v[c + 5]), pack2_bf16(v[c + 6], v[c + 7]));
+      } else {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + idx);
+#pragma unroll
+        for (int c = 0; c < D / 4; c += 4) dst[c / 4] = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
+      }
+    } else {
+      // A row with no live position (an empty split) leaves its partial output unwritten:
+      // the combine skips rows whose log-sum-exp is -inf.
+      const int64_t unit = (static_cast<int64_t>(split) * rows_cap + qrow) * a.num_q_heads + hq;
+      if (L > 0.f) {
+        float4* dst = reinterpret_cast<float4*>(a.part_o + unit * D + c0);
+#pragma unroll
+        for (int c = 0; c < D / 4; c += 4) dst[c / 4] = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
+      }
+      if (q == 0) a.part_lse[unit] = L > 0.f ? (m_ref[rt] + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int RT, int D, int KDT, bool SPARSE>
+hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
+                    hipStream_t s) {
+  static const int per_cu = resident_per_cu(sdv_attn_waves_kernel<RT, D, KDT, SPARSE>);
+  AttnArgs args = a;
+  args.target_wgs = per_cu * device_cu_count();
+  dim3 grid(a.num_kv_heads * a.B, a.num_splits);
+  hipLaunchKernelGGL((sdv_attn_waves_kernel<RT, D, KDT, SPARSE>), grid, dim3(256), 0, s, args, ds, ss);
+  return hipGetLastError();
+}
+
+template <bool SPARSE>
+hipError_t dispatch(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
+                    hipStream_t s) {
+  const int rows = a.max_qo_len * (a.num_q_heads / a.num_kv_heads);
+  const int rt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+#define SDV_WAVES_CASE(RTV, DV, KDTV)                                                  \
+  if (rt == RTV && a.head_dim == DV && a.kv_dt == KDTV)                                \
+    return launch_t<RTV, DV, KDTV, SPARSE>(a, ds, ss, s);
+  SDV_WAVES_CASE(1, 128, SDV_BF16)
+  SDV_WAVES_CASE(2, 128, SDV_BF16)
+  SDV_WAVES_CASE(4, 128, SDV_BF16)
+  SDV_WAVES_CASE(1, 64, SDV_BF16)
+  SDV_WAVES_CASE(2, 64, SDV_BF16)
+  SDV_WAVES_CASE(4, 64, SDV_BF16)
+  SDV_WAVES_CASE(1, 128, SDV_FP8_E4M3)
+  SDV_WAVES_CASE(2, 128, SDV_FP8_E4M3)
+  SDV_WAVES_CASE(4, 128, SDV_FP8_E4M3)
+  SDV_WAVES_CASE(1, 64, SDV_FP8_E4M3)
+  SDV_WAVES_CASE(2, 64, SDV_FP8_E4M3)
+  SDV_WAVES_CASE(4, 64, SDV_FP8_E4M3)
+#undef SDV_WAVES_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_dense_waves(const AttnArgs& a, const DenseSource& src, hipStream_t s) {
+  return dispatch<false>(a, src, SparseSource{}, s);
+}
+
+hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
+  return dispatch<true>(a, DenseSource{}, src, s);
+}
+
+}  // namespace sdv

@@ -123,7 +123,7 @@ const char* sdv_status_string(int32_t status) {
 const char* sdv_last_error(void) { return g_last_error.c_str(); }
 
 int32_t sdv_set_kernel_family(int32_t family) {
-  return g_family.exchange(family >= 0 && family <= 2 ? family : 0);
+  return g_family.exchange(family >= 0 && family <= 4 ? family : 0);
 }
 
 int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_table,
@@ -235,7 +235,8 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   hipError_t e;
   if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_dense_valu(a, src, stream);
   else if (fam == 2 || !stream_ok) e = sdv::launch_attn_dense_mfma(a, src, stream);
-  else e = sdv::launch_attn_dense_stream(a, src, stream);
+  else if (fam == 3) e = sdv::launch_attn_dense_waves(a, src, stream);
+  else e = sdv::launch_attn_dense_stream(a, src, stream);   // 0 (automatic) and 4
   if (e != hipSuccess) return hip_status(e, "verify_attention_dense launch");
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
@@ -357,7 +358,8 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
   hipError_t e;
   if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_sparse_valu(a, src, stream);
   else if (fam == 2) e = sdv::launch_attn_sparse_mfma(a, src, stream);
-  else e = sdv::launch_attn_sparse_stream(a, src, stream);
+  else if (fam == 4) e = sdv::launch_attn_sparse_stream(a, src, stream);
+  else e = sdv::launch_attn_sparse_waves(a, src, stream);
   if (e != hipSuccess) return hip_status(e, "verify_attention_sparse launch");
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),

@@ -71,7 +71,7 @@ def test_subpage_offsets_bad_slot_flags_and_maps_to_slot0():
     assert list(o[1, 0, 0:4]) == [0, 1, 2, 3] and list(o[0, 1, 4:8]) == [4, 5, 6, 7]
 
 
-@pytest.mark.parametrize("family", [0, 1, 2])
+@pytest.mark.parametrize("family", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("splits", [1, 2, 16])
 @pytest.mark.parametrize("w", DENSE_CASES, ids=lambda w: w.name)
 def test_dense_parity(w, splits, family):
@@ -136,7 +136,7 @@ def test_topk_integer_ties_from_given_scores():
     assert rows == w.batch * 4
 
 
-@pytest.mark.parametrize("family", [0, 1, 2])
+@pytest.mark.parametrize("family", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("splits", [1, 2, 16])
 @pytest.mark.parametrize("w", SPARSE_CASES, ids=lambda w: w.name)
 def test_sparse_parity(w, splits, family):
@@ -206,7 +206,7 @@ def _poison_stale_tail_hnd(pool, bt, kv_lens):
             pool[int(bt[r, kv // 128]), :, kv % 128:, :] = float("nan")
 
 
-@pytest.mark.parametrize("family", [0, 1, 2])
+@pytest.mark.parametrize("family", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("w", [SPARSE_S, LONG_S, RAGGED_S], ids=lambda w: w.name)
 def test_sparse_poison_never_read(w, family):
     sdv.set_kernel_family(family)
@@ -224,7 +224,7 @@ def test_sparse_poison_never_read(w, family):
     assert ok, worst
 
 
-@pytest.mark.parametrize("family", [0, 1, 2])
+@pytest.mark.parametrize("family", [0, 1, 2, 3, 4])
 def test_dense_poison_never_read(family):
     sdv.set_kernel_family(family)
     w = DENSE_S
