@@ -158,7 +158,8 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
  * Float32 accumulation.  (Sources: PR #17835 Description — the Eagle3 drafter reads
  * its KV through the non-owning sub-page view; PR #3 MSA verify commit — the ladder.)
  *
- * q            device [B*max_qo_len rows capacity][num_q_heads][head_dim], q_dt.
+ * q            device [B*max_qo_len rows capacity][num_q_heads][head_dim], q_dt;
+ *              16-byte aligned (every call that takes q checks this).
  * qo_indptr    device int32 [B+1];  kv_len device int32 [B].
  * view         host: from kv_subpage_view_init.
  * sub_offsets  device int32 [B][2][max_sub_pages]; kv_len[r] <= 32 * max_sub_pages.
@@ -174,7 +175,8 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
  *              workspace.
  * workspace    device, >= sdv_workspace_bytes(B*max_qo_len, num_q_heads, head_dim,
  *              num_splits) bytes (nullable when that is 0).
- * out          device [rows][num_q_heads][head_dim], out_dt (F32 or BF16).
+ * out          device [rows][num_q_heads][head_dim], out_dt (F32 or BF16); 16-byte
+ *              aligned.
  * Supported: q_dt F32 with F32 K/V; q_dt BF16 with BF16 or FP8 K/V; head_dim 64 or
  * 128; num_q_heads % num_kv_heads == 0; max_qo_len * G <= 64.
  */

@@ -73,16 +73,29 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   const int p_first = blockIdx.x * PPB;
   if (p_first >= n_pages_r) return;
 
-  // Stage this request's queries of KV head h as float: q_lds[(t * G + g) * D + c].
-  for (int i = threadIdx.x; i < qo * G * D; i += blockDim.x) {
-    const int t = i / (G * D);
-    const int rem = i - t * (G * D);
-    const int g = rem / D;
-    const int c = rem - g * D;
-    const int64_t src = (static_cast<int64_t>(row0 + t) * num_q_heads + h * G + g) * D + c;
-    q_lds[i] = q_dt == SDV_F32 ? reinterpret_cast<const float*>(q)[src]
-                               : __uint_as_float(static_cast<uint32_t>(
-                                     reinterpret_cast<const uint16_t*>(q)[src]) << 16);
+  // Stage this request's queries of KV head h as float: q_lds[(t * G + g) * D + c], eight
+  // channels (one 16- or 32-byte load) per thread and step.
+  for (int i8 = threadIdx.x; i8 < qo * G * (D / 8); i8 += blockDim.x) {
+    const int tg = i8 / (D / 8);
+    const int c0 = (i8 - tg * (D / 8)) * 8;
+    const int t = tg / G;
+    const int g = tg - t * G;
+    const int64_t src = (static_cast<int64_t>(row0 + t) * num_q_heads + h * G + g) * D + c0;
+    float* dst = q_lds + tg * D + c0;
+    if (q_dt == SDV_F32) {
+      const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + src);
+      const float4 x0 = s4[0], x1 = s4[1];
+      reinterpret_cast<float4*>(dst)[0] = x0;
+      reinterpret_cast<float4*>(dst)[1] = x1;
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + src);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dst[2 * k] = __uint_as_float(ws[k] << 16);
+        dst[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+      }
+    }
   }
   __syncthreads();
 

@@ -64,6 +64,8 @@ int32_t check_query_side(const void* q, const int32_t* qo_indptr, const int32_t*
                 num_q_heads, max_qo_len);
   if (B > 0 && (!q || !qo_indptr || !kv_len))
     return fail(SDV_ERR_NULL_POINTER, "q, qo_indptr and kv_len must be non-null");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "q must be 16-byte aligned");
   return SDV_OK;
 }
 
@@ -219,6 +221,8 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   if (st) return st;
   if (B > 0 && (!sub_offsets || !out))
     return fail(SDV_ERR_NULL_POINTER, "sub_offsets and out must be non-null");
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "out must be 16-byte aligned");
   if (B == 0) return ok();
 
   sdv::AttnArgs a{};
@@ -343,6 +347,8 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
   if (st) return st;
   if (B > 0 && (!block_table || !topk_idx || !out))
     return fail(SDV_ERR_NULL_POINTER, "block_table, topk_idx and out must be non-null");
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "out must be 16-byte aligned");
   if (B == 0) return ok();
 
   sdv::AttnArgs a{};

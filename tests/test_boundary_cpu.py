@@ -107,6 +107,8 @@ def test_dense_rejections():
     need = L.load().sdv_workspace_bytes(8, 64, 128, 4)
     assert need >= 4 * 8 * 64 * 129 * 4
     assert _dense(v, splits=4, ws=FAKE, ws_bytes=need - 1) == L.SDV_ERR_WORKSPACE
+    assert _dense(v, q=C.c_void_p(0x10008)) == L.SDV_ERR_SHAPE    # q not 16-byte aligned
+    assert _dense(v, out=C.c_void_p(0x10004)) == L.SDV_ERR_SHAPE  # out not 16-byte aligned
     assert _dense(v, B=0) == L.SDV_OK                             # nothing to do
     empty = L.SubpageView()
     assert _dense(empty) != L.SDV_OK
@@ -157,11 +159,12 @@ def test_topk_rejections():
 
 
 def _sparse(kv, **kw):
-    a = dict(q_dt=L.SDV_BF16, B=2, max_qo=4, Hq=16, max_pages=8, bt=8, k=2, splits=1, out_dt=L.SDV_BF16)
+    a = dict(q=FAKE, q_dt=L.SDV_BF16, B=2, max_qo=4, Hq=16, max_pages=8, bt=8, k=2, splits=1,
+             out=FAKE, out_dt=L.SDV_BF16)
     a.update(kw)
     return L.load().verify_attention_sparse(
-        FAKE, a["q_dt"], FAKE, FAKE, a["B"], a["max_qo"], a["Hq"], C.byref(kv), FAKE,
-        a["max_pages"], a["bt"], FAKE, a["k"], 0.088, a["splits"], None, 0, FAKE, a["out_dt"],
+        a["q"], a["q_dt"], FAKE, FAKE, a["B"], a["max_qo"], a["Hq"], C.byref(kv), FAKE,
+        a["max_pages"], a["bt"], FAKE, a["k"], 0.088, a["splits"], None, 0, a["out"], a["out_dt"],
         None, None)
 
 
@@ -173,6 +176,8 @@ def test_sparse_rejections():
     assert _sparse(_kv(), max_pages=20000, bt=20000) == L.SDV_ERR_SHAPE
     assert _sparse(_kv(), splits=2) == L.SDV_ERR_WORKSPACE
     assert _sparse(_kv(), Hq=15) == L.SDV_ERR_SHAPE
+    assert _sparse(_kv(), q=C.c_void_p(0x10002)) == L.SDV_ERR_SHAPE   # q not 16-byte aligned
+    assert _sparse(_kv(), out=C.c_void_p(0x10008)) == L.SDV_ERR_SHAPE # out not 16-byte aligned
     assert _sparse(_kv(), B=0) == L.SDV_OK
 
 
