@@ -95,7 +95,7 @@ DENSE_BF16 = VerifyWorkload(
 SPARSE_BF16 = VerifyWorkload(
     name="sparse_bf16", batch=64, qo=4, kv=("uniform", 4096, 32768),
     num_q_heads=16, num_kv_heads=4, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
-    values="normal", top_k=16, num_splits=2)
+    values="normal", top_k=16, num_splits=1)
 
 # 4. Long-context sparse verify with fp8 e4m3 K/V and a 16-way split-KV.
 LONG_FP8 = VerifyWorkload(
