@@ -40,6 +40,8 @@ def parse():
                    help="attention kernels: 0 auto, 1 vector-ALU, 2 register-streaming MFMA, "
                         "3 per-wave LDS stream, 4 workgroup LDS ring")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-paged", action="store_true")
+    p.add_argument("--paged-splits", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -110,7 +112,21 @@ KERNEL_SOURCES = {
                                 "device.h", "internal.h", "sdv_api.cpp"),
     "verify_attention_dense": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
                                "internal.h", "sdv_api.cpp"),
+    "verify_attention_paged": ("k_attn_waves.hip", "mfma_attn.h", "k_small.hip", "device.h",
+                               "internal.h", "sdv_api.cpp"),
 }
+
+
+def paged_algorithmic_bytes(case):
+    """Dense over head-major pages: every valid K and V row of every (request, KV head)
+    once, Q read, O written, one block-table entry per page."""
+    w = case.w
+    e = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    eq = {"f32": 4, "bf16": 2}[w.q_dtype]
+    kv = case.lengths.kv
+    rows = case.lengths.total_q
+    return int(kv.sum()) * w.num_kv_heads * w.head_dim * e * 2 + \
+        2 * rows * w.num_q_heads * w.head_dim * eq + int((-(-kv // 128)).sum()) * 4
 
 
 def source_hash(*names):
@@ -365,6 +381,38 @@ def main():
                                                  source_hash(*KERNEL_SOURCES["verify_attention_dense"]))},
         }
         del d, outd, wsd
+
+    # ---- target dense layers: ladder attention over ordinary head-major P128 pages ----
+    if not args.no_paged:
+        wp = W.PAGED_BF16
+        psplits = args.paged_splits or wp.num_splits
+        pc = W.make_sparse_case(wp, device=dev)
+        pkv = sdv.PagedKV(pc.k_pool, pc.v_pool, pc.k_scale, pc.v_scale)
+        rows_p = wp.batch * wp.max_qo()
+        outp = torch.empty((rows_p, wp.num_q_heads, wp.head_dim), dtype=torch.bfloat16, device=dev)
+        wsp = sdv.alloc_workspace(rows_p, wp.num_q_heads, wp.head_dim, psplits, dev)
+
+        def k_paged():
+            sdv.verify_attention_paged(pc.q, pc.qo_indptr, pc.kv_len, pkv, pc.block_table,
+                                       max_qo_len=wp.max_qo(), softmax_scale=pc.softmax_scale,
+                                       num_splits=psplits, workspace=wsp, out=outp)
+
+        msp, perp, _ = time_steps([("verify_attention_paged", k_paged)], args.steps, args.warmup,
+                                  torch, flush)
+        pb = paged_algorithmic_bytes(pc)
+        gbs = pb / (perp["verify_attention_paged"]["avg_us"] * 1e-6) / 1e9
+        result["paged"] = {
+            "workload": "paged_bf16: target dense-layer verify over head-major P128 pages, batch 64, "
+                        "qo_len 4, 16 q / 4 kv heads, head_dim 128, kv_len U[4096, 32768]",
+            "value": pc.lengths.total_q / (msp * 1e-3), "unit": "verify tokens/s",
+            "ms_per_step": msp, "num_splits": psplits, "algorithmic_bytes": pb,
+            "kernels": perp,
+            "roofline": {"bound": "hbm", "kernel": "verify_attention_paged", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": load_traffic("verify_attention_paged", wp.name,
+                                                 source_hash(*KERNEL_SOURCES["verify_attention_paged"]))},
+        }
+        del pc, pkv, outp, wsp
 
     if not args.no_probe:
         result["attainable_read_GB_s"] = attainable_read_gbs(torch, sdv, dev)

@@ -270,6 +270,28 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
                                 int32_t* dev_err, hipStream_t stream);
 
 /*
+ * verify_attention_paged — dense GQA verify attention over ordinary head-major P128
+ * pages, for the target model's dense layers: token t, query head hq of KV head h
+ * attends every position j < bound(r,t) of its request (the ladder mask; at qo_len = 1
+ * it is ordinary decode attention).  Position j lives at token j % 128 of page
+ * block_table[r][j / 128].  (Source: PR #3 MSA verify commit — the dense layers 0-2
+ * take a ladder attention mask.)
+ *
+ * Arguments as in verify_attention_sparse, without topk_idx.  num_splits >= 1 as in
+ * verify_attention_dense with the capacity 4 * max_pages 32-token blocks; each split
+ * holds at most 1024 blocks, so ceil(4 * max_pages / num_splits) <= 1024.
+ * Supported: q BF16 with BF16 or FP8 K/V; head_dim 64 or 128; G * max_qo_len <= 64.
+ * Errors as verify_attention_sparse; SDV_ERR_DTYPE for F32 q.
+ */
+int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_paged_kv* kv,
+                               const int32_t* block_table, int32_t max_pages,
+                               int32_t bt_stride, float softmax_scale, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* out,
+                               int32_t out_dt, int32_t* dev_err, hipStream_t stream);
+
+/*
  * lse_combine — merge split-KV partials:  LSE = log sum_s exp(lse[s]),
  * out = sum_s exp(lse[s] - LSE) * partial_out[s]; partials with lse = -inf are
  * skipped; a row with no live partial gets 0.

@@ -40,14 +40,14 @@ from .view import (subpage_offsets, gather_subpage_view, gather_hnd, head_slice_
 from .attention import attend, dense_verify_request, sparse_verify_request, lse_combine
 from .proxy import proxy_scores_request, canonical_dot_f32
 from .topk import ladder_topk_request
-from .pipeline import (dense_verify_case, sparse_verify_case, dense_rows, sparse_rows,
-                       request_kv_dense, request_kv_sparse)
+from .pipeline import (dense_verify_case, sparse_verify_case, paged_verify_case, dense_rows,
+                       sparse_rows, request_kv_dense, request_kv_sparse)
 
 __all__ = [
     "ladder_bounds", "n_valid_pages", "decode_e4m3fn", "decode_bf16", "decode_store",
     "subpage_offsets", "gather_subpage_view", "gather_hnd", "head_slice_contiguous",
     "head_slice_grouped", "attend", "dense_verify_request", "sparse_verify_request",
     "lse_combine", "proxy_scores_request", "canonical_dot_f32", "ladder_topk_request",
-    "dense_verify_case", "sparse_verify_case", "dense_rows", "sparse_rows",
+    "dense_verify_case", "sparse_verify_case", "paged_verify_case", "dense_rows", "sparse_rows",
     "request_kv_dense", "request_kv_sparse",
 ]

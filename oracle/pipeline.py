@@ -64,6 +64,25 @@ def dense_rows(*args, **kwargs):
     return dense_verify_case(*args, **kwargs)
 
 
+def paged_verify_case(q_raw, q_dtype, qo_indptr, kv_len, k_pool_raw, v_pool_raw, kv_dtype,
+                      block_table, k_scale, v_scale, softmax_scale, requests=None):
+    """Dense verify attention over ordinary head-major P128 pages: the target's dense
+    layers, whose attention takes a ladder mask ([PR3] MSA verify commit: dense layers
+    0-2 get a ladder SDPA mask, the old math at qo_len = 1).  K/V of a request come
+    from its block table (position j in page block_table[r][j // 128], token j % 128).
+    out [sum(qo), Hq, d] float64; rows of requests outside `requests` stay NaN."""
+    q = _q_values(q_raw, q_dtype)
+    out = np.full(q.shape, np.nan)
+    B = len(kv_len)
+    for r in (range(B) if requests is None else requests):
+        a, b = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        kvr = int(kv_len[r])
+        k, v = request_kv_sparse(k_pool_raw, v_pool_raw, kv_dtype, block_table[r], kvr)
+        out[a:b] = dense_verify_request(q[a:b].astype(np.float64), k.astype(np.float64) * k_scale,
+                                        v.astype(np.float64) * v_scale, kvr, softmax_scale)
+    return out
+
+
 def sparse_verify_case(q_raw, q_dtype, qo_indptr, kv_len, k_pool_raw, v_pool_raw, kv_dtype,
                        block_table, k_scale, v_scale, top_k, softmax_scale, max_pages,
                        requests=None):

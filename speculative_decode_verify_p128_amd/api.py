@@ -208,6 +208,29 @@ def verify_attention_sparse(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: to
     return out
 
 
+def verify_attention_paged(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
+                           kv: PagedKV, block_table: torch.Tensor, *, max_qo_len: int,
+                           softmax_scale: float, num_splits: int = 1,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, out_dtype=None,
+                           dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense verify attention over every page below each token's ladder bound."""
+    _need(q, "q")
+    B = kv_len.numel()
+    rows_cap = B * max_qo_len
+    out = _out(out, q, rows_cap, out_dtype)
+    if workspace is None and num_splits > 1:
+        workspace = alloc_workspace(rows_cap, q.shape[1], q.shape[2], num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ckv = kv.c()
+    L.check(L.load().verify_attention_paged(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(ckv), _ptr(block_table), block_table.shape[1], block_table.stride(0),
+        softmax_scale, num_splits, _ptr(workspace), ws_bytes, _ptr(out), dtype_code(out.dtype),
+        _ptr(dev_err), _stream(q.device)))
+    return out
+
+
 def lse_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, *, out_dtype=torch.float32,
                 out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
                 want_lse: bool = False):

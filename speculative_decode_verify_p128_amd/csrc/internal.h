@@ -111,6 +111,12 @@ hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src,
 hipError_t launch_attn_dense_waves(const AttnArgs& a, const DenseSource& src, hipStream_t s);
 hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 
+// Dense verify attention over ordinary head-major P128 pages and a block table (every
+// position below the ladder bound), on the two matrix-core LDS kernels above; `src`
+// carries the pools and the block table, topk_idx is unused.
+hipError_t launch_attn_paged_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+hipError_t launch_attn_paged_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+
 // Rows [*row_begin_dev, *row_end_dev) are combined (all rows_cap rows when null).
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t num_splits,
                           int32_t rows_cap, const int32_t* row_begin_dev,

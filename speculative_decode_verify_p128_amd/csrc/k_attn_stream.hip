@@ -92,7 +92,7 @@ struct BlockCopier {
 template <int RT>
 constexpr int ring_stages() { return 4; }
 
-template <int RT, int D, int KDT, bool SPARSE>
+template <int RT, int D, int KDT, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
                                                              SparseSource ss) {
@@ -113,7 +113,9 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   float (*o_lds)[OPAD] = reinterpret_cast<float (*)[OPAD]>(ring);
   __shared__ float L_lds[ROWS];
   __shared__ float M_lds[ROWS];
-  __shared__ typename std::conditional<SPARSE, UnionLds, DenseMeta>::type ul;
+  using BL = BlockList<MODE, D, KDT>;
+  __shared__ typename BL::Lds ul;
+  __shared__ int chunk_lds;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -133,8 +135,8 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   const int r = blockIdx.x / Hkv;
   const int G = a.num_q_heads / Hkv;
 
-  const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
-                                : static_cast<int64_t>(ds.max_sub_pages) * kSub;
+  const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
+                                           : static_cast<int64_t>(ss.max_pages) * kPage;
   const int row0 = a.qo_indptr[r];
   const int qo = a.qo_indptr[r + 1] - row0;
   const int kv = a.kv_len[r];
@@ -172,77 +174,15 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
 
-  // This split's blocks and their addresses, staged in LDS before the copy pipeline
-  // starts: a vector load of block metadata inside the loop would wait behind every
-  // asynchronous copy in flight.
-  int nblk, base;
-  if constexpr (SPARSE) {
-    const int n_union = build_union(ul, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
-    const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
-    base = split * chunk;
-    nblk = 4 * max(0, min(n_union, base + chunk) - base);
-  } else {
-    __shared__ int chunk_lds;
-    const int chunk = dense_chunk(a, ds, &chunk_lds);
-    const int nb = (kv + kSub - 1) / kSub;
-    base = split * chunk;
-    nblk = max(0, min(nb, base + chunk) - base);
-    const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
-    for (int b = tid; b < nblk; b += 256) {
-      const int32_t xk = offs[base + b];
-      const int32_t xv = offs[ds.max_sub_pages + base + b];
-      const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
-      if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
-      ul.xk[b] = ok ? xk : -1;
-    }
-    __syncthreads();
-  }
+  BL bl;
+  bl.stage(ul, &chunk_lds, a, ds, ss, r, h, split, row0, qo, kv);
+  const int nblk = bl.nblk;
 
   // Metadata of block b as stored in LDS (wave-uniform values, still in vector registers).
   // It is fetched one block ahead of its use, so the read's latency hides under compute.
-  struct RawMeta {
-    int a, b, c;
-  };
-  auto fetch = [&](int b) {
-    RawMeta m;
-    if constexpr (SPARSE) {
-      const int e = base + (b >> 2);
-      m.a = ul.upage[e];
-      m.b = ul.uphys[e];
-      m.c = ul.umask[e];
-    } else {
-      m.a = ul.xk[b];
-      m.b = m.c = 0;
-    }
-    return m;
-  };
-  // Block b's K and V byte addresses, first position and the verify tokens that selected
-  // it, all in scalar registers.
-  auto resolve = [&](const RawMeta& m, int b, uint64_t& kbase, uint64_t& vbase, int& pos0,
-                     int& mask) {
-    if constexpr (SPARSE) {
-      const int quarter = b & 3;
-      const int p = __builtin_amdgcn_readfirstlane(m.a);
-      const int phys = __builtin_amdgcn_readfirstlane(m.b);
-      mask = __builtin_amdgcn_readfirstlane(m.c);
-      pos0 = p * kPage + quarter * kSub;
-      const uint64_t off = static_cast<uint64_t>(
-          (static_cast<int64_t>(phys) * ss.page_stride +
-           (static_cast<int64_t>(h) * kPage + quarter * kSub) * D) * Gm::EB);
-      kbase = reinterpret_cast<uint64_t>(ss.k) + off;
-      vbase = reinterpret_cast<uint64_t>(ss.v) + off;
-    } else {
-      int64_t xk = __builtin_amdgcn_readfirstlane(m.a);
-      mask = xk < 0 ? 0 : ~0;       // an index outside the pool reads page 0, masked out
-      xk = xk < 0 ? 0 : xk;
-      const int64_t xv = xk + 4;
-      pos0 = (base + b) * kSub;
-      kbase = reinterpret_cast<uint64_t>(ds.root) +
-              static_cast<uint64_t>((xk * Hkv + h) * kSub * D * Gm::EB);
-      vbase = reinterpret_cast<uint64_t>(ds.root) +
-              static_cast<uint64_t>((xv * Hkv + h) * kSub * D * Gm::EB);
-    }
-  };
+  auto fetch = [&](int b) { return bl.fetch(ul, b); };
+  auto resolve = [&](const typename BL::Raw& m, int b, uint64_t& kbase, uint64_t& vbase, int& pos0,
+                     int& mask) { bl.resolve(m, b, h, Hkv, ds, ss, kbase, vbase, pos0, mask); };
 
   BlockCopier<D, KDT> copier;
   copier.init(__builtin_amdgcn_readfirstlane(wave), lane);
@@ -271,7 +211,7 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
       copier.issue(kb, vb, ring_lds + j * Gm::BLOCK);
     }
   }
-  RawMeta next{0, 0, 0};
+  typename BL::Raw next{0, 0, 0};
   if (kStages - 1 < nblk) next = fetch(kStages - 1);
 
   // Block b lives in slot b % kStages; the loop runs kStages blocks per trip so that every
@@ -437,25 +377,25 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   }
 }
 
-template <int RT, int D, int KDT, bool SPARSE>
+template <int RT, int D, int KDT, int MODE>
 hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
                     hipStream_t s) {
-  static const int per_cu = resident_per_cu(sdv_attn_stream_kernel<RT, D, KDT, SPARSE>);
+  static const int per_cu = resident_per_cu(sdv_attn_stream_kernel<RT, D, KDT, MODE>);
   AttnArgs args = a;
   args.target_wgs = per_cu * device_cu_count();
   dim3 grid(a.num_kv_heads * a.B, a.num_splits);
-  hipLaunchKernelGGL((sdv_attn_stream_kernel<RT, D, KDT, SPARSE>), grid, dim3(256), 0, s, args, ds, ss);
+  hipLaunchKernelGGL((sdv_attn_stream_kernel<RT, D, KDT, MODE>), grid, dim3(256), 0, s, args, ds, ss);
   return hipGetLastError();
 }
 
-template <bool SPARSE>
+template <int MODE>
 hipError_t dispatch(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
                     hipStream_t s) {
   const int rows = a.max_qo_len * (a.num_q_heads / a.num_kv_heads);
   const int rt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
 #define SDV_STREAM_CASE(RTV, DV, KDTV)                                                 \
   if (rt == RTV && a.head_dim == DV && a.kv_dt == KDTV)                                \
-    return launch_t<RTV, DV, KDTV, SPARSE>(a, ds, ss, s);
+    return launch_t<RTV, DV, KDTV, MODE>(a, ds, ss, s);
   SDV_STREAM_CASE(1, 128, SDV_BF16)
   SDV_STREAM_CASE(2, 128, SDV_BF16)
   SDV_STREAM_CASE(4, 128, SDV_BF16)
@@ -475,11 +415,15 @@ hipError_t dispatch(const AttnArgs& a, const DenseSource& ds, const SparseSource
 }  // namespace
 
 hipError_t launch_attn_dense_stream(const AttnArgs& a, const DenseSource& src, hipStream_t s) {
-  return dispatch<false>(a, src, SparseSource{}, s);
+  return dispatch<kSrcView>(a, src, SparseSource{}, s);
 }
 
 hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
-  return dispatch<true>(a, DenseSource{}, src, s);
+  return dispatch<kSrcSparse>(a, DenseSource{}, src, s);
+}
+
+hipError_t launch_attn_paged_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
+  return dispatch<kSrcPaged>(a, DenseSource{}, src, s);
 }
 
 }  // namespace sdv

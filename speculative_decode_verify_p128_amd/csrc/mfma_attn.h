@@ -15,6 +15,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "sparse_union.h"
 
 namespace sdv {
 namespace {
@@ -212,14 +213,14 @@ __device__ __forceinline__ void wait_blocks(int after) {
 // at once, at least what num_splits splits need for the longest request, and at most
 // the 1024 blocks whose metadata a workgroup stages (the caller guarantees that
 // ceil(max_sub_pages / num_splits) fits).  All threads call; wave 0 reads every kv_len.
-__device__ inline int dense_chunk(const AttnArgs& a, const DenseSource& ds, int* slot_lds) {
+__device__ inline int dense_chunk(const AttnArgs& a, int max_blocks, int* slot_lds) {
   const int tid = threadIdx.x;
   if (tid < kWave) {
     int64_t sum = 0;
     int mx = 0;
     for (int rr = tid; rr < a.B; rr += kWave) {
       const int64_t k = a.kv_len[rr];
-      const int nb = static_cast<int>(k <= 0 ? 0 : min<int64_t>((k + kSub - 1) / kSub, ds.max_sub_pages));
+      const int nb = static_cast<int>(k <= 0 ? 0 : min<int64_t>((k + kSub - 1) / kSub, max_blocks));
       sum += nb;
       mx = max(mx, nb);
     }
@@ -244,12 +245,128 @@ __device__ inline int dense_chunk(const AttnArgs& a, const DenseSource& ds, int*
   return *slot_lds;
 }
 
-struct NoUnion {};
+// Where the 32-token blocks of a (request, KV head) come from.
+enum SourceMode : int {
+  kSrcView = 0,     // dense, through the P32 sub-page view of the draft layer
+  kSrcSparse = 1,   // sparse: the union of the P128 pages the tokens selected
+  kSrcPaged = 2,    // dense over ordinary head-major P128 pages and a block table
+};
 
-// P32 page index of the K sub-page of a dense split's blocks; -1 marks an index outside
-// the pool.  The view's geometry puts V one P128 page (four P32 pages) after K.
+// Per dense split: for kSrcView the P32 page index of each block's K sub-page (the view
+// puts V one P128 page, four P32 pages, after K); for kSrcPaged the physical P128 page
+// of each block.  -1 marks an index outside the pool.
 struct DenseMeta {
-  int32_t xk[kMaxDenseBlocks];
+  int32_t x[kMaxDenseBlocks];
+};
+
+// The block list of one workgroup's split, staged in LDS before any asynchronous copy
+// (a vector load of block metadata inside the copy pipeline would wait behind every
+// copy in flight), then read back one block ahead of use and resolved into scalar
+// addresses.
+template <int MODE, int D, int KDT>
+struct BlockList {
+  using Gm = Geo<D, KDT>;
+  using Lds = typename std::conditional<MODE == kSrcSparse, UnionLds, DenseMeta>::type;
+  struct Raw {
+    int a, b, c;
+  };
+  int base;    // first block (dense) or union entry (sparse) of the split
+  int nblk;    // blocks of the split
+
+  // All 256 threads call.  Sparse: the union of the pages the request's tokens chose,
+  // cut into num_splits near-equal runs.  Dense: runs of one length for the whole call.
+  __device__ __forceinline__ void stage(Lds& ul, int* chunk_lds, const AttnArgs& a,
+                                        const DenseSource& ds, const SparseSource& ss, int r,
+                                        int h, int split, int row0, int qo, int kv) {
+    const int tid = threadIdx.x;
+    if constexpr (MODE == kSrcSparse) {
+      const int n_union = build_union(ul, ss, r, h, a.num_kv_heads, row0, qo, kv, a.dev_err);
+      const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
+      base = split * chunk;
+      nblk = 4 * max(0, min(n_union, base + chunk) - base);
+    } else {
+      const int cap = MODE == kSrcView ? ds.max_sub_pages : 4 * ss.max_pages;
+      const int chunk = dense_chunk(a, cap, chunk_lds);
+      const int nb = (kv + kSub - 1) / kSub;
+      base = split * chunk;
+      nblk = max(0, min(nb, base + chunk) - base);
+      if constexpr (MODE == kSrcView) {
+        const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
+        for (int b = tid; b < nblk; b += 256) {
+          const int32_t xk = offs[base + b];
+          const int32_t xv = offs[ds.max_sub_pages + base + b];
+          const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
+          if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+          ul.x[b] = ok ? xk : -1;
+        }
+      } else {
+        const int32_t* bt = ss.block_table + static_cast<int64_t>(r) * ss.bt_stride;
+        for (int b = tid; b < nblk; b += 256) {
+          const int32_t phys = bt[(base + b) >> 2];
+          const bool ok = phys >= 0 && phys < ss.num_pages;
+          if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+          ul.x[b] = ok ? phys : -1;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Metadata of split-local block b as stored (wave-uniform values in vector registers).
+  __device__ __forceinline__ Raw fetch(const Lds& ul, int b) const {
+    Raw m;
+    if constexpr (MODE == kSrcSparse) {
+      const int e = base + (b >> 2);
+      m.a = ul.upage[e];
+      m.b = ul.uphys[e];
+      m.c = ul.umask[e];
+    } else {
+      m.a = ul.x[b];
+      m.b = m.c = 0;
+    }
+    return m;
+  }
+
+  // Block b's K and V byte addresses, first position and the verify tokens it serves, in
+  // scalar registers.  A block whose page index was out of range reads page 0 masked out.
+  __device__ __forceinline__ void resolve(const Raw& m, int b, int h, int Hkv,
+                                          const DenseSource& ds, const SparseSource& ss,
+                                          uint64_t& kbase, uint64_t& vbase, int& pos0,
+                                          int& mask) const {
+    if constexpr (MODE == kSrcSparse) {
+      const int quarter = b & 3;
+      const int p = __builtin_amdgcn_readfirstlane(m.a);
+      const int phys = __builtin_amdgcn_readfirstlane(m.b);
+      mask = __builtin_amdgcn_readfirstlane(m.c);
+      pos0 = p * kPage + quarter * kSub;
+      const uint64_t off = static_cast<uint64_t>(
+          (static_cast<int64_t>(phys) * ss.page_stride +
+           (static_cast<int64_t>(h) * kPage + quarter * kSub) * D) * Gm::EB);
+      kbase = reinterpret_cast<uint64_t>(ss.k) + off;
+      vbase = reinterpret_cast<uint64_t>(ss.v) + off;
+    } else if constexpr (MODE == kSrcView) {
+      int64_t xk = __builtin_amdgcn_readfirstlane(m.a);
+      mask = xk < 0 ? 0 : ~0;
+      xk = xk < 0 ? 0 : xk;
+      const int64_t xv = xk + 4;
+      pos0 = (base + b) * kSub;
+      kbase = reinterpret_cast<uint64_t>(ds.root) +
+              static_cast<uint64_t>((xk * Hkv + h) * kSub * D * Gm::EB);
+      vbase = reinterpret_cast<uint64_t>(ds.root) +
+              static_cast<uint64_t>((xv * Hkv + h) * kSub * D * Gm::EB);
+    } else {
+      int64_t phys = __builtin_amdgcn_readfirstlane(m.a);
+      mask = phys < 0 ? 0 : ~0;
+      phys = phys < 0 ? 0 : phys;
+      const int blk = base + b;
+      pos0 = blk * kSub;
+      const uint64_t off = static_cast<uint64_t>(
+          (phys * ss.page_stride + (static_cast<int64_t>(h) * kPage + (blk & 3) * kSub) * D) *
+          Gm::EB);
+      kbase = reinterpret_cast<uint64_t>(ss.k) + off;
+      vbase = reinterpret_cast<uint64_t>(ss.v) + off;
+    }
+  }
 };
 
 }  // namespace

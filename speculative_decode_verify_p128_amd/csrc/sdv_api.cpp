@@ -316,6 +316,65 @@ int32_t ladder_topk_pages(const float* scores, const int32_t* qo_indptr, const i
                     "ladder_topk_pages launch");
 }
 
+int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_paged_kv* kv,
+                               const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                               float softmax_scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* out, int32_t out_dt,
+                               int32_t* dev_err, hipStream_t stream) {
+  int32_t st = check_paged_kv(kv);
+  if (st) return st;
+  st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv->num_kv_heads);
+  if (st) return st;
+  if (q_dt != SDV_BF16 || (kv->kv_dtype != SDV_BF16 && kv->kv_dtype != SDV_FP8_E4M3))
+    return fail(SDV_ERR_DTYPE, "q dtype %d with kv dtype %d (supported: BF16 q, BF16/FP8 K/V)",
+                q_dt, kv->kv_dtype);
+  if (!valid_out_dtype(out_dt)) return fail(SDV_ERR_DTYPE, "out dtype %d", out_dt);
+  const int32_t G = num_q_heads / kv->num_kv_heads;
+  if (static_cast<int64_t>(G) * max_qo_len > 64)
+    return fail(SDV_ERR_SHAPE, "group %d x max_qo_len %d exceeds 64 query rows", G, max_qo_len);
+  if (max_qo_len > 32) return fail(SDV_ERR_SHAPE, "max_qo_len %d > 32", max_qo_len);
+  if (max_pages < 1 || max_pages > (1 << 20) || bt_stride < max_pages)
+    return fail(SDV_ERR_SHAPE, "max_pages %d (<= 2^20), bt_stride %d", max_pages, bt_stride);
+  if (num_splits < 1 || (4ll * max_pages + num_splits - 1) / num_splits > sdv::kStreamMaxDenseBlocks)
+    return fail(SDV_ERR_SHAPE, "num_splits %d too small: each split may hold at most %d "
+                "32-token blocks of the %d-page capacity", num_splits,
+                sdv::kStreamMaxDenseBlocks, max_pages);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
+  if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
+  st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, kv->head_dim, num_splits);
+  if (st) return st;
+  if (B > 0 && (!block_table || !out))
+    return fail(SDV_ERR_NULL_POINTER, "block_table and out must be non-null");
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "out must be 16-byte aligned");
+  if (B == 0) return ok();
+
+  sdv::AttnArgs a{};
+  a.q = q; a.q_dt = q_dt; a.qo_indptr = qo_indptr; a.kv_len = kv_len; a.B = B;
+  a.max_qo_len = max_qo_len; a.num_q_heads = num_q_heads; a.num_kv_heads = kv->num_kv_heads;
+  a.head_dim = kv->head_dim; a.kv_dt = kv->kv_dtype; a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale; a.softmax_scale = softmax_scale; a.num_splits = num_splits;
+  a.out = out; a.out_dt = out_dt; a.dev_err = dev_err;
+  split_workspace(workspace, rows_cap, num_q_heads, kv->head_dim, num_splits, &a.part_o, &a.part_lse);
+  sdv::SparseSource src{kv->k, kv->v, kv->page_stride, kv->num_pages, block_table, bt_stride,
+                        max_pages, nullptr, 0};
+  const int32_t fam = g_family.load();
+  hipError_t e = fam == 4 ? sdv::launch_attn_paged_stream(a, src, stream)
+                          : sdv::launch_attn_paged_waves(a, src, stream);
+  if (e != hipSuccess) return hip_status(e, "verify_attention_paged launch");
+  if (num_splits > 1) {
+    e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
+                            qo_indptr, qo_indptr + B, num_q_heads, kv->head_dim, out, out_dt,
+                            nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, "verify_attention_paged combine launch");
+  }
+  return ok();
+}
+
 int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                 const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                 int32_t num_q_heads, const sdv_paged_kv* kv,

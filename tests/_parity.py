@@ -52,6 +52,22 @@ class SparseRun:
                                            num_splits=num_splits, dev_err=dev_err)
 
 
+class PagedRun(SparseRun):
+    def attend_paged(self, num_splits=1, dev_err=None):
+        return sdv.verify_attention_paged(self.q, self.qo_indptr, self.kv_len, self.kv, self.bt,
+                                          max_qo_len=self.max_qo,
+                                          softmax_scale=self.c.softmax_scale,
+                                          num_splits=num_splits, dev_err=dev_err)
+
+
+def paged_oracle(c: W.SparseCase, requests=None):
+    w = c.w
+    return oracle.paged_verify_case(
+        raw_numpy(c.q), w.q_dtype, c.qo_indptr.numpy(), c.lengths.kv, raw_numpy(c.k_pool),
+        raw_numpy(c.v_pool), w.kv_dtype, c.block_table.numpy(), c.k_scale, c.v_scale,
+        c.softmax_scale, requests=requests)
+
+
 def sparse_oracle(c: W.SparseCase, requests=None, top_k=None):
     w = c.w
     return oracle.sparse_verify_case(

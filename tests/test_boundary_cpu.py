@@ -181,6 +181,27 @@ def test_sparse_rejections():
     assert _sparse(_kv(), B=0) == L.SDV_OK
 
 
+def _paged(kv, **kw):
+    a = dict(q=FAKE, q_dt=L.SDV_BF16, B=2, max_qo=4, Hq=16, max_pages=8, bt=8, splits=1,
+             out=FAKE, out_dt=L.SDV_BF16)
+    a.update(kw)
+    return L.load().verify_attention_paged(
+        a["q"], a["q_dt"], FAKE, FAKE, a["B"], a["max_qo"], a["Hq"], C.byref(kv), FAKE,
+        a["max_pages"], a["bt"], 0.088, a["splits"], None, 0, a["out"], a["out_dt"], None, None)
+
+
+def test_paged_rejections():
+    assert _paged(_kv(), q_dt=L.SDV_F32) == L.SDV_ERR_DTYPE           # matrix-core kernels only
+    assert _paged(_kv(kv_dtype=L.SDV_F32)) == L.SDV_ERR_DTYPE
+    assert _paged(_kv(), Hq=64, max_qo=5) == L.SDV_ERR_SHAPE          # 16 x 5 > 64 rows
+    assert _paged(_kv(), max_pages=300, bt=300) == L.SDV_ERR_SHAPE     # 1200 blocks in one split
+    assert _paged(_kv(), splits=2, max_pages=300, bt=300) == L.SDV_ERR_WORKSPACE
+    assert _paged(_kv(), bt=4) == L.SDV_ERR_SHAPE                     # stride < max_pages
+    assert _paged(_kv(), q=C.c_void_p(0x10004)) == L.SDV_ERR_SHAPE
+    assert _paged(_kv(), out=None) == L.SDV_ERR_NULL_POINTER
+    assert _paged(_kv(), B=0) == L.SDV_OK
+
+
 def test_combine_and_helpers():
     lib = L.load()
     assert lib.lse_combine(FAKE, FAKE, 0, 4, 4, 128, FAKE, 0, None, None) == L.SDV_ERR_SHAPE
