@@ -414,6 +414,33 @@ def main():
         }
         del pc, pkv, outp, wsp
 
+    # ---- ladder KV slot staging of the verify tokens (the step before the path) ----
+    if not args.no_paged:
+        ws_ = W.PAGED_BF16
+        sc = W.make_sparse_case(ws_, device=dev)
+        rows_s = sc.lengths.total_q
+        g = torch.Generator(device=dev).manual_seed(W.seed_for(ws_))
+        kn = torch.randn((rows_s, ws_.num_kv_heads, ws_.head_dim), generator=g,
+                         device=dev).to(torch.bfloat16)
+        vn = torch.randn_like(kn)
+        skv = sdv.PagedKV(sc.k_pool, sc.v_pool)
+
+        def k_stage():
+            sdv.stage_verify_kv_paged(kn, vn, sc.qo_indptr, sc.kv_len, skv, sc.block_table,
+                                      max_qo_len=ws_.max_qo())
+
+        mss, pers, _ = time_steps([("stage_verify_kv_paged", k_stage)], args.steps, args.warmup,
+                                  torch, flush)
+        sb = 2 * 2 * rows_s * ws_.num_kv_heads * ws_.head_dim * 2   # K and V rows, read + write
+        result["staging"] = {
+            "workload": "paged_bf16 verify tokens: 256 rows x 4 kv heads x 128 channels of K and "
+                        "V into head-major P128 pages",
+            "kernels": pers, "algorithmic_bytes": sb,
+            "GB_s": sb / (pers["stage_verify_kv_paged"]["avg_us"] * 1e-6) / 1e9,
+            "bound": "latency (one small launch)",
+        }
+        del sc, skv, kn, vn
+
     if not args.no_probe:
         result["attainable_read_GB_s"] = attainable_read_gbs(torch, sdv, dev)
     if not args.no_cpu_baseline:

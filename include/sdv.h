@@ -292,6 +292,48 @@ int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_in
                                int32_t out_dt, int32_t* dev_err, hipStream_t stream);
 
 /*
+ * stage_verify_kv_paged — ladder KV slot staging into ordinary head-major P128 pages:
+ * the K/V rows of the qo_len new tokens of every request are written at logical
+ * positions kv_len - qo_len + t (kv_len counts them), i.e. token (j % 128) of page
+ * block_table[r][j / 128] for j = kv_len - qo_len + t, across page boundaries.  Each
+ * request addresses only its own block-table row with its own lengths, so after a
+ * correction that shortens a request the next call writes at the corrected positions
+ * and no other request's pages move.  (Source: PR #3 MSA verify commit — KV slot
+ * staging generalises to the causal ladder; the overlap-correction fix.)
+ *
+ * k_new, v_new device [B*max_qo_len rows capacity][num_kv_heads][head_dim], rows in
+ *              qo_indptr order, stored in the cache's dtype (new_dt must equal
+ *              kv->kv_dtype: the bytes are copied, not converted); 16-byte aligned.
+ * kv           host descriptor of the cache; the K/V storage kv->k / kv->v points
+ *              to is WRITTEN (device memory the caller owns).
+ * block_table  device int32 [B][bt_stride]; kv_len[r] <= 128 * max_pages.
+ * dev_err      nullable; SDV_DEVERR_QO_LEN / _KV_CAPACITY / _PAGE_RANGE skip the
+ *              affected request or row.
+ * Rows of different requests must not share a (page, slot): the writes would race.
+ */
+int32_t stage_verify_kv_paged(const void* k_new, const void* v_new, int32_t new_dt,
+                              const int32_t* qo_indptr, const int32_t* kv_len, int32_t B,
+                              int32_t max_qo_len, const sdv_paged_kv* kv,
+                              const int32_t* block_table, int32_t max_pages,
+                              int32_t bt_stride, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * stage_verify_kv_view — the same staging into the draft layer through the P32 view:
+ * position j of request r goes to token j % 32 of P32 page sub_offsets[r][0][j / 32]
+ * (K) and sub_offsets[r][1][j / 32] (V), element ((x * Hkv + h) * 32 + j % 32) * d
+ * from the view root.  (Sources: PR #3 MSA verify commit, staging; PR #17835 item 2,
+ * the grouped-HND layout of the view.)
+ *
+ * view, sub_offsets, max_sub_pages as for verify_attention_dense; the view's storage
+ * is WRITTEN.  Other arguments as stage_verify_kv_paged; kv_len[r] <= 32 * max_sub_pages.
+ */
+int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_dt,
+                             const int32_t* qo_indptr, const int32_t* kv_len, int32_t B,
+                             int32_t max_qo_len, const sdv_subpage_view* view,
+                             const int32_t* sub_offsets, int32_t max_sub_pages,
+                             int32_t* dev_err, hipStream_t stream);
+
+/*
  * lse_combine — merge split-KV partials:  LSE = log sum_s exp(lse[s]),
  * out = sum_s exp(lse[s] - LSE) * partial_out[s]; partials with lse = -inf are
  * skipped; a row with no live partial gets 0.

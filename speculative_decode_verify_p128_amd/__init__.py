@@ -3,14 +3,16 @@ C ABI, see include/sdv.h).  The PyTorch binding passes tensors' device pointers 
 the current stream; nothing here computes on the host."""
 from .api import (PagedKV, SubpageView, alloc_workspace, dtype_code, fill_u32,
                   kv_subpage_view_init, ladder_topk_pages, lse_combine, proxy_page_scores,
-                  read_probe, set_kernel_family, verify_attention_dense, verify_attention_paged,
-                  verify_attention_sparse, workspace_bytes)
+                  read_probe, set_kernel_family, stage_verify_kv_paged, stage_verify_kv_view,
+                  verify_attention_dense, verify_attention_paged, verify_attention_sparse,
+                  workspace_bytes)
 from ._lib import LIB_PATH, SdvError, load
 
 __all__ = [
     "PagedKV", "SubpageView", "alloc_workspace", "dtype_code", "fill_u32",
     "kv_subpage_view_init", "ladder_topk_pages", "lse_combine", "proxy_page_scores", "read_probe",
-    "set_kernel_family", "verify_attention_dense", "verify_attention_paged",
+    "set_kernel_family", "stage_verify_kv_paged", "stage_verify_kv_view",
+    "verify_attention_dense", "verify_attention_paged",
     "verify_attention_sparse",
     "workspace_bytes", "LIB_PATH", "SdvError", "load",
 ]

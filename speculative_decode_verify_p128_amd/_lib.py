@@ -73,6 +73,10 @@ SIGNATURES = {
                                      _P, _I, _F, _I, _P, _S, _P, _I, _P, _P]),
     "verify_attention_paged": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I,
                                     _F, _I, _P, _S, _P, _I, _P, _P]),
+    "stage_verify_kv_paged": (_I, [_P, _P, _I, _P, _P, _I, _I, C.POINTER(PagedKV), _P, _I, _I,
+                                   _P, _P]),
+    "stage_verify_kv_view": (_I, [_P, _P, _I, _P, _P, _I, _I, C.POINTER(SubpageView), _P, _I,
+                                  _P, _P]),
     "lse_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "sdv_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "sdv_status_string": (C.c_char_p, [_I]),

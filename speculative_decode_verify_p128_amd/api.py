@@ -231,6 +231,39 @@ def verify_attention_paged(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: tor
     return out
 
 
+def stage_verify_kv_paged(k_new: torch.Tensor, v_new: torch.Tensor, qo_indptr: torch.Tensor,
+                          kv_len: torch.Tensor, kv: PagedKV, block_table: torch.Tensor, *,
+                          max_qo_len: int, dev_err: Optional[torch.Tensor] = None) -> None:
+    """Write the new tokens' K/V rows [rows, Hkv, d] (cache dtype) into kv.k / kv.v."""
+    _need(k_new, "k_new")
+    _need(v_new, "v_new")
+    if v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    B = kv_len.numel()
+    ckv = kv.c()
+    L.check(L.load().stage_verify_kv_paged(
+        _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(qo_indptr), _ptr(kv_len), B,
+        max_qo_len,
+        C.byref(ckv), _ptr(block_table), block_table.shape[1], block_table.stride(0),
+        _ptr(dev_err), _stream(k_new.device)))
+
+
+def stage_verify_kv_view(k_new: torch.Tensor, v_new: torch.Tensor, qo_indptr: torch.Tensor,
+                         kv_len: torch.Tensor, view: SubpageView, sub_offsets: torch.Tensor, *,
+                         max_qo_len: int, dev_err: Optional[torch.Tensor] = None) -> None:
+    """Write the new tokens' K/V rows [rows, Hkv, d] into the draft layer through the view."""
+    _need(k_new, "k_new")
+    _need(v_new, "v_new")
+    if v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    _need(sub_offsets, "sub_offsets", torch.int32)
+    B = kv_len.numel()
+    L.check(L.load().stage_verify_kv_view(
+        _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(qo_indptr), _ptr(kv_len), B,
+        max_qo_len, C.byref(view.c), _ptr(sub_offsets), sub_offsets.shape[-1], _ptr(dev_err),
+        _stream(k_new.device)))
+
+
 def lse_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, *, out_dtype=torch.float32,
                 out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
                 want_lse: bool = False):

@@ -52,6 +52,11 @@ struct AttnArgs {
   int32_t target_wgs;           // workgroups the GPU holds at once for the chosen kernel
 };
 
+// Bytes per stored element of an sdv_dtype.
+__host__ __device__ inline int elem_bytes_of(int32_t dt) {
+  return dt == SDV_F32 ? 4 : (dt == SDV_BF16 ? 2 : 1);
+}
+
 // Compute units of the current device (cached per device; 0 on error).
 inline int device_cu_count() {
   static int cache[64] = {0};
@@ -122,6 +127,17 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t nu
                           int32_t rows_cap, const int32_t* row_begin_dev,
                           const int32_t* row_end_dev, int32_t num_heads, int32_t head_dim,
                           void* out, int32_t out_dt, float* lse_out, hipStream_t s);
+
+// Ladder KV slot staging: rows [rows][Hkv][d] copied as stored into the paged cache.
+hipError_t launch_stage_paged(const void* k_new, const void* v_new, const int32_t* qo_indptr,
+                              const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                              const sdv_paged_kv& kv, const int32_t* block_table,
+                              int32_t max_pages, int32_t bt_stride, int32_t* dev_err,
+                              hipStream_t s);
+hipError_t launch_stage_view(const void* k_new, const void* v_new, const int32_t* qo_indptr,
+                             const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                             const sdv_subpage_view& view, const int32_t* sub_offsets,
+                             int32_t max_sub_pages, int32_t* dev_err, hipStream_t s);
 
 hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,

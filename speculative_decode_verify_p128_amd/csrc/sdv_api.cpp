@@ -316,6 +316,62 @@ int32_t ladder_topk_pages(const float* scores, const int32_t* qo_indptr, const i
                     "ladder_topk_pages launch");
 }
 
+// Shared checks of the staging calls' new rows and lengths.
+static int32_t check_stage_rows(const void* k_new, const void* v_new, int32_t new_dt,
+                                int32_t kv_dt, const int32_t* qo_indptr, const int32_t* kv_len,
+                                int32_t B, int32_t max_qo_len) {
+  if (B < 0) return fail(SDV_ERR_SHAPE, "batch %d < 0", B);
+  if (max_qo_len < 1) return fail(SDV_ERR_SHAPE, "max_qo_len %d < 1", max_qo_len);
+  if (static_cast<int64_t>(B) * max_qo_len > INT32_MAX)
+    return fail(SDV_ERR_SHAPE, "batch %d x max_qo_len %d too large", B, max_qo_len);
+  if (new_dt != kv_dt)
+    return fail(SDV_ERR_DTYPE, "new rows dtype %d differs from the cache dtype %d (rows are "
+                "copied as stored)", new_dt, kv_dt);
+  if (B > 0 && (!k_new || !v_new || !qo_indptr || !kv_len))
+    return fail(SDV_ERR_NULL_POINTER, "k_new, v_new, qo_indptr and kv_len must be non-null");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "k_new and v_new must be 16-byte aligned");
+  return SDV_OK;
+}
+
+int32_t stage_verify_kv_paged(const void* k_new, const void* v_new, int32_t new_dt,
+                              const int32_t* qo_indptr, const int32_t* kv_len, int32_t B,
+                              int32_t max_qo_len, const sdv_paged_kv* kv,
+                              const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                              int32_t* dev_err, hipStream_t stream) {
+  int32_t st = check_paged_kv(kv);
+  if (st) return st;
+  st = check_stage_rows(k_new, v_new, new_dt, kv->kv_dtype, qo_indptr, kv_len, B, max_qo_len);
+  if (st) return st;
+  if (max_pages < 1 || max_pages > (1 << 20) || bt_stride < max_pages)
+    return fail(SDV_ERR_SHAPE, "max_pages %d (<= 2^20), bt_stride %d", max_pages, bt_stride);
+  if (B > 0 && !block_table) return fail(SDV_ERR_NULL_POINTER, "block_table must be non-null");
+  if (B == 0) return ok();
+  return hip_status(sdv::launch_stage_paged(k_new, v_new, qo_indptr, kv_len, B, max_qo_len, *kv,
+                                            block_table, max_pages, bt_stride, dev_err, stream),
+                    "stage_verify_kv_paged launch");
+}
+
+int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_dt,
+                             const int32_t* qo_indptr, const int32_t* kv_len, int32_t B,
+                             int32_t max_qo_len, const sdv_subpage_view* view,
+                             const int32_t* sub_offsets, int32_t max_sub_pages,
+                             int32_t* dev_err, hipStream_t stream) {
+  if (!view) return fail(SDV_ERR_NULL_POINTER, "view must be non-null");
+  if (!view->k_root || view->num_sub_pages < 8 || !valid_head_dim(view->head_dim) ||
+      view->num_kv_heads < 1 || !valid_dtype(view->kv_dtype))
+    return fail(SDV_ERR_GEOMETRY, "native P128 draft view unavailable: view not initialised");
+  int32_t st = check_stage_rows(k_new, v_new, new_dt, view->kv_dtype, qo_indptr, kv_len, B,
+                                max_qo_len);
+  if (st) return st;
+  if (max_sub_pages < 1) return fail(SDV_ERR_SHAPE, "max_sub_pages %d < 1", max_sub_pages);
+  if (B > 0 && !sub_offsets) return fail(SDV_ERR_NULL_POINTER, "sub_offsets must be non-null");
+  if (B == 0) return ok();
+  return hip_status(sdv::launch_stage_view(k_new, v_new, qo_indptr, kv_len, B, max_qo_len, *view,
+                                           sub_offsets, max_sub_pages, dev_err, stream),
+                    "stage_verify_kv_view launch");
+}
+
 int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                int32_t num_q_heads, const sdv_paged_kv* kv,
