@@ -441,6 +441,41 @@ def main():
         }
         del sc, skv, kn, vn
 
+    # ---- grouped head-major head-slice transfer of the draft layer (two TP ranks -> one) ----
+    if not args.no_dense:
+        wt = W.DENSE_BF16
+        dc = W.make_dense_case(wt, device=dev)
+        H, per = wt.num_kv_heads, wt.num_kv_heads // 2
+        pages = [s_ * wt.slot_stride + wt.root_page for s_ in range(dc.num_slots)]
+        pages = np.array(pages + [p_ + 1 for p_ in pages])
+        e_ = dc.pool.element_size()
+        senders = [dc.pool[:, :, r_ * per:(r_ + 1) * per].contiguous() for r_ in range(2)]
+        recv = torch.zeros_like(dc.pool)
+        descs = [torch.from_numpy(sdv.hnd_head_slice_descriptors(
+            token_groups=4, src_heads=per, src_head_begin=0, dst_heads=H, dst_head_begin=r_ * per,
+            num_heads=per, head_dim=wt.head_dim, kv_dtype=dc.pool.dtype,
+            src_page_offsets=pages * (4 * per * 32 * wt.head_dim * e_),
+            dst_page_offsets=pages * (4 * H * 32 * wt.head_dim * e_))).to(dev) for r_ in range(2)]
+
+        def k_transfer():
+            for r_ in range(2):
+                sdv.copy_descriptors(senders[r_], recv, descs[r_])
+
+        mst, pert, _ = time_steps([("copy_descriptors", k_transfer)], args.steps, args.warmup,
+                                  torch, flush)
+        tb = 2 * len(pages) * 4 * H * 32 * wt.head_dim * e_          # read + written
+        gbs = tb / (pert["copy_descriptors"]["avg_us"] * 1e-6) / 1e9
+        result["transfer"] = {
+            "workload": "dense_bf16 draft layer (K and V of every slot, grouped head-major P128 "
+                        "pages) from two 2-head ranks into one 4-head pool, one descriptor per "
+                        "(page, K/V, token group)",
+            "kernels": pert, "bytes_read_and_written": tb,
+            "roofline": {"bound": "hbm", "kernel": "copy_descriptors", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None},
+        }
+        del dc, senders, recv, descs
+
     if not args.no_probe:
         result["attainable_read_GB_s"] = attainable_read_gbs(torch, sdv, dev)
     if not args.no_cpu_baseline:

@@ -73,6 +73,8 @@ typedef enum sdv_dtype {
 #define SDV_DEVERR_KV_CAPACITY 2  /* kv_len larger than the page table can address    */
 #define SDV_DEVERR_PAGE_RANGE 4   /* a slot, page or sub-page index outside the pool   */
 #define SDV_DEVERR_TOPK_INDEX 8   /* a top-k page index >= the token's valid pages     */
+#define SDV_DEVERR_COPY_RANGE 16  /* a copy descriptor outside its buffers or not a
+                                     multiple of 16 bytes                              */
 
 #define SDV_PHYS_PAGE 128
 #define SDV_SUB_PAGE 32
@@ -332,6 +334,54 @@ int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_d
                              int32_t max_qo_len, const sdv_subpage_view* view,
                              const int32_t* sub_offsets, int32_t max_sub_pages,
                              int32_t* dev_err, hipStream_t stream);
+
+/* One byte-range copy: dst_base[dst_offset ..) = src_base[src_offset ..), `bytes` long. */
+typedef struct sdv_copy_desc {
+  int64_t src_offset;
+  int64_t dst_offset;
+  int64_t bytes;
+} sdv_copy_desc;
+
+/*
+ * hnd_head_slice_descriptors — the head-slice transfer mapper for head-major pages
+ * whose tokens may be split into token groups (host only, no HIP call).  A page of G
+ * token groups is laid out [G][heads][page_tokens / G][head_dim]; the P32 view of the
+ * draft layer's P128 pages is G = 4 ([4][local_head][32][d]), ordinary head-major
+ * pages are G = 1.  For every listed page pair i and every group g it emits one
+ * descriptor that moves heads [src_head_begin, + num_heads) of source page i to heads
+ * [dst_head_begin, + num_heads) of destination page i — one descriptor per (layer,
+ * K/V, token group) when the list enumerates the layers' K and V pages.  Mapping a
+ * grouped page with G = 1 (one contiguous head slice per page) selects the right heads
+ * only in the first group.  (Source: PR #17835, Root causes and fixes, item 2
+ * "Grouped-HND draft KV transfer": the hnd_token_groups page-table field, default 1,
+ * four groups for the shared draft K/V.)
+ *
+ * src_page_offsets, dst_page_offsets  host int64 [num_pages]: byte offset of each page
+ *              from the source / destination base.
+ * out          host [capacity]; descriptors in page-major, group-minor order.
+ * count_out    host: num_pages * token_groups.
+ * Errors: SDV_ERR_SHAPE for page_tokens not a multiple of token_groups, head ranges
+ * outside [0, src_heads) / [0, dst_heads), or capacity < num_pages * token_groups.
+ */
+int32_t hnd_head_slice_descriptors(int32_t token_groups, int32_t src_heads,
+                                   int32_t src_head_begin, int32_t dst_heads,
+                                   int32_t dst_head_begin, int32_t num_heads,
+                                   int32_t head_dim, int32_t kv_dtype, int32_t page_tokens,
+                                   const int64_t* src_page_offsets,
+                                   const int64_t* dst_page_offsets, int32_t num_pages,
+                                   sdv_copy_desc* out, int32_t capacity, int32_t* count_out);
+
+/*
+ * copy_descriptors — execute byte-range copies on the device (the transfer engine's
+ * work on one GPU; across GPUs the same descriptors drive peer copies).
+ * descs device [num_descs]; every range must lie inside [0, src_bytes) / [0, dst_bytes)
+ * and offsets and lengths must be multiples of 16 bytes, else that descriptor is
+ * skipped and SDV_DEVERR_COPY_RANGE is flagged.  Destination ranges must not overlap
+ * each other or the source.
+ */
+int32_t copy_descriptors(const void* src_base, size_t src_bytes, void* dst_base,
+                         size_t dst_bytes, const sdv_copy_desc* descs, int32_t num_descs,
+                         int32_t* dev_err, hipStream_t stream);
 
 /*
  * lse_combine — merge split-KV partials:  LSE = log sum_s exp(lse[s]),

@@ -36,7 +36,7 @@ torch.float8_e4m3fn, coordinate-encoded pools and the pages' own statements.
 from .ladder import ladder_bounds, n_valid_pages
 from .fp8 import decode_e4m3fn, decode_bf16, decode_store
 from .view import (subpage_offsets, gather_subpage_view, gather_hnd, head_slice_contiguous,
-                   head_slice_grouped)
+                   head_slice_grouped, head_slice_descriptors)
 from .attention import attend, dense_verify_request, sparse_verify_request, lse_combine
 from .proxy import proxy_scores_request, canonical_dot_f32
 from .topk import ladder_topk_request
@@ -46,7 +46,7 @@ from .pipeline import (dense_verify_case, sparse_verify_case, paged_verify_case,
 __all__ = [
     "ladder_bounds", "n_valid_pages", "decode_e4m3fn", "decode_bf16", "decode_store",
     "subpage_offsets", "gather_subpage_view", "gather_hnd", "head_slice_contiguous",
-    "head_slice_grouped", "attend", "dense_verify_request", "sparse_verify_request",
+    "head_slice_grouped", "head_slice_descriptors", "attend", "dense_verify_request", "sparse_verify_request",
     "lse_combine", "proxy_scores_request", "canonical_dot_f32", "ladder_topk_request",
     "dense_verify_case", "sparse_verify_case", "paged_verify_case", "dense_rows", "sparse_rows",
     "request_kv_dense", "request_kv_sparse",

@@ -87,6 +87,26 @@ def head_slice_contiguous(num_heads: int, h0: int, h1: int, head_dim: int, page:
     return [(h0 * page * head_dim, (h1 - h0) * page * head_dim)]
 
 
+def head_slice_descriptors(token_groups: int, src_heads: int, src_h0: int, dst_heads: int,
+                           dst_h0: int, n_heads: int, head_dim: int, elem_bytes: int,
+                           src_pages, dst_pages, page_tokens: int = 128):
+    """Byte-range copies (src offset, dst offset, length) that move heads
+    [src_h0, src_h0 + n_heads) of each source page to heads [dst_h0, dst_h0 + n_heads) of
+    the matching destination page.  A page of `token_groups` groups is laid out
+    [group, heads, page_tokens / groups, d]; the mapper emits one descriptor per
+    (page, token group) — per (layer, K/V, token group) when the page list enumerates
+    the layers' K and V pages ([PR17835] item 2).  token_groups = 1 is the ordinary
+    head-major slice [heads, page_tokens, d]."""
+    tpg = page_tokens // token_groups
+    row = tpg * head_dim * elem_bytes            # one head's bytes in one group
+    out = []
+    for sp, dp in zip(src_pages, dst_pages):
+        for g in range(token_groups):
+            out.append((int(sp) + (g * src_heads + src_h0) * row,
+                        int(dp) + (g * dst_heads + dst_h0) * row, n_heads * row))
+    return out
+
+
 def apply_descriptors(dst_flat: np.ndarray, src_flat: np.ndarray, descriptors) -> None:
     """Copy src sequentially into dst at the descriptor ranges, in order."""
     pos = 0

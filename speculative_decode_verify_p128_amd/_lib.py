@@ -26,6 +26,7 @@ DEVERR_QO_LEN = 1
 DEVERR_KV_CAPACITY = 2
 DEVERR_PAGE_RANGE = 4
 DEVERR_TOPK_INDEX = 8
+DEVERR_COPY_RANGE = 16
 
 
 class SubpageGeom(C.Structure):
@@ -77,6 +78,9 @@ SIGNATURES = {
                                    _P, _P]),
     "stage_verify_kv_view": (_I, [_P, _P, _I, _P, _P, _I, _I, C.POINTER(SubpageView), _P, _I,
                                   _P, _P]),
+    "hnd_head_slice_descriptors": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I,
+                                        _P]),
+    "copy_descriptors": (_I, [_P, _S, _P, _S, _P, _I, _P, _P]),
     "lse_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "sdv_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "sdv_status_string": (C.c_char_p, [_I]),

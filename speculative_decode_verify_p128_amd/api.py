@@ -12,6 +12,7 @@ import ctypes as C
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
 import torch
 
 from . import _lib as L
@@ -262,6 +263,33 @@ def stage_verify_kv_view(k_new: torch.Tensor, v_new: torch.Tensor, qo_indptr: to
         _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(qo_indptr), _ptr(kv_len), B,
         max_qo_len, C.byref(view.c), _ptr(sub_offsets), sub_offsets.shape[-1], _ptr(dev_err),
         _stream(k_new.device)))
+
+
+def hnd_head_slice_descriptors(*, token_groups: int, src_heads: int, src_head_begin: int,
+                               dst_heads: int, dst_head_begin: int, num_heads: int,
+                               head_dim: int, kv_dtype, src_page_offsets, dst_page_offsets,
+                               page_tokens: int = 128) -> np.ndarray:
+    """Host-side mapper: int64 [num_pages * token_groups, 3] (src offset, dst offset,
+    bytes), one row per (page, token group)."""
+    src = np.ascontiguousarray(src_page_offsets, dtype=np.int64)
+    dst = np.ascontiguousarray(dst_page_offsets, dtype=np.int64)
+    n = src.size
+    out = np.zeros((max(n * token_groups, 1), 3), dtype=np.int64)
+    count = C.c_int32(0)
+    L.check(L.load().hnd_head_slice_descriptors(
+        token_groups, src_heads, src_head_begin, dst_heads, dst_head_begin, num_heads, head_dim,
+        dtype_code(kv_dtype), page_tokens, src.ctypes.data, dst.ctypes.data, n,
+        out.ctypes.data, out.shape[0], C.byref(count)))
+    return out[:count.value]
+
+
+def copy_descriptors(src: torch.Tensor, dst: torch.Tensor, descs: torch.Tensor, *,
+                     dev_err: Optional[torch.Tensor] = None) -> None:
+    """Execute byte-range copies (descs: int64 [n, 3] on the device) from src into dst."""
+    _need(descs, "descs", torch.int64)
+    L.check(L.load().copy_descriptors(
+        _ptr(src), src.numel() * src.element_size(), _ptr(dst), dst.numel() * dst.element_size(),
+        _ptr(descs), descs.shape[0], _ptr(dev_err), _stream(dst.device)))
 
 
 def lse_combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, *, out_dtype=torch.float32,

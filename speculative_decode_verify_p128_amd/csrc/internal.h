@@ -139,6 +139,10 @@ hipError_t launch_stage_view(const void* k_new, const void* v_new, const int32_t
                              const sdv_subpage_view& view, const int32_t* sub_offsets,
                              int32_t max_sub_pages, int32_t* dev_err, hipStream_t s);
 
+hipError_t launch_copy_descriptors(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
+                                  const sdv_copy_desc* descs, int32_t n, int32_t* dev_err,
+                                  hipStream_t s);
+
 hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
                              hipStream_t s);

@@ -372,6 +372,56 @@ int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_d
                     "stage_verify_kv_view launch");
 }
 
+int32_t hnd_head_slice_descriptors(int32_t token_groups, int32_t src_heads,
+                                   int32_t src_head_begin, int32_t dst_heads,
+                                   int32_t dst_head_begin, int32_t num_heads,
+                                   int32_t head_dim, int32_t kv_dtype, int32_t page_tokens,
+                                   const int64_t* src_page_offsets,
+                                   const int64_t* dst_page_offsets, int32_t num_pages,
+                                   sdv_copy_desc* out, int32_t capacity, int32_t* count_out) {
+  if (!valid_dtype(kv_dtype)) return fail(SDV_ERR_DTYPE, "kv dtype %d", kv_dtype);
+  if (token_groups < 1 || page_tokens < 1 || page_tokens % token_groups != 0)
+    return fail(SDV_ERR_SHAPE, "page_tokens %d is not a multiple of token_groups %d",
+                page_tokens, token_groups);
+  if (head_dim < 1 || num_heads < 1 || src_heads < 1 || dst_heads < 1 || src_head_begin < 0 ||
+      dst_head_begin < 0 || src_head_begin + num_heads > src_heads ||
+      dst_head_begin + num_heads > dst_heads)
+    return fail(SDV_ERR_SHAPE, "heads [%d, +%d) of %d to [%d, +%d) of %d", src_head_begin,
+                num_heads, src_heads, dst_head_begin, num_heads, dst_heads);
+  if (num_pages < 0) return fail(SDV_ERR_SHAPE, "num_pages %d < 0", num_pages);
+  if (!count_out) return fail(SDV_ERR_NULL_POINTER, "count_out must be non-null");
+  const int64_t need = static_cast<int64_t>(num_pages) * token_groups;
+  *count_out = static_cast<int32_t>(need > INT32_MAX ? INT32_MAX : need);
+  if (need > capacity) return fail(SDV_ERR_SHAPE, "capacity %d < %lld descriptors", capacity,
+                                   static_cast<long long>(need));
+  if (num_pages > 0 && (!src_page_offsets || !dst_page_offsets || !out))
+    return fail(SDV_ERR_NULL_POINTER, "page offsets and out must be non-null");
+  const int64_t row = static_cast<int64_t>(page_tokens / token_groups) * head_dim *
+                      sdv::elem_bytes_of(kv_dtype);   // one head in one group
+  int64_t k = 0;
+  for (int32_t i = 0; i < num_pages; ++i)
+    for (int32_t g = 0; g < token_groups; ++g, ++k) {
+      out[k].src_offset = src_page_offsets[i] + (static_cast<int64_t>(g) * src_heads + src_head_begin) * row;
+      out[k].dst_offset = dst_page_offsets[i] + (static_cast<int64_t>(g) * dst_heads + dst_head_begin) * row;
+      out[k].bytes = num_heads * row;
+    }
+  return ok();
+}
+
+int32_t copy_descriptors(const void* src_base, size_t src_bytes, void* dst_base,
+                         size_t dst_bytes, const sdv_copy_desc* descs, int32_t num_descs,
+                         int32_t* dev_err, hipStream_t stream) {
+  if (num_descs < 0) return fail(SDV_ERR_SHAPE, "num_descs %d < 0", num_descs);
+  if (num_descs == 0) return ok();
+  if (!src_base || !dst_base || !descs)
+    return fail(SDV_ERR_NULL_POINTER, "src_base, dst_base and descs must be non-null");
+  if ((reinterpret_cast<uintptr_t>(src_base) | reinterpret_cast<uintptr_t>(dst_base)) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "src_base and dst_base must be 16-byte aligned");
+  return hip_status(sdv::launch_copy_descriptors(src_base, src_bytes, dst_base, dst_bytes, descs,
+                                                 num_descs, dev_err, stream),
+                    "copy_descriptors launch");
+}
+
 int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                int32_t num_q_heads, const sdv_paged_kv* kv,
