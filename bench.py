@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify tokens/sec + achieved HBM GB/s (% of peak), sparse paged GQA qo_len=4"
 HBM_PEAK_GBS = 8000.0
+ACCEPT_VOCAB = 131072          # synthetic vocabulary size of the acceptance line
 
 
 def parse():
@@ -475,6 +476,33 @@ def main():
                          "traffic": None},
         }
         del dc, senders, recv, descs
+
+    # ---- greedy acceptance after the verify step (target argmax vs draft tokens) ----
+    if not args.no_paged:
+        wa = W.SPARSE_BF16
+        ac = W.make_accept_case(wa, ACCEPT_VOCAB, device=dev)
+        acc_outs = (torch.empty(wa.batch * wa.max_qo(), dtype=torch.int32, device=dev),
+                    torch.empty(wa.batch, dtype=torch.int32, device=dev),
+                    torch.empty((wa.batch, wa.max_qo()), dtype=torch.int32, device=dev),
+                    torch.empty(wa.batch, dtype=torch.int32, device=dev))
+
+        def k_accept():
+            sdv.greedy_accept(ac.logits, ac.tokens, ac.qo_indptr, ac.kv_len, max_qo_len=wa.max_qo(),
+                              outs=acc_outs)
+
+        msa, pera, _ = time_steps([("greedy_accept", k_accept)], args.steps, args.warmup, torch,
+                                  flush)
+        ab_ = ac.lengths.total_q * ACCEPT_VOCAB * 2 + ac.lengths.total_q * 4 * 2
+        gbs = ab_ / (pera["greedy_accept"]["avg_us"] * 1e-6) / 1e9
+        result["accept"] = {
+            "workload": f"sparse_bf16 verify rows: 256 rows of {ACCEPT_VOCAB} bf16 logits (synthetic "
+                        "vocabulary size), greedy argmax and accepted-prefix per request",
+            "kernels": pera, "algorithmic_bytes": ab_,
+            "roofline": {"bound": "hbm", "kernel": "greedy_accept", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None},
+        }
+        del ac
 
     if not args.no_probe:
         result["attainable_read_GB_s"] = attainable_read_gbs(torch, sdv, dev)

@@ -335,6 +335,35 @@ int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_d
                              const int32_t* sub_offsets, int32_t max_sub_pages,
                              int32_t* dev_err, hipStream_t stream);
 
+/*
+ * greedy_accept — greedy acceptance of the draft tokens after the verify step.  Row t
+ * of request r holds its t-th verify input token (row 0 the last accepted token, rows
+ * 1 .. qo_len - 1 the drafts) and the target's logits after it.  The target's greedy
+ * token after a row is the argmax of its logits (ties to the lowest index, NaN never
+ * chosen, -1 for an all-NaN row).  Draft t + 1 is accepted while it equals the target
+ * after row t for every earlier row; with a accepted drafts the step emits them and
+ * the bonus token (the target after row a): a + 1 tokens, the acceptance length.  The
+ * cache keeps the verify tokens through draft a, so the corrected kv_len is
+ * kv_len - qo_len + 1 + a.  (Sources: PR #17835, Acceptance and accuracy evidence —
+ * acceptance under greedy decoding, rate and mean length; PR #3 MSA verify commit —
+ * the verify batch of qo_len = 1 + draft_len tokens.)
+ *
+ * logits       device [B*max_qo_len rows capacity][vocab], F32 or BF16, 16-byte
+ *              aligned; vocab a multiple of 4 (F32) or 8 (BF16).
+ * tokens       device int32 [rows]: the verify input tokens.
+ * targets_out  device int32 [B*max_qo_len]: argmax per row (rows past qo_indptr[B]
+ *              untouched).
+ * accept_out   device int32 [B]: accepted drafts a (-1 for a request with unusable
+ *              lengths, flagged SDV_DEVERR_QO_LEN).
+ * emitted_out  device int32 [B][max_qo_len]: the a + 1 emitted tokens, -1 padded.
+ * new_kv_len_out device int32 [B]: kv_len - qo_len + 1 + a (kv_len when flagged).
+ */
+int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
+                      const int32_t* tokens, const int32_t* qo_indptr, const int32_t* kv_len,
+                      int32_t B, int32_t max_qo_len, int32_t* targets_out,
+                      int32_t* accept_out, int32_t* emitted_out, int32_t* new_kv_len_out,
+                      int32_t* dev_err, hipStream_t stream);
+
 /* One byte-range copy: dst_base[dst_offset ..) = src_base[src_offset ..), `bytes` long. */
 typedef struct sdv_copy_desc {
   int64_t src_offset;

@@ -40,6 +40,7 @@ from .view import (subpage_offsets, gather_subpage_view, gather_hnd, head_slice_
 from .attention import attend, dense_verify_request, sparse_verify_request, lse_combine
 from .proxy import proxy_scores_request, canonical_dot_f32
 from .topk import ladder_topk_request
+from .accept import greedy_accept_case, greedy_accept_request, greedy_argmax
 from .pipeline import (dense_verify_case, sparse_verify_case, paged_verify_case, dense_rows,
                        sparse_rows, request_kv_dense, request_kv_sparse)
 
@@ -49,5 +50,6 @@ __all__ = [
     "head_slice_grouped", "head_slice_descriptors", "attend", "dense_verify_request", "sparse_verify_request",
     "lse_combine", "proxy_scores_request", "canonical_dot_f32", "ladder_topk_request",
     "dense_verify_case", "sparse_verify_case", "paged_verify_case", "dense_rows", "sparse_rows",
-    "request_kv_dense", "request_kv_sparse",
+    "request_kv_dense", "request_kv_sparse", "greedy_argmax", "greedy_accept_request",
+    "greedy_accept_case",
 ]

@@ -422,6 +422,30 @@ int32_t copy_descriptors(const void* src_base, size_t src_bytes, void* dst_base,
                     "copy_descriptors launch");
 }
 
+int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
+                      const int32_t* tokens, const int32_t* qo_indptr, const int32_t* kv_len,
+                      int32_t B, int32_t max_qo_len, int32_t* targets_out, int32_t* accept_out,
+                      int32_t* emitted_out, int32_t* new_kv_len_out, int32_t* dev_err,
+                      hipStream_t stream) {
+  if (logits_dt != SDV_F32 && logits_dt != SDV_BF16)
+    return fail(SDV_ERR_DTYPE, "logits dtype %d (supported: F32, BF16)", logits_dt);
+  const int per = logits_dt == SDV_F32 ? 4 : 8;
+  if (vocab < 1 || vocab % per != 0)
+    return fail(SDV_ERR_SHAPE, "vocab %d must be a positive multiple of %d", vocab, per);
+  if (B < 0 || max_qo_len < 1 || static_cast<int64_t>(B) * max_qo_len > INT32_MAX)
+    return fail(SDV_ERR_SHAPE, "B %d, max_qo_len %d", B, max_qo_len);
+  if (B == 0) return ok();
+  if (!logits || !tokens || !qo_indptr || !kv_len || !targets_out || !accept_out ||
+      !emitted_out || !new_kv_len_out)
+    return fail(SDV_ERR_NULL_POINTER, "every array argument but dev_err must be non-null");
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "logits must be 16-byte aligned");
+  return hip_status(sdv::launch_greedy_accept(logits, logits_dt, vocab, tokens, qo_indptr, kv_len,
+                                              B, max_qo_len, targets_out, accept_out, emitted_out,
+                                              new_kv_len_out, dev_err, stream),
+                    "greedy_accept launch");
+}
+
 int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                int32_t num_q_heads, const sdv_paged_kv* kv,

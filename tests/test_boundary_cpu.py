@@ -202,6 +202,17 @@ def test_paged_rejections():
     assert _paged(_kv(), B=0) == L.SDV_OK
 
 
+def test_greedy_accept_rejections():
+    lib = L.load()
+    args = lambda dt, vocab, logits=FAKE, tokens=FAKE: (  # noqa: E731
+        logits, dt, vocab, tokens, FAKE, FAKE, 2, 4, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert lib.greedy_accept(*args(L.SDV_FP8_E4M3, 1024)) == L.SDV_ERR_DTYPE
+    assert lib.greedy_accept(*args(L.SDV_BF16, 1020)) == L.SDV_ERR_SHAPE     # not a multiple of 8
+    assert lib.greedy_accept(*args(L.SDV_F32, 0)) == L.SDV_ERR_SHAPE
+    assert lib.greedy_accept(*args(L.SDV_BF16, 1024, tokens=None)) == L.SDV_ERR_NULL_POINTER
+    assert lib.greedy_accept(*args(L.SDV_BF16, 1024, logits=C.c_void_p(0x10008))) == L.SDV_ERR_SHAPE
+
+
 def test_combine_and_helpers():
     lib = L.load()
     assert lib.lse_combine(FAKE, FAKE, 0, 4, 4, 128, FAKE, 0, None, None) == L.SDV_ERR_SHAPE

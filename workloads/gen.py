@@ -34,7 +34,7 @@ _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float
 
 
 def seed_for(workload: VerifyWorkload, base: int = 1000) -> int:
-    names = ("tiny_fp32", "dense_bf16", "sparse_bf16", "long_fp8", "ragged_mixed")
+    names = ("tiny_fp32", "dense_bf16", "sparse_bf16", "long_fp8", "ragged_mixed", "paged_bf16")
     idx = names.index(workload.name) + 1 if workload.name in names else 99
     return base + idx
 
@@ -254,3 +254,57 @@ def raw_numpy(t: torch.Tensor) -> np.ndarray:
 
 
 DTYPE_NAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
+
+
+@dataclass
+class AcceptCase:
+    lengths: Lengths
+    logits: torch.Tensor          # [sum(qo), vocab], f32 or bf16
+    tokens: torch.Tensor          # int32 [sum(qo)]: row 0 the last accepted token, then drafts
+    qo_indptr: torch.Tensor
+    kv_len: torch.Tensor
+    planted: np.ndarray           # int64 [sum(qo)]: the index given the margin in each row
+
+
+def make_accept_case(w: VerifyWorkload, vocab: int, p_match: float = 0.8,
+                     dtype: torch.dtype = torch.bfloat16, tie_rows: float = 0.1,
+                     nan_rows: float = 0.0, seed: Optional[int] = None,
+                     device=None) -> AcceptCase:
+    """Target logits for the verify rows of workload w's lengths, with known structure:
+    each row holds N(0, 1) values plus one planted index raised 2.0 above the row's
+    largest draw; a fraction of rows copies that value to a second, random index (two
+    equal maxima); a fraction gets NaN at random places.  Row t >= 1 of a request holds
+    the planted index of row t - 1 with probability p_match, else another random token
+    (only the drawing is done here: which token the target picks is left to the code
+    under test)."""
+    seed = seed_for(w, 3000) if seed is None else seed
+    qo_, kv_ = draw_lengths(w, seed)
+    lengths = Lengths(qo=qo_, kv=kv_)
+    rows = lengths.total_q
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, vocab)).astype(np.float32)
+    planted = rng.integers(0, vocab, size=rows)
+    top = x.max(axis=1) + 2.0
+    x[np.arange(rows), planted] = top
+    tie = rng.random(rows) < tie_rows
+    second = rng.integers(0, vocab, size=rows)
+    x[tie, second[tie]] = top[tie]
+    if nan_rows > 0:
+        nanr = rng.random(rows) < nan_rows
+        cols = rng.integers(0, vocab, size=(rows, 4))
+        for r_ in np.nonzero(nanr)[0]:
+            x[r_, cols[r_]] = np.nan
+    tokens = rng.integers(0, vocab, size=rows)
+    ind = lengths.qo_indptr
+    for r in range(w.batch):
+        for t in range(1, int(lengths.qo[r])):
+            row = ind[r] + t
+            if rng.random() < p_match:
+                tokens[row] = planted[row - 1]
+    logits = torch.from_numpy(x).to(dtype)
+    dev = device if device is not None else torch.device("cpu")
+    return AcceptCase(lengths=lengths, logits=logits.to(dev),
+                      tokens=torch.from_numpy(tokens.astype(np.int32)).to(dev),
+                      qo_indptr=torch.from_numpy(ind.astype(np.int32)).to(dev),
+                      kv_len=torch.from_numpy(lengths.kv.astype(np.int32)).to(dev),
+                      planted=planted)
