@@ -115,6 +115,8 @@ KERNEL_SOURCES = {
                                "internal.h", "sdv_api.cpp"),
     "verify_attention_paged": ("k_attn_waves.hip", "mfma_attn.h", "k_small.hip", "device.h",
                                "internal.h", "sdv_api.cpp"),
+    "greedy_accept": ("k_accept.hip", "device.h", "internal.h", "sdv_api.cpp"),
+    "copy_descriptors": ("k_copy.hip", "device.h", "internal.h", "sdv_api.cpp"),
 }
 
 
@@ -473,7 +475,8 @@ def main():
             "kernels": pert, "bytes_read_and_written": tb,
             "roofline": {"bound": "hbm", "kernel": "copy_descriptors", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None},
+                         "traffic": load_traffic("copy_descriptors", wt.name,
+                                                 source_hash(*KERNEL_SOURCES["copy_descriptors"]))},
         }
         del dc, senders, recv, descs
 
@@ -500,7 +503,8 @@ def main():
             "kernels": pera, "algorithmic_bytes": ab_,
             "roofline": {"bound": "hbm", "kernel": "greedy_accept", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None},
+                         "traffic": load_traffic("greedy_accept", wa.name,
+                                                 source_hash(*KERNEL_SOURCES["greedy_accept"]))},
         }
         del ac
 
