@@ -281,7 +281,11 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
  *
  * Arguments as in verify_attention_sparse, without topk_idx.  num_splits >= 1 as in
  * verify_attention_dense with the capacity 4 * max_pages 32-token blocks; each split
- * holds at most 1024 blocks, so ceil(4 * max_pages / num_splits) <= 1024.
+ * holds at most 1024 blocks, so ceil(4 * max_pages / num_splits) <= 1024.  With
+ * num_splits >= 2, B <= 2048 and ceil(4 * max_pages / (num_splits - 1)) <= 1024 the
+ * call runs persistent: the (request, KV head) pairs are laid end to end and every
+ * workgroup attends an equal range of 32-token blocks, so num_splits bounds how many
+ * workgroups share one pair rather than fixing where a pair is cut.
  * Supported: q BF16 with BF16 or FP8 K/V; head_dim 64 or 128; G * max_qo_len <= 64.
  * Errors as verify_attention_sparse; SDV_ERR_DTYPE for F32 q.
  */
@@ -440,7 +444,12 @@ const char* sdv_last_error(void);
  * one LDS block stream per wave for sparse attention, the workgroup-shared LDS block
  * ring for dense attention; vector-ALU kernels for fp32), 1 = the vector-ALU kernels,
  * 2 = the matrix-core kernels that stream K/V through registers, 3 = the per-wave
- * LDS-stream kernels for both, 4 = the workgroup-shared LDS-ring kernels for both.
+ * LDS-stream kernels for both, 4 = the workgroup-shared LDS-ring kernels for both,
+ * 5 = for dense attention with num_splits >= 2, the persistent per-wave kernel that
+ * gives every workgroup an equal range of 32-token blocks over all (request, KV head)
+ * pairs (split slots are then consecutive pieces of a pair; needs B <= 2048 and
+ * ceil(block capacity / (num_splits - 1)) <= 1024, else as 0).  Automatic selection
+ * uses it for verify_attention_paged when it applies, the per-wave kernel otherwise.
  * Process-wide; returns the previous value. */
 int32_t sdv_set_kernel_family(int32_t family);
 

@@ -120,6 +120,15 @@ hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, 
 // position below the ladder bound), on the two matrix-core LDS kernels above; `src`
 // carries the pools and the block table, topk_idx is unused.
 hipError_t launch_attn_paged_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+// Dense persistent split-KV (equal block ranges per workgroup over all (request, KV head)
+// pairs; num_splits >= 2 partial slots per row, then the combine).  persist_supported
+// says whether a call fits it: num_splits >= 2, B <= kPersistMaxRequests,
+// ceil(cap_blocks / (num_splits - 1)) <= 1024 and B * Hkv * cap_blocks < 2^31, where
+// cap_blocks is the 32-token block capacity of a request.
+constexpr int kPersistMaxRequests = 2048;
+bool persist_supported(const AttnArgs& a, int64_t cap_blocks);
+hipError_t launch_attn_dense_persist(const AttnArgs& a, const DenseSource& src, hipStream_t s);
+hipError_t launch_attn_paged_persist(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 hipError_t launch_attn_paged_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 
 // Rows [*row_begin_dev, *row_end_dev) are combined (all rows_cap rows when null).

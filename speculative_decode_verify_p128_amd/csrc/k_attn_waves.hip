@@ -86,54 +86,48 @@ __device__ __forceinline__ int merge_index(int row, int k) {
   return row * (D / 4) + (k ^ (row & 15));
 }
 
+// LDS of the per-wave kernels: the four waves' rings (the merge regions reuse them), the
+// waves' row maxima and sums, and the staged block list.
 template <int RT, int D, int KDT, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
+struct WavesLds {
+  using Gm = Geo<D, KDT>;
+  static constexpr int ROWS = RT * 16;
+  static constexpr int WAVE_RING = kWaveSlots * Gm::BLOCK;
+  static constexpr int RING = 4 * WAVE_RING;
+  static_assert(2 * ROWS * D * 4 <= RING, "merge regions reuse the ring");
+  __attribute__((aligned(16))) char ring[RING];
+  float M[4][ROWS];
+  float L[4][ROWS];
+  typename BlockList<MODE, D, KDT>::Lds ul;
+  int chunk;
+};
+
+// Attention of the G x qo query rows of (request r, KV head h) over the staged block
+// range `bl` (whose metadata sits in sh.ul): every wave streams every fourth block, then
+// the waves merge and wave 0 writes the rows (out_slot < 0) or the normalised partial and
+// log-sum-exp into split slot out_slot.  All 256 threads call; LDS is free again only
+// after a barrier that follows the call.
+template <int RT, int D, int KDT, int MODE>
+__device__ __forceinline__ void waves_attend(WavesLds<RT, D, KDT, MODE>& sh, const AttnArgs& a,
+                                             const DenseSource& ds, const SparseSource& ss,
+                                             const BlockList<MODE, D, KDT>& bl, int r, int h,
+                                             int row0, int qo, int kv, int out_slot) {
   using Gm = Geo<D, KDT>;
   using Cp = WaveCopier<D, KDT>;
+  using BL = BlockList<MODE, D, KDT>;
   constexpr int STEPS = Gm::STEPS;
   constexpr int NT = Gm::NT;
   constexpr int ROWS = RT * 16;
   constexpr int A = kWaveSlots;
   constexpr int WAVE_RING = A * Gm::BLOCK;
-  constexpr int RING = 4 * WAVE_RING;
-  constexpr int MERGE = 2 * ROWS * D * 4;   // two regions of ROWS x D floats
-  static_assert(MERGE <= RING, "merge regions reuse the ring");
   static_assert(D / 4 <= 32 && (D / 4) % 8 == 0, "a lane's quarter row");
-
-  __shared__ __attribute__((aligned(16))) char ring[RING];
-  __shared__ float M_lds[4][ROWS];
-  __shared__ float L_lds[4][ROWS];
-  using BL = BlockList<MODE, D, KDT>;
-  __shared__ typename BL::Lds ul;
-  __shared__ int chunk_lds;
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int i = lane & 15;
   const int q = lane >> 4;
-  // Grid x = (request, KV head), y = split, so consecutive workgroups (dealt round-robin
-  // to the XCDs) are different (request, head) pairs of one split.
   const int Hkv = a.num_kv_heads;
-  const int split = blockIdx.y;
-  const int h = blockIdx.x % Hkv;
-  const int r = blockIdx.x / Hkv;
   const int G = a.num_q_heads / Hkv;
-
-  const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
-                                           : static_cast<int64_t>(ss.max_pages) * kPage;
-  const int row0 = a.qo_indptr[r];
-  const int qo = a.qo_indptr[r + 1] - row0;
-  const int kv = a.kv_len[r];
-  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
-                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
-  const bool bad_cap = !bad_len && kv > kv_cap;
-  if (bad_len || bad_cap) {
-    if (tid == 0 && split == 0 && h == 0)
-      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
-    return;
-  }
   const int nrows = qo * G;
 
   // This lane's query row of every row tile (lane i of the tile), its token and bound.
@@ -162,20 +156,17 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
 
-  // The split's block list, staged in LDS, read back one block ahead of use.
-  BL bl;
-  bl.stage(ul, &chunk_lds, a, ds, ss, r, h, split, row0, qo, kv);
-  const int nblk = bl.nblk;
   // This wave's blocks: split-local b = wave + 4 j, j < nbw.
+  const int nblk = bl.nblk;
   const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;
 
-  auto fetch = [&](int b) { return bl.fetch(ul, b); };
+  auto fetch = [&](int b) { return bl.fetch(sh.ul, b); };
   auto resolve = [&](const typename BL::Raw& m, int b, uint64_t& kbase, uint64_t& vbase, int& pos0,
                      int& mask) { bl.resolve(m, b, h, Hkv, ds, ss, kbase, vbase, pos0, mask); };
 
   Cp copier;
   copier.init(lane);
-  char* wring = ring + wave * WAVE_RING;
+  char* wring = sh.ring + wave * WAVE_RING;
   const uint32_t wring_lds = lds_address(wring);
   const int all_tokens = qo >= 32 ? ~0 : (1 << qo) - 1;
   const int first_bound = kv - qo + 1;
@@ -314,8 +305,8 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
     l_run[rt] += __shfl_xor(l_run[rt], 16, kWave);
     l_run[rt] += __shfl_xor(l_run[rt], 32, kWave);
     if (q == 0) {
-      M_lds[wave][rt * 16 + i] = m_run[rt];
-      L_lds[wave][rt * 16 + i] = l_run[rt];
+      sh.M[wave][rt * 16 + i] = m_run[rt];
+      sh.L[wave][rt * 16 + i] = l_run[rt];
     }
   }
   __syncthreads();   // every wave is done with its ring; M and L are visible
@@ -323,14 +314,14 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = rt * 16 + i;
-    float mref = M_lds[0][row];
+    float mref = sh.M[0][row];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) mref = fmaxf(mref, M_lds[w][row]);
+    for (int w = 1; w < 4; ++w) mref = fmaxf(mref, sh.M[w][row]);
     float lt = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float mw = M_lds[w][row];
-      lt += mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mref) * L_lds[w][row];
+      const float mw = sh.M[w][row];
+      lt += mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mref) * sh.L[w][row];
     }
     m_ref[rt] = mref;
     l_tot[rt] = lt;
@@ -341,7 +332,7 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   // Piece k = 4 n' ... of a lane: element e of tile n is channel NT * (4q + e) + n; the
   // lane's 4 NT values form the contiguous channels q * D/4 .. q * D/4 + D/4 - 1, kept
   // as D/16 pieces of 4 floats: piece k holds channels q * D/4 + 4k .. + 3.
-  float4* reg0 = reinterpret_cast<float4*>(ring);
+  float4* reg0 = reinterpret_cast<float4*>(sh.ring);
   float4* reg1 = reg0 + ROWS * D / 4;
   auto lane_piece = [&](int rt, int k) {
     // channels c = q*D/4 + 4k + c4, c4 = 0..3  ->  (e, n) with NT*(4q+e) + n = c
@@ -404,7 +395,7 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) v[c] = o[rt][c % NT][c / NT] * inv;
     const int c0 = q * (D / 4);
-    if (a.num_splits == 1) {
+    if (out_slot < 0) {
       const int64_t idx = (qrow * a.num_q_heads + hq) * D + c0;
       if (a.out_dt == SDV_BF16) {
         uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + idx);
@@ -420,7 +411,7 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
     } else {
       // A row with no live position (an empty split) leaves its partial output unwritten:
       // the combine skips rows whose log-sum-exp is -inf.
-      const int64_t unit = (static_cast<int64_t>(split) * rows_cap + qrow) * a.num_q_heads + hq;
+      const int64_t unit = (static_cast<int64_t>(out_slot) * rows_cap + qrow) * a.num_q_heads + hq;
       if (L > 0.f) {
         float4* dst = reinterpret_cast<float4*>(a.part_o + unit * D + c0);
 #pragma unroll
@@ -428,6 +419,151 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
       }
       if (q == 0) a.part_lse[unit] = L > 0.f ? (m_ref[rt] + __log2f(L)) * kLn2 : -INFINITY;
     }
+  }
+}
+
+template <int RT, int D, int KDT, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
+  __shared__ WavesLds<RT, D, KDT, MODE> sh;
+  // Grid x = (request, KV head), y = split, so consecutive workgroups (dealt round-robin
+  // to the XCDs) are different (request, head) pairs of one split.
+  const int Hkv = a.num_kv_heads;
+  const int split = blockIdx.y;
+  const int h = blockIdx.x % Hkv;
+  const int r = blockIdx.x / Hkv;
+  const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
+                                           : static_cast<int64_t>(ss.max_pages) * kPage;
+  const int row0 = a.qo_indptr[r];
+  const int qo = a.qo_indptr[r + 1] - row0;
+  const int kv = a.kv_len[r];
+  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
+  const bool bad_cap = !bad_len && kv > kv_cap;
+  if (bad_len || bad_cap) {
+    if (threadIdx.x == 0 && split == 0 && h == 0)
+      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  // The split's block list, staged in LDS, read back one block ahead of use.
+  BlockList<MODE, D, KDT> bl;
+  bl.stage(sh.ul, &sh.chunk, a, ds, ss, r, h, split, row0, qo, kv);
+  waves_attend<RT, D, KDT, MODE>(sh, a, ds, ss, bl, r, h, row0, qo, kv,
+                                 a.num_splits > 1 ? split : -1);
+}
+
+// Dense persistent variant (split-KV in the "stream-K" manner): the (request, KV head)
+// pairs, request-major, laid end to end form one list of W 32-token blocks; workgroup g
+// takes blocks [g L, (g + 1) L) of that list, so every workgroup has the same amount of
+// work whatever the spread of kv_len.  Each piece of a pair inside the range is attended
+// by waves_attend and written as the partial of split slot (g - first workgroup of the
+// pair); the workgroup that ends a pair writes lse = -inf into the pair's later slots,
+// so the combine sees exactly num_splits slots per row.  L is at least
+// ceil(max blocks of a request / (num_splits - 1)), so no pair spans more than
+// num_splits workgroups, and at most kMaxDenseBlocks.  Requests with inconsistent
+// lengths count as empty (workgroup 0 flags them).
+template <int RT, int D, int KDT, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sdv_attn_waves_persist_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
+  static_assert(MODE != kSrcSparse, "dense sources only");
+  __shared__ WavesLds<RT, D, KDT, MODE> sh;
+  __shared__ int cum[kPersistMaxRequests + 1];   // blocks per request, then their prefix
+  __shared__ int seg_len;
+  const int tid = threadIdx.x;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int S = a.num_splits;
+  const int cap = MODE == kSrcView ? ds.max_sub_pages : 4 * ss.max_pages;
+  const int64_t kv_cap = static_cast<int64_t>(cap) * kSub;
+  for (int rr = tid; rr < a.B; rr += 256) {
+    const int row0 = a.qo_indptr[rr];
+    const int qo = a.qo_indptr[rr + 1] - row0;
+    const int kv = a.kv_len[rr];
+    const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
+                         static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
+    const bool bad_cap = !bad_len && kv > kv_cap;
+    if ((bad_len || bad_cap) && blockIdx.x == 0)
+      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    cum[rr] = bad_len || bad_cap ? 0 : (kv + kSub - 1) / kSub;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // exclusive prefix of the block counts in place (cum[B] = total), their maximum, and
+    // the range length L
+    int run = 0, mx = 0;
+    for (int c = 0; c < a.B; c += kWave) {
+      const int rr = c + tid;
+      const int v = rr < a.B ? cum[rr] : 0;
+      int inc = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(inc, off, kWave);
+        if (tid >= off) inc += t;
+      }
+      if (rr < a.B) cum[rr] = run + inc - v;
+      run += __shfl(inc, kWave - 1, kWave);
+      mx = max(mx, v);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, kWave));
+    if (tid == 0) {
+      cum[a.B] = run;
+      const int64_t work = static_cast<int64_t>(run) * Hkv;
+      const int64_t wgs = a.target_wgs > 0 ? a.target_wgs : 1;
+      int64_t len = max<int64_t>((work + wgs - 1) / wgs, (mx + S - 2) / (S - 1));
+      len = min<int64_t>(max<int64_t>(len, 1), kMaxDenseBlocks);
+      seg_len = static_cast<int>(len);
+    }
+  }
+  __syncthreads();
+  // values read from LDS are uniform: keep them in scalar registers
+  const int L = __builtin_amdgcn_readfirstlane(seg_len);
+  const int W = __builtin_amdgcn_readfirstlane(cum[a.B]) * Hkv;
+  const int g = blockIdx.x;
+  if (static_cast<int64_t>(g) * L >= W) return;
+  const int begin = g * L;
+  const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(begin) + L, W));
+  // the request holding `begin`: the last r with Hkv * cum[r] <= begin (it is not empty)
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(cum[mid]) * Hkv <= begin) lo = mid;
+    else hi = mid - 1;
+  }
+  int r = lo;
+  int pos = begin;
+  const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
+  while (pos < end) {
+    const int c0 = __builtin_amdgcn_readfirstlane(cum[r]);
+    const int nb = __builtin_amdgcn_readfirstlane(cum[r + 1]) - c0;
+    const int rstart = c0 * Hkv;
+    if (nb == 0 || pos >= rstart + nb * Hkv) {
+      ++r;
+      continue;
+    }
+    const int h = (pos - rstart) / nb;
+    const int pstart = rstart + h * nb;
+    const int pend = pstart + nb;
+    const int stop = min(end, pend);
+    const int slot = g - pstart / L;
+    const int row0 = a.qo_indptr[r];
+    const int qo = a.qo_indptr[r + 1] - row0;
+    const int kv = a.kv_len[r];
+    BlockList<MODE, D, KDT> bl;
+    bl.stage_range(sh.ul, a, ds, ss, r, pos - pstart, stop - pos);
+    waves_attend<RT, D, KDT, MODE>(sh, a, ds, ss, bl, r, h, row0, qo, kv, slot);
+    if (stop == pend) {
+      // the pair ends here: its later split slots hold no keys
+      const int rows = qo * G;
+      for (int e = tid; e < (S - 1 - slot) * rows; e += 256) {
+        const int k = slot + 1 + e / rows;
+        const int row = e % rows;
+        const int t = row / G;
+        a.part_lse[(k * rows_cap + row0 + t) * a.num_q_heads + h * G + (row - t * G)] = -INFINITY;
+      }
+    }
+    __syncthreads();   // LDS (ring, merge regions, block list) is reused by the next piece
+    pos = stop;
   }
 }
 
@@ -442,14 +578,31 @@ hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int RT, int D, int KDT, int MODE>
+hipError_t launch_persist_t(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
+                            int64_t cap_blocks, hipStream_t s) {
+  static const int per_cu = resident_per_cu(sdv_attn_waves_persist_kernel<RT, D, KDT, MODE>);
+  AttnArgs args = a;
+  args.target_wgs = per_cu * device_cu_count();
+  // enough workgroups for ranges of kMaxDenseBlocks when the balanced length is longer
+  const int64_t need = (static_cast<int64_t>(a.B) * a.num_kv_heads * cap_blocks + kMaxDenseBlocks - 1) /
+                       kMaxDenseBlocks;
+  const int64_t wgs = std::max<int64_t>(args.target_wgs, need);
+  hipLaunchKernelGGL((sdv_attn_waves_persist_kernel<RT, D, KDT, MODE>), dim3(static_cast<uint32_t>(wgs)),
+                     dim3(256), 0, s, args, ds, ss);
+  return hipGetLastError();
+}
+
+template <int MODE, bool PERSIST>
 hipError_t dispatch(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
-                    hipStream_t s) {
+                    int64_t cap_blocks, hipStream_t s) {
   const int rows = a.max_qo_len * (a.num_q_heads / a.num_kv_heads);
   const int rt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
 #define SDV_WAVES_CASE(RTV, DV, KDTV)                                                  \
-  if (rt == RTV && a.head_dim == DV && a.kv_dt == KDTV)                                \
-    return launch_t<RTV, DV, KDTV, MODE>(a, ds, ss, s);
+  if (rt == RTV && a.head_dim == DV && a.kv_dt == KDTV) {                              \
+    if constexpr (PERSIST) return launch_persist_t<RTV, DV, KDTV, MODE>(a, ds, ss, cap_blocks, s); \
+    else return launch_t<RTV, DV, KDTV, MODE>(a, ds, ss, s);                           \
+  }
   SDV_WAVES_CASE(1, 128, SDV_BF16)
   SDV_WAVES_CASE(2, 128, SDV_BF16)
   SDV_WAVES_CASE(4, 128, SDV_BF16)
@@ -469,15 +622,30 @@ hipError_t dispatch(const AttnArgs& a, const DenseSource& ds, const SparseSource
 }  // namespace
 
 hipError_t launch_attn_dense_waves(const AttnArgs& a, const DenseSource& src, hipStream_t s) {
-  return dispatch<kSrcView>(a, src, SparseSource{}, s);
+  return dispatch<kSrcView, false>(a, src, SparseSource{}, 0, s);
 }
 
 hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
-  return dispatch<kSrcSparse>(a, DenseSource{}, src, s);
+  return dispatch<kSrcSparse, false>(a, DenseSource{}, src, 0, s);
 }
 
 hipError_t launch_attn_paged_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
-  return dispatch<kSrcPaged>(a, DenseSource{}, src, s);
+  return dispatch<kSrcPaged, false>(a, DenseSource{}, src, 0, s);
+}
+
+bool persist_supported(const AttnArgs& a, int64_t cap_blocks) {
+  if (a.num_splits < 2 || a.B > kPersistMaxRequests || cap_blocks < 1) return false;
+  if ((cap_blocks + a.num_splits - 2) / (a.num_splits - 1) > kMaxDenseBlocks) return false;
+  // every flattened block index and every split slot's row index fits in 32 bits
+  return static_cast<int64_t>(a.B) * a.num_kv_heads * cap_blocks <= INT32_MAX;
+}
+
+hipError_t launch_attn_dense_persist(const AttnArgs& a, const DenseSource& src, hipStream_t s) {
+  return dispatch<kSrcView, true>(a, src, SparseSource{}, src.max_sub_pages, s);
+}
+
+hipError_t launch_attn_paged_persist(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
+  return dispatch<kSrcPaged, true>(a, DenseSource{}, src, 4ll * src.max_pages, s);
 }
 
 }  // namespace sdv

@@ -73,32 +73,8 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   const int p_first = blockIdx.x * PPB;
   if (p_first >= n_pages_r) return;
 
-  // Stage this request's queries of KV head h as float: q_lds[(t * G + g) * D + c], eight
-  // channels (one 16- or 32-byte load) per thread and step.
-  for (int i8 = threadIdx.x; i8 < qo * G * (D / 8); i8 += blockDim.x) {
-    const int tg = i8 / (D / 8);
-    const int c0 = (i8 - tg * (D / 8)) * 8;
-    const int t = tg / G;
-    const int g = tg - t * G;
-    const int64_t src = (static_cast<int64_t>(row0 + t) * num_q_heads + h * G + g) * D + c0;
-    float* dst = q_lds + tg * D + c0;
-    if (q_dt == SDV_F32) {
-      const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + src);
-      const float4 x0 = s4[0], x1 = s4[1];
-      reinterpret_cast<float4*>(dst)[0] = x0;
-      reinterpret_cast<float4*>(dst)[1] = x1;
-    } else {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + src);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dst[2 * k] = __uint_as_float(ws[k] << 16);
-        dst[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
-      }
-    }
-  }
-  __syncthreads();
-
+  // This lane group's page: its block-table entry is loaded first, so that its latency
+  // overlaps the query staging below.
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int grp = lane / LPR;
@@ -106,14 +82,51 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   const int p = p_first + wave * PPW + grp;
   bool active = p < n_pages_r;
   int32_t phys = 0;
-  if (active) {
-    phys = block_table[static_cast<int64_t>(r) * bt_stride + p];
-    if (phys < 0 || phys >= num_pages) {
-      set_err(dev_err, SDV_DEVERR_PAGE_RANGE);
-      active = false;
-      phys = 0;
+  if (active) phys = block_table[static_cast<int64_t>(r) * bt_stride + p];
+
+  // Stage this request's queries of KV head h as float: q_lds[(t * G + g) * D + c], eight
+  // channels (one 16- or 32-byte load) per item, QB items per thread in flight at once.
+  constexpr int QB = 4;
+  const int q_items = qo * G * (D / 8);
+  for (int i0 = threadIdx.x; i0 < q_items; i0 += QB * blockDim.x) {
+    float4 x[QB][2];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      const int i8 = i0 + k * blockDim.x;
+      if (i8 >= q_items) continue;
+      const int tg = i8 / (D / 8);
+      const int c0 = (i8 - tg * (D / 8)) * 8;
+      const int t = tg / G;
+      const int g = tg - t * G;
+      const int64_t src = (static_cast<int64_t>(row0 + t) * num_q_heads + h * G + g) * D + c0;
+      if (q_dt == SDV_F32) {
+        const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + src);
+        x[k][0] = s4[0];
+        x[k][1] = s4[1];
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + src);
+        x[k][0] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+        x[k][1] = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                              __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      const int i8 = i0 + k * blockDim.x;
+      if (i8 >= q_items) continue;
+      float4* dst = reinterpret_cast<float4*>(q_lds + static_cast<int64_t>(i8) * 8);
+      dst[0] = x[k][0];
+      dst[1] = x[k][1];
     }
   }
+  __syncthreads();
+
+  if (active && (phys < 0 || phys >= num_pages)) {
+    set_err(dev_err, SDV_DEVERR_PAGE_RANGE);
+    active = false;
+  }
+  if (!active) phys = 0;
   const char* kp = reinterpret_cast<const char*>(kbase) +
                    (static_cast<int64_t>(phys) * page_stride + static_cast<int64_t>(h) * kPage * D) * EB +
                    sub * 16;
@@ -131,10 +144,10 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     L = L < 0 ? 0 : (L > kPage ? kPage : L);
     // Step 1: extend the running sums to the first L positions of the page.
     for (; j + U <= L; j += U) {
+      const char* rows = kp + static_cast<int64_t>(j) * ROW_BYTES;
       uint4 w[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        w[u] = load_stream(kp + static_cast<int64_t>(j + u) * ROW_BYTES);
+      for (int u = 0; u < U; ++u) w[u] = load_stream(rows + u * ROW_BYTES);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[V];

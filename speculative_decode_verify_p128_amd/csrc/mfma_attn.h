@@ -278,7 +278,6 @@ struct BlockList {
   __device__ __forceinline__ void stage(Lds& ul, int* chunk_lds, const AttnArgs& a,
                                         const DenseSource& ds, const SparseSource& ss, int r,
                                         int h, int split, int row0, int qo, int kv) {
-    const int tid = threadIdx.x;
     if constexpr (MODE == kSrcSparse) {
       const int n_union = build_union(ul, ss, r, h, a.num_kv_heads, row0, qo, kv, a.dev_err);
       const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
@@ -288,28 +287,39 @@ struct BlockList {
       const int cap = MODE == kSrcView ? ds.max_sub_pages : 4 * ss.max_pages;
       const int chunk = dense_chunk(a, cap, chunk_lds);
       const int nb = (kv + kSub - 1) / kSub;
-      base = split * chunk;
-      nblk = max(0, min(nb, base + chunk) - base);
-      if constexpr (MODE == kSrcView) {
-        const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
-        for (int b = tid; b < nblk; b += 256) {
-          const int32_t xk = offs[base + b];
-          const int32_t xv = offs[ds.max_sub_pages + base + b];
-          const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
-          if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
-          ul.x[b] = ok ? xk : -1;
-        }
-      } else {
-        const int32_t* bt = ss.block_table + static_cast<int64_t>(r) * ss.bt_stride;
-        for (int b = tid; b < nblk; b += 256) {
-          const int32_t phys = bt[(base + b) >> 2];
-          const bool ok = phys >= 0 && phys < ss.num_pages;
-          if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
-          ul.x[b] = ok ? phys : -1;
-        }
-      }
-      __syncthreads();
+      const int first = split * chunk;
+      stage_range(ul, a, ds, ss, r, first, max(0, min(nb, first + chunk) - first));
     }
+  }
+
+  // Dense only: blocks [first, first + n) of request r, n <= kMaxDenseBlocks.  Every
+  // block's page index is checked against the pool (out of range: flagged, and the block
+  // is read masked out).  All 256 threads call; ends with a barrier.
+  __device__ __forceinline__ void stage_range(Lds& ul, const AttnArgs& a, const DenseSource& ds,
+                                              const SparseSource& ss, int r, int first, int n) {
+    static_assert(MODE != kSrcSparse, "dense block lists only");
+    const int tid = threadIdx.x;
+    base = first;
+    nblk = n;
+    if constexpr (MODE == kSrcView) {
+      const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
+      for (int b = tid; b < nblk; b += 256) {
+        const int32_t xk = offs[base + b];
+        const int32_t xv = offs[ds.max_sub_pages + base + b];
+        const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
+        if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+        ul.x[b] = ok ? xk : -1;
+      }
+    } else {
+      const int32_t* bt = ss.block_table + static_cast<int64_t>(r) * ss.bt_stride;
+      for (int b = tid; b < nblk; b += 256) {
+        const int32_t phys = bt[(base + b) >> 2];
+        const bool ok = phys >= 0 && phys < ss.num_pages;
+        if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
+        ul.x[b] = ok ? phys : -1;
+      }
+    }
+    __syncthreads();
   }
 
   // Metadata of split-local block b as stored (wave-uniform values in vector registers).

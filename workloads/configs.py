@@ -116,7 +116,7 @@ RAGGED_MIXED = VerifyWorkload(
 PAGED_BF16 = VerifyWorkload(
     name="paged_bf16", batch=64, qo=4, kv=("uniform", 4096, 32768),
     num_q_heads=16, num_kv_heads=4, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
-    values="normal", top_k=16, num_splits=1)
+    values="normal", top_k=16, num_splits=3)
 
 ALL = (TINY_FP32, DENSE_BF16, SPARSE_BF16, LONG_FP8, RAGGED_MIXED, PAGED_BF16)
 BY_NAME = {w.name: w for w in ALL}
