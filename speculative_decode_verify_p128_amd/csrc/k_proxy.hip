@@ -23,7 +23,9 @@
 //   scores a token as soon as the running sum reaches that token's bound; the
 //   tokens' bounds differ by one position, so every token shares one pass.
 //   The halving tree first pairs channels c and c + d/2, which live in different
-//   lanes of the group (xor shuffles), and ends inside the lane.
+//   lanes of the group (DPP row shifts inside 16-lane rows), and ends inside the lane.
+//   Granularity matters more than per-wave start-up: four pages per wave measured
+//   faster than eight or sixteen streamed one after another by the same lanes.
 #include "device.h"
 #include "internal.h"
 
@@ -38,6 +40,30 @@ __device__ __forceinline__ uint4 load_stream(const char* p) {
 }
 
 constexpr int kProxyWaves = 1;   // waves per workgroup
+
+// Value of lane l + OFF for lane l, valid where l % 16 + OFF < 16 (and for every lane
+// when OFF >= 16); the halving tree reads it only in lanes whose partner is OFF above.
+// Within a 16-lane row a DPP row shift does the exchange inside the vector ALU; across
+// rows the LDS crossbar does.
+template <int OFF>
+__device__ __forceinline__ float lane_above(float v) {
+  if constexpr (OFF < 16) {
+    constexpr int kRowShl = 0x100;   // DPP row_shl:n, n = 1 .. 15: lane l reads lane l + n
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                              kRowShl + OFF, 0xF, 0xF, false));
+  } else {
+    return __shfl_xor(v, OFF, kWave);
+  }
+}
+
+template <int OFF, int V>
+__device__ __forceinline__ void halving_levels(float (&u)[V]) {
+  if constexpr (OFF >= 1) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) u[e] = u[e] + lane_above<OFF>(u[e]);
+    halving_levels<OFF / 2, V>(u);
+  }
+}
 
 template <int KDT, int D>
 __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
@@ -166,16 +192,19 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     // Steps 2-4 for every query head of the group.
     float best = -INFINITY;
     for (int g = 0; g < G; ++g) {
-      const float* qv = q_lds + (t * G + g) * D + sub * V;
+      const float4* qv = reinterpret_cast<const float4*>(q_lds + (t * G + g) * D + sub * V);
       float u[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) u[e] = qv[e] * acc[e];
-      // channel c pairs with c + n/2: across lanes while n/2 >= V ...
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) u[e] = u[e] + __shfl_xor(u[e], off, kWave);
+      for (int e4 = 0; e4 < V / 4; ++e4) {
+        const float4 q4 = qv[e4];
+        u[4 * e4 + 0] = q4.x * acc[4 * e4 + 0];
+        u[4 * e4 + 1] = q4.y * acc[4 * e4 + 1];
+        u[4 * e4 + 2] = q4.z * acc[4 * e4 + 2];
+        u[4 * e4 + 3] = q4.w * acc[4 * e4 + 3];
       }
+      // channel c pairs with c + n/2: across lanes while n/2 >= V (lane l of the group
+      // adds lane l + n/(2V), so the live lanes are the low half of the previous ones) ...
+      halving_levels<LPR / 2, V>(u);
       // ... then inside the lane.
 #pragma unroll
       for (int n = V; n >= 2; n >>= 1) {
