@@ -55,7 +55,7 @@ struct BlockCopier {
       const int ins = wave * Gm::LPT + n;               // 0 .. 2 * 32 / RPI - 1
       const int half = ins / (32 / Gm::RPI);            // 0 = K, 1 = V
       const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
-      const int gchunk = ((lane % Gm::CPR) ^ row) & (Gm::CPR - 1);
+      const int gchunk = ((lane % Gm::CPR) ^ Gm::swz(row)) & (Gm::CPR - 1);
       off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
       lds[n] = static_cast<uint32_t>(half * Gm::HALF + (ins % (32 / Gm::RPI)) * 64 * 16);
       is_v[n] = half != 0;

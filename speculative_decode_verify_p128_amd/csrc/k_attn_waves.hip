@@ -50,7 +50,7 @@ struct WaveCopier {
 #pragma unroll
     for (int n = 0; n < PER_HALF; ++n) {
       const int row = n * Gm::RPI + lane / Gm::CPR;
-      const int gchunk = ((lane % Gm::CPR) ^ row) & (Gm::CPR - 1);
+      const int gchunk = ((lane % Gm::CPR) ^ Gm::swz(row)) & (Gm::CPR - 1);
       off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
     }
   }
@@ -79,11 +79,12 @@ struct WaveCopier {
   }
 };
 
-// Merge buffer slot of (row, 16-byte piece k of the row): pieces are XOR-swizzled by the
-// row so that 16 lanes writing the same piece of 16 rows hit different banks.
+// Merge buffer slot of (row, 16-byte piece k of the row): pieces are XOR-swizzled by a
+// key of the row (row_key16), as the K/V rows are, since lane (i, q) accesses piece
+// q * D/16 + k of row i: the same lane-to-bank-group pattern as the K operand reads.
 template <int D>
 __device__ __forceinline__ int merge_index(int row, int k) {
-  return row * (D / 4) + (k ^ (row & 15));
+  return row * (D / 4) + (k ^ row_key16(row & 15));
 }
 
 // LDS of the per-wave kernels: the four waves' rings (the merge regions reuse them), the
