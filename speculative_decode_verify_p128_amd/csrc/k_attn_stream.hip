@@ -92,31 +92,41 @@ struct BlockCopier {
 template <int RT>
 constexpr int ring_stages() { return 4; }
 
+// LDS of the ring kernels: the block ring (after the last block the same bytes stage
+// the output rows), the rows' maxima and sums, and the staged block list.
 template <int RT, int D, int KDT, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
-sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
-                                                             SparseSource ss) {
+struct RingLds {
   using Gm = Geo<D, KDT>;
+  static constexpr int ROWS = RT * 16;
+  static constexpr int OPAD = D + 4;
+  static constexpr int RING = ring_stages<RT>() * Gm::BLOCK;
+  static constexpr int OUTB = ROWS * OPAD * 4;
+  __attribute__((aligned(16))) char ring[RING > OUTB ? RING : OUTB];
+  float L[ROWS];
+  float M[ROWS];
+  typename BlockList<MODE, D, KDT>::Lds ul;
+  int chunk;
+};
+
+// Attention of the G x qo query rows of (request r, KV head h) over the staged block
+// range `bl` (metadata in sh.ul), written as the final rows (out_slot < 0) or as the
+// normalised partial and log-sum-exp of split slot out_slot.  All 256 threads call; LDS
+// is free again only after a barrier that follows the call.
+template <int RT, int D, int KDT, int MODE>
+__device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE>& sh, const AttnArgs& a,
+                                            const DenseSource& ds, const SparseSource& ss,
+                                            const BlockList<MODE, D, KDT>& bl, int r, int h,
+                                            int row0, int qo, int kv, int out_slot) {
+  using Gm = Geo<D, KDT>;
+  using BL = BlockList<MODE, D, KDT>;
   constexpr int STEPS = Gm::STEPS;
   constexpr int NT = Gm::NT;
   constexpr int NCP = 4 / RT;          // output-channel parts
   constexpr int NTW = NT / NCP;        // output tiles per wave
-  constexpr int ROWS = RT * 16;
   constexpr int OPAD = D + 4;
   constexpr int kStages = ring_stages<RT>();
   static_assert(NTW >= 1, "tiles per wave");
-
-  // The block ring; after the last block the same bytes stage the output rows.
-  constexpr int RING = kStages * Gm::BLOCK;
-  constexpr int OUTB = ROWS * OPAD * 4;
-  __shared__ __attribute__((aligned(16))) char ring[RING > OUTB ? RING : OUTB];
-  float (*o_lds)[OPAD] = reinterpret_cast<float (*)[OPAD]>(ring);
-  __shared__ float L_lds[ROWS];
-  __shared__ float M_lds[ROWS];
-  using BL = BlockList<MODE, D, KDT>;
-  __shared__ typename BL::Lds ul;
-  __shared__ int chunk_lds;
-
+  float (*o_lds)[OPAD] = reinterpret_cast<float (*)[OPAD]>(sh.ring);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -125,29 +135,8 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   const int rt = wave % RT;
   const int cp = wave / RT;
   const int n0 = cp * NTW;
-  // Grid x = (request, KV head), y = split: consecutive workgroups, which the hardware
-  // deals round-robin to the eight XCDs, are different (request, head) pairs of the same
-  // split, so long and short requests spread evenly over the XCDs, and the high splits
-  // (empty for short requests) are dispatched last.
   const int Hkv = a.num_kv_heads;
-  const int split = blockIdx.y;
-  const int h = blockIdx.x % Hkv;
-  const int r = blockIdx.x / Hkv;
   const int G = a.num_q_heads / Hkv;
-
-  const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
-                                           : static_cast<int64_t>(ss.max_pages) * kPage;
-  const int row0 = a.qo_indptr[r];
-  const int qo = a.qo_indptr[r + 1] - row0;
-  const int kv = a.kv_len[r];
-  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
-                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
-  const bool bad_cap = !bad_len && kv > kv_cap;
-  if (bad_len || bad_cap) {
-    if (tid == 0 && split == 0 && h == 0)
-      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
-    return;
-  }
   const int nrows = qo * G;
 
   // This wave's query row (lane i of row tile rt), its token and its ladder bound.
@@ -174,19 +163,17 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
 
-  BL bl;
-  bl.stage(ul, &chunk_lds, a, ds, ss, r, h, split, row0, qo, kv);
   const int nblk = bl.nblk;
 
   // Metadata of block b as stored in LDS (wave-uniform values, still in vector registers).
   // It is fetched one block ahead of its use, so the read's latency hides under compute.
-  auto fetch = [&](int b) { return bl.fetch(ul, b); };
+  auto fetch = [&](int b) { return bl.fetch(sh.ul, b); };
   auto resolve = [&](const typename BL::Raw& m, int b, uint64_t& kbase, uint64_t& vbase, int& pos0,
                      int& mask) { bl.resolve(m, b, h, Hkv, ds, ss, kbase, vbase, pos0, mask); };
 
   BlockCopier<D, KDT> copier;
   copier.init(__builtin_amdgcn_readfirstlane(wave), lane);
-  const uint32_t ring_lds = lds_address(ring);
+  const uint32_t ring_lds = lds_address(sh.ring);
   // Blocks wholly inside every row's ladder bound and chosen by every token need no
   // masking: the common case, tested once per block for the whole workgroup.
   const int all_tokens = qo >= 32 ? ~0 : (1 << qo) - 1;
@@ -227,7 +214,7 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
 
     // All of this wave's reads of the block first, so their latency runs under the copy
     // issue below and under the score products.
-    const char* kb = ring + u * Gm::BLOCK;
+    const char* kb = sh.ring + u * Gm::BLOCK;
     const char* vb = kb + Gm::HALF;
     bf16x8 kop[2][STEPS];
 #pragma unroll
@@ -329,8 +316,8 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   if (cp == 0 && q == 0) {
-    L_lds[row] = l_run;
-    M_lds[row] = m_run;
+    sh.L[row] = l_run;
+    sh.M[row] = m_run;
   }
 #pragma unroll
   for (int n = 0; n < NTW; ++n)
@@ -346,12 +333,12 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     const int g = orow - t * G;
     const int hq = h * G + g;
     const int64_t qrow = row0 + t;
-    const float L = L_lds[orow];
+    const float L = sh.L[orow];
     const float inv = L > 0.f ? a.v_scale / L : 0.f;
     float v8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v8[e] = o_lds[orow][c0 + e] * inv;
-    if (a.num_splits == 1) {
+    if (out_slot < 0) {
       const int64_t idx = (qrow * a.num_q_heads + hq) * D + c0;
       if (a.out_dt == SDV_BF16) {
         const uint4 w = make_uint4(pack2_bf16(v8[0], v8[1]), pack2_bf16(v8[2], v8[3]),
@@ -365,16 +352,46 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds,
     } else {
       // A row with no live position (an empty split) leaves its partial output unwritten:
       // the combine skips rows whose log-sum-exp is -inf.
-      const int64_t unit = (static_cast<int64_t>(split) * rows_cap + qrow) * a.num_q_heads + hq;
+      const int64_t unit = (static_cast<int64_t>(out_slot) * rows_cap + qrow) * a.num_q_heads + hq;
       if (L > 0.f) {
         float4* dst = reinterpret_cast<float4*>(a.part_o + unit * D + c0);
         dst[0] = make_float4(v8[0], v8[1], v8[2], v8[3]);
         dst[1] = make_float4(v8[4], v8[5], v8[6], v8[7]);
       }
       if (c0 == 0)
-        a.part_lse[unit] = L > 0.f ? (M_lds[orow] + __log2f(L)) * kLn2 : -INFINITY;
+        a.part_lse[unit] = L > 0.f ? (sh.M[orow] + __log2f(L)) * kLn2 : -INFINITY;
     }
   }
+}
+
+template <int RT, int D, int KDT, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+sdv_attn_stream_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
+  __shared__ RingLds<RT, D, KDT, MODE> sh;
+  // Grid x = (request, KV head), y = split: consecutive workgroups, which the hardware
+  // deals round-robin to the eight XCDs, are different (request, head) pairs of the same
+  // split, so long and short requests spread evenly over the XCDs, and the high splits
+  // (empty for short requests) are dispatched last.
+  const int Hkv = a.num_kv_heads;
+  const int split = blockIdx.y;
+  const int h = blockIdx.x % Hkv;
+  const int r = blockIdx.x / Hkv;
+  const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
+                                           : static_cast<int64_t>(ss.max_pages) * kPage;
+  const int row0 = a.qo_indptr[r];
+  const int qo = a.qo_indptr[r + 1] - row0;
+  const int kv = a.kv_len[r];
+  const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
+  const bool bad_cap = !bad_len && kv > kv_cap;
+  if (bad_len || bad_cap) {
+    if (threadIdx.x == 0 && split == 0 && h == 0)
+      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  BlockList<MODE, D, KDT> bl;
+  bl.stage(sh.ul, &sh.chunk, a, ds, ss, r, h, split, row0, qo, kv);
+  ring_attend<RT, D, KDT, MODE>(sh, a, ds, ss, bl, r, h, row0, qo, kv, a.num_splits > 1 ? split : -1);
 }
 
 template <int RT, int D, int KDT, int MODE>

@@ -453,119 +453,20 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
                                  a.num_splits > 1 ? split : -1);
 }
 
-// Dense persistent variant (split-KV in the "stream-K" manner): the (request, KV head)
-// pairs, request-major, laid end to end form one list of W 32-token blocks; workgroup g
-// takes blocks [g L, (g + 1) L) of that list, so every workgroup has the same amount of
-// work whatever the spread of kv_len.  Each piece of a pair inside the range is attended
-// by waves_attend and written as the partial of split slot (g - first workgroup of the
-// pair); the workgroup that ends a pair writes lse = -inf into the pair's later slots,
-// so the combine sees exactly num_splits slots per row.  L is at least
-// ceil(max blocks of a request / (num_splits - 1)), so no pair spans more than
-// num_splits workgroups, and at most kMaxDenseBlocks.  Requests with inconsistent
-// lengths count as empty (workgroup 0 flags them).
+// Dense persistent variant: equal ranges of 32-token blocks per workgroup across all
+// (request, KV head) pairs (persistent_walk), each piece attended as above.
 template <int RT, int D, int KDT, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sdv_attn_waves_persist_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   static_assert(MODE != kSrcSparse, "dense sources only");
   __shared__ WavesLds<RT, D, KDT, MODE> sh;
-  __shared__ int cum[kPersistMaxRequests + 1];   // blocks per request, then their prefix
-  __shared__ int seg_len;
-  const int tid = threadIdx.x;
-  const int Hkv = a.num_kv_heads;
-  const int G = a.num_q_heads / Hkv;
-  const int S = a.num_splits;
-  const int cap = MODE == kSrcView ? ds.max_sub_pages : 4 * ss.max_pages;
-  const int64_t kv_cap = static_cast<int64_t>(cap) * kSub;
-  for (int rr = tid; rr < a.B; rr += 256) {
-    const int row0 = a.qo_indptr[rr];
-    const int qo = a.qo_indptr[rr + 1] - row0;
-    const int kv = a.kv_len[rr];
-    const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
-                         static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
-    const bool bad_cap = !bad_len && kv > kv_cap;
-    if ((bad_len || bad_cap) && blockIdx.x == 0)
-      set_err(a.dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
-    cum[rr] = bad_len || bad_cap ? 0 : (kv + kSub - 1) / kSub;
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    // exclusive prefix of the block counts in place (cum[B] = total), their maximum, and
-    // the range length L
-    int run = 0, mx = 0;
-    for (int c = 0; c < a.B; c += kWave) {
-      const int rr = c + tid;
-      const int v = rr < a.B ? cum[rr] : 0;
-      int inc = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_up(inc, off, kWave);
-        if (tid >= off) inc += t;
-      }
-      if (rr < a.B) cum[rr] = run + inc - v;
-      run += __shfl(inc, kWave - 1, kWave);
-      mx = max(mx, v);
-    }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, kWave));
-    if (tid == 0) {
-      cum[a.B] = run;
-      const int64_t work = static_cast<int64_t>(run) * Hkv;
-      const int64_t wgs = a.target_wgs > 0 ? a.target_wgs : 1;
-      int64_t len = max<int64_t>((work + wgs - 1) / wgs, (mx + S - 2) / (S - 1));
-      len = min<int64_t>(max<int64_t>(len, 1), kMaxDenseBlocks);
-      seg_len = static_cast<int>(len);
-    }
-  }
-  __syncthreads();
-  // values read from LDS are uniform: keep them in scalar registers
-  const int L = __builtin_amdgcn_readfirstlane(seg_len);
-  const int W = __builtin_amdgcn_readfirstlane(cum[a.B]) * Hkv;
-  const int g = blockIdx.x;
-  if (static_cast<int64_t>(g) * L >= W) return;
-  const int begin = g * L;
-  const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(begin) + L, W));
-  // the request holding `begin`: the last r with Hkv * cum[r] <= begin (it is not empty)
-  int lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(cum[mid]) * Hkv <= begin) lo = mid;
-    else hi = mid - 1;
-  }
-  int r = lo;
-  int pos = begin;
-  const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
-  while (pos < end) {
-    const int c0 = __builtin_amdgcn_readfirstlane(cum[r]);
-    const int nb = __builtin_amdgcn_readfirstlane(cum[r + 1]) - c0;
-    const int rstart = c0 * Hkv;
-    if (nb == 0 || pos >= rstart + nb * Hkv) {
-      ++r;
-      continue;
-    }
-    const int h = (pos - rstart) / nb;
-    const int pstart = rstart + h * nb;
-    const int pend = pstart + nb;
-    const int stop = min(end, pend);
-    const int slot = g - pstart / L;
-    const int row0 = a.qo_indptr[r];
-    const int qo = a.qo_indptr[r + 1] - row0;
-    const int kv = a.kv_len[r];
-    BlockList<MODE, D, KDT> bl;
-    bl.stage_range(sh.ul, a, ds, ss, r, pos - pstart, stop - pos);
-    waves_attend<RT, D, KDT, MODE>(sh, a, ds, ss, bl, r, h, row0, qo, kv, slot);
-    if (stop == pend) {
-      // the pair ends here: its later split slots hold no keys
-      const int rows = qo * G;
-      for (int e = tid; e < (S - 1 - slot) * rows; e += 256) {
-        const int k = slot + 1 + e / rows;
-        const int row = e % rows;
-        const int t = row / G;
-        a.part_lse[(k * rows_cap + row0 + t) * a.num_q_heads + h * G + (row - t * G)] = -INFINITY;
-      }
-    }
-    __syncthreads();   // LDS (ring, merge regions, block list) is reused by the next piece
-    pos = stop;
-  }
+  __shared__ PersistLds pl;
+  persistent_walk<MODE>(pl, a, ds, ss,
+                        [&](int r, int h, int row0, int qo, int kv, int first, int n, int slot) {
+                          BlockList<MODE, D, KDT> bl;
+                          bl.stage_range(sh.ul, a, ds, ss, r, first, n);
+                          waves_attend<RT, D, KDT, MODE>(sh, a, ds, ss, bl, r, h, row0, qo, kv, slot);
+                        });
 }
 
 template <int RT, int D, int KDT, int MODE>

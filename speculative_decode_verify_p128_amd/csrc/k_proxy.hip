@@ -164,14 +164,24 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   int j = 0;
   float* out_rows = scores + (static_cast<int64_t>(row0) * Hkv + h) * max_pages + p;
 
+  // Positions of this page below token t's bound.
+  auto rows_below = [&](int t) {
+    const int L = active ? kv - qo + t + 1 - p * kPage : 0;
+    return L < 0 ? 0 : (L > kPage ? kPage : L);
+  };
+  const int L_last = rows_below(qo - 1);
+  // One register batch serves both the full steps and the page's last, partial stretch:
+  // rows rb .. rb + U - 1 stay in w across tokens (rb < 0: w holds no such stretch), so
+  // the remainder rows of every token (the last token's bound ends up to qo - 1 rows
+  // further) come from one batch of loads instead of one load after another.
+  uint4 w[U];
+  int rb = -1;
   for (int t = 0; t < qo; ++t) {
-    const int bound = kv - qo + t + 1;
-    int L = active ? bound - p * kPage : 0;
-    L = L < 0 ? 0 : (L > kPage ? kPage : L);
+    const int L = rows_below(t);
     // Step 1: extend the running sums to the first L positions of the page.
     for (; j + U <= L; j += U) {
+      rb = -1;
       const char* rows = kp + static_cast<int64_t>(j) * ROW_BYTES;
-      uint4 w[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) w[u] = load_stream(rows + u * ROW_BYTES);
 #pragma unroll
@@ -182,12 +192,26 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
         for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
       }
     }
-    for (; j < L; ++j) {
-      const uint4 w = load_stream(kp + static_cast<int64_t>(j) * ROW_BYTES);
-      float x[V];
-      V16::decode(w, x);
+    if (j < L) {
+      if (rb < 0 || L > rb + U) {
+        // rows j .. min(j + U, L_last) - 1; the rest of the batch repeats the last of
+        // them (in bounds, never added)
+        rb = j;
+        const int last = (rb + U < L_last ? rb + U : L_last) - 1;
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
+        for (int u = 0; u < U; ++u)
+          w[u] = load_stream(kp + static_cast<int64_t>(rb + u < last ? rb + u : last) * ROW_BYTES);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (rb + u >= j && rb + u < L) {
+          float x[V];
+          V16::decode(w[u], x);
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
+        }
+      }
+      j = L;
     }
     // Steps 2-4 for every query head of the group.
     float best = -INFINITY;

@@ -19,7 +19,7 @@ if torch.cuda.is_available():
     from _parity import (DEV, DenseRun, PagedRun, dense_oracle, out_numpy, paged_oracle,
                          rows_of, tol_ok)
 
-FAMILY = 5
+FAMILIES = [5]   # the per-wave kernel under the persistent partition
 
 MANY_SHORT_VIEW = W.DENSE_BF16.scaled(name="many_short_view", batch=600, kv=("uniform", 4, 100),
                                       kv_capacity=128, num_q_heads=16)
@@ -49,14 +49,15 @@ def _paged(w):
 @pytest.fixture(autouse=True)
 def _announce(request):
     print(f"\n[gpu] {request.node.name}", flush=True)
-    sdv.set_kernel_family(FAMILY)
     yield
     sdv.set_kernel_family(0)
 
 
+@pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("splits", [2, 3, 16])
 @pytest.mark.parametrize("w", [MANY_SHORT_VIEW, FEW_LONG_VIEW], ids=lambda w: w.name)
-def test_persist_view_parity(w, splits):
+def test_persist_view_parity(w, splits, family):
+    sdv.set_kernel_family(family)
     c, ref = _dense(w)
     run = DenseRun(c)
     view, offs = run.view()
@@ -68,10 +69,12 @@ def test_persist_view_parity(w, splits):
     assert ok, f"max abs err {worst}"
 
 
+@pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("splits", [2, 3, 16])
 @pytest.mark.parametrize("w", [MANY_SHORT_PAGED, FEW_LONG_PAGED, RAGGED_PAGED_FP8],
                          ids=lambda w: w.name)
-def test_persist_paged_parity(w, splits):
+def test_persist_paged_parity(w, splits, family):
+    sdv.set_kernel_family(family)
     c, ref = _paged(w)
     run = PagedRun(c)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -82,11 +85,13 @@ def test_persist_paged_parity(w, splits):
     assert ok, f"max abs err {worst}"
 
 
-def test_persist_inconsistent_requests_flagged_others_exact():
+@pytest.mark.parametrize("family", FAMILIES)
+def test_persist_inconsistent_requests_flagged_others_exact(family):
     """Request 2 shorter than its verify tokens, request 5 beyond the table's capacity:
     both are flagged and count as empty; every other request matches the oracle."""
     w = W.PAGED_BF16.scaled(name="persist_flags", batch=8, kv=("uniform", 200, 2000),
                             kv_capacity=2048)
+    sdv.set_kernel_family(family)
     c = W.make_sparse_case(w)
     run = PagedRun(c)
     kv_bad = c.kv_len.clone()
@@ -104,9 +109,11 @@ def test_persist_inconsistent_requests_flagged_others_exact():
     assert ok, worst
 
 
-def test_persist_matches_per_split_kernel_at_benchmark_size():
+@pytest.mark.parametrize("family", FAMILIES)
+def test_persist_matches_per_split_kernel_at_benchmark_size(family):
     """The dense benchmark configuration: the persistent kernel and the per-split kernel
     agree to the bf16 tolerance on every row, and sampled requests match the oracle."""
+    sdv.set_kernel_family(family)
     w = W.DENSE_BF16
     c = W.make_dense_case(w, device=DEV)
     run = DenseRun(c)
