@@ -212,6 +212,85 @@ def cpu_baseline(case, n_req):
                       f"sparse attention, one thread; {dt:.1f} s"}
 
 
+def _oracle_worker_init():
+    """Worker start-up (untimed): one BLAS/OpenMP thread, the oracle imported."""
+    from threadpoolctl import threadpool_limits
+    import oracle  # noqa: F401
+    threadpool_limits(limits=1)
+
+
+def _oracle_worker(task):
+    """One process of the all-cores oracle timing: attaches the shared inputs and runs the
+    oracle, one thread, on its share of the requests."""
+    from multiprocessing import shared_memory
+    from threadpoolctl import threadpool_limits
+    import oracle
+    names, shapes, dtypes, meta, req = task
+    shms = [shared_memory.SharedMemory(name=n) for n in names]
+    try:
+        q_raw, kp, vp, bt, ind, kvl = [np.ndarray(sh, dtype=dt, buffer=m.buf)
+                                       for m, sh, dt in zip(shms, shapes, dtypes)]
+        if req:
+            with threadpool_limits(limits=1):
+                oracle.sparse_verify_case(q_raw, meta["q_dtype"], ind, kvl, kp, vp, meta["kv_dtype"],
+                                          bt, meta["k_scale"], meta["v_scale"], meta["top_k"],
+                                          meta["softmax_scale"], meta["max_pages"], requests=req)
+        del q_raw, kp, vp, bt, ind, kvl
+    finally:
+        for m in shms:
+            m.close()
+    return len(req)
+
+
+def cpu_baseline_all_cores(case, n_req, max_procs=16):
+    """The same oracle sample split over one process per core (requests dealt round-robin
+    after sorting by length); inputs shared, worker start-up not timed."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    from workloads import raw_numpy
+    w = case.w
+    req = sorted(range(min(n_req, w.batch)), key=lambda r: -int(case.lengths.kv[r]))
+    procs = max(1, min(max_procs, len(os.sched_getaffinity(0)), len(req)))
+    arrays = [raw_numpy(case.q), raw_numpy(case.k_pool), raw_numpy(case.v_pool),
+              case.block_table.cpu().numpy(), case.qo_indptr.cpu().numpy(),
+              np.asarray(case.lengths.kv)]
+    shms = []
+    try:
+        for a in arrays:
+            m = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            np.ndarray(a.shape, dtype=a.dtype, buffer=m.buf)[...] = a
+            shms.append(m)
+        meta = {"q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "k_scale": case.k_scale,
+                "v_scale": case.v_scale, "top_k": w.top_k, "softmax_scale": case.softmax_scale,
+                "max_pages": w.max_pages()}
+        base = ([m.name for m in shms], [a.shape for a in arrays], [a.dtype for a in arrays], meta)
+        threads_env = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+        saved = {k: os.environ.get(k) for k in threads_env}
+        os.environ.update({k: "1" for k in threads_env})   # inherited by the spawned workers
+        try:
+            with mp.get_context("spawn").Pool(procs, initializer=_oracle_worker_init) as pool:
+                # untimed warm-up: every worker attaches and runs the shortest request once
+                pool.map(_oracle_worker, [base + ([req[-1]],)] * (2 * procs), chunksize=1)
+                t0 = time.perf_counter()
+                pool.map(_oracle_worker, [base + (req[i::procs],) for i in range(procs)],
+                         chunksize=1)
+                dt = time.perf_counter() - t0
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        for m in shms:
+            m.close()
+            m.unlink()
+    toks = int(sum(case.lengths.qo[r] for r in req))
+    return {"value": toks / dt, "unit": "verify tokens/s", "cores": procs, "kind": "oracle",
+            "sample": f"the same {len(req)} requests over {procs} processes, one thread each; "
+                      f"{dt:.2f} s"}
+
+
 def attainable_read_gbs(torch, sdv, dev, gib=4):
     """Best rate of the streaming-read probe over a buffer far larger than the caches."""
     buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
@@ -513,6 +592,7 @@ def main():
     if not args.no_cpu_baseline:
         c_cpu = W.SparseCase(**{**c.__dict__})
         result["cpu_baseline"] = cpu_baseline(c_cpu, args.cpu_sample)
+        result["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(c_cpu, args.cpu_sample)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))
