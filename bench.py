@@ -242,15 +242,35 @@ def _oracle_worker(task):
     return len(req)
 
 
-def cpu_baseline_all_cores(case, n_req, max_procs=16):
-    """The same oracle sample split over one process per core (requests dealt round-robin
-    after sorting by length); inputs shared, worker start-up not timed."""
+def start_oracle_pool(max_procs=16):
+    """The worker processes of the all-cores oracle timing, started before this process
+    touches the GPU (new processes are never started from a GPU-initialised one), with
+    one BLAS/OpenMP thread each."""
     import multiprocessing as mp
+    procs = max(1, min(max_procs, len(os.sched_getaffinity(0))))
+    threads_env = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in threads_env}
+    os.environ.update({k: "1" for k in threads_env})   # inherited by the spawned workers
+    try:
+        pool = mp.get_context("spawn").Pool(procs, initializer=_oracle_worker_init)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return pool, procs
+
+
+def cpu_baseline_all_cores(case, n_req, pool, procs):
+    """The same oracle sample split over the pool's processes, one per core (requests
+    dealt round-robin after sorting by length); inputs shared; the second of two identical
+    passes is timed (the first one pays the workers' first-use costs)."""
     from multiprocessing import shared_memory
     from workloads import raw_numpy
     w = case.w
     req = sorted(range(min(n_req, w.batch)), key=lambda r: -int(case.lengths.kv[r]))
-    procs = max(1, min(max_procs, len(os.sched_getaffinity(0)), len(req)))
+    procs = max(1, min(procs, len(req)))
     arrays = [raw_numpy(case.q), raw_numpy(case.k_pool), raw_numpy(case.v_pool),
               case.block_table.cpu().numpy(), case.qo_indptr.cpu().numpy(),
               np.asarray(case.lengths.kv)]
@@ -264,23 +284,11 @@ def cpu_baseline_all_cores(case, n_req, max_procs=16):
                 "v_scale": case.v_scale, "top_k": w.top_k, "softmax_scale": case.softmax_scale,
                 "max_pages": w.max_pages()}
         base = ([m.name for m in shms], [a.shape for a in arrays], [a.dtype for a in arrays], meta)
-        threads_env = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
-        saved = {k: os.environ.get(k) for k in threads_env}
-        os.environ.update({k: "1" for k in threads_env})   # inherited by the spawned workers
-        try:
-            with mp.get_context("spawn").Pool(procs, initializer=_oracle_worker_init) as pool:
-                # untimed warm-up: every worker attaches and runs the shortest request once
-                pool.map(_oracle_worker, [base + ([req[-1]],)] * (2 * procs), chunksize=1)
-                t0 = time.perf_counter()
-                pool.map(_oracle_worker, [base + (req[i::procs],) for i in range(procs)],
-                         chunksize=1)
-                dt = time.perf_counter() - t0
-        finally:
-            for k, v in saved.items():
-                if v is None:
-                    os.environ.pop(k, None)
-                else:
-                    os.environ[k] = v
+        tasks = [base + (req[i::procs],) for i in range(procs)]
+        pool.map(_oracle_worker, tasks, chunksize=1)   # untimed: workers' first pass
+        t0 = time.perf_counter()
+        pool.map(_oracle_worker, tasks, chunksize=1)
+        dt = time.perf_counter() - t0
     finally:
         for m in shms:
             m.close()
@@ -328,6 +336,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verify path "
               "here is a single-GPU kernel library with no cross-GPU step.", file=sys.stderr)
         sys.exit(2)
+    oracle_pool = None
+    if not args.no_cpu_baseline and not args.calibrate_copy:
+        oracle_pool = start_oracle_pool()
     import torch
 
     import speculative_decode_verify_p128_amd as sdv
@@ -592,7 +603,13 @@ def main():
     if not args.no_cpu_baseline:
         c_cpu = W.SparseCase(**{**c.__dict__})
         result["cpu_baseline"] = cpu_baseline(c_cpu, args.cpu_sample)
-        result["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(c_cpu, args.cpu_sample)
+        pool, procs = oracle_pool
+        try:
+            result["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(c_cpu, args.cpu_sample,
+                                                                         pool, procs)
+        finally:
+            pool.close()
+            pool.join()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))
