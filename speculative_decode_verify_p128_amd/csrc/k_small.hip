@@ -42,44 +42,84 @@ hipError_t launch_subpage_offsets(const int32_t* block_table, int32_t B, int32_t
   return hipGetLastError();
 }
 
-// Split-KV combine: one wave per (query row, query head); each lane owns head_dim / 64
-// channels.  LSE = log sum_s exp(lse_s), out = sum_s exp(lse_s - LSE) * O_s; partials
-// with lse = -inf (no keys) are skipped and never read.
+// Split-KV combine: LPU = head_dim / 8 lanes per (query row, query head), each lane
+// eight channels.  LSE = log sum_s exp(lse_s), out = sum_s exp(lse_s - LSE) * O_s, in
+// ascending s; partials with lse = -inf (no keys) are skipped and never read.  A lane
+// loads every split's lse at once and then every split's partial, so the call costs two
+// memory round trips, not two per split (up to kCombineUnroll splits; more loop).
+constexpr int kCombineUnroll = 8;
+
 template <int D>
 __global__ void __launch_bounds__(256) sdv_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int32_t num_splits,
     int32_t rows_cap, const int32_t* __restrict__ row_begin_dev,
     const int32_t* __restrict__ row_end_dev, int32_t num_heads, void* __restrict__ out,
     int32_t out_dt, float* __restrict__ lse_out) {
-  constexpr int PER = D / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  constexpr int LPU = D / 8;
+  const int sub = threadIdx.x % LPU;
+  const int64_t unit = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / LPU;
   const int64_t units = static_cast<int64_t>(rows_cap) * num_heads;
   if (unit >= units) return;
   const int64_t row = unit / num_heads;
   if (row_begin_dev && (row < *row_begin_dev || row >= *row_end_dev)) return;
   const int64_t plane = units;   // rows_cap * num_heads
-  float m = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) m = fmaxf(m, part_lse[s * plane + unit]);
-  float acc[PER];
+  const int S = num_splits;
+  float acc[8];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float tot = 0.f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < num_splits; ++s) {
-      const float l = part_lse[s * plane + unit];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - m);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float m = -INFINITY, tot = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kCombineUnroll) {
+    const int n = min(kCombineUnroll, S - s0);
+    float l[kCombineUnroll];
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k)
+      l[k] = k < n ? part_lse[(s0 + k) * plane + unit] : -INFINITY;
+    float mc = m;
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) mc = fmaxf(mc, l[k]);
+    if (mc == -INFINITY) continue;
+    if (mc > m) {
+      // rescale what earlier chunks of splits accumulated to the new reference
+      const float f = m == -INFINITY ? 0.f : __expf(m - mc);
+      tot *= f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= f;
+      m = mc;
+    }
+    float4 x[kCombineUnroll][2];
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      if (l[k] != -INFINITY) {
+        const float4* src = reinterpret_cast<const float4*>(part_o + ((s0 + k) * plane + unit) * D + sub * 8);
+        x[k][0] = src[0];
+        x[k][1] = src[1];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      if (l[k] == -INFINITY) continue;
+      const float w = __expf(l[k] - m);
       tot += w;
-      const float* src = part_o + (s * plane + unit) * D;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * src[lane * PER + e];
+      acc[0] += w * x[k][0].x; acc[1] += w * x[k][0].y; acc[2] += w * x[k][0].z; acc[3] += w * x[k][0].w;
+      acc[4] += w * x[k][1].x; acc[5] += w * x[k][1].y; acc[6] += w * x[k][1].z; acc[7] += w * x[k][1].w;
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const int64_t idx = unit * D + sub * 8;
+  if (out_dt == SDV_BF16) {
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(out) + idx;
+    uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) store_out(out, unit * D + lane * PER + e, acc[e] * inv, out_dt);
-  if (lse_out && lane == 0) lse_out[unit] = (m == -INFINITY) ? -INFINITY : m + __logf(tot);
+    for (int k = 0; k < 4; ++k)
+      w[k] = static_cast<uint32_t>(f32_to_bf16_rne(acc[2 * k] * inv)) |
+             (static_cast<uint32_t>(f32_to_bf16_rne(acc[2 * k + 1] * inv)) << 16);
+    *reinterpret_cast<uint4*>(o16) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    float4* o32 = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx);
+    o32[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    o32[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  }
+  if (lse_out && sub == 0) lse_out[unit] = (m == -INFINITY) ? -INFINITY : m + __logf(tot);
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t num_splits,
@@ -88,8 +128,8 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t nu
                           void* out, int32_t out_dt, float* lse_out, hipStream_t s) {
   const int64_t units = static_cast<int64_t>(rows_cap) * num_heads;
   if (units == 0) return hipSuccess;
-  const int waves_per_block = 4;
-  const int64_t blocks = (units + waves_per_block - 1) / waves_per_block;
+  const int lpu = head_dim / 8;
+  const int64_t blocks = (units * lpu + 255) / 256;
   if (head_dim == 128)
     hipLaunchKernelGGL(sdv_combine_kernel<128>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
                        part_o, part_lse, num_splits, rows_cap, row_begin_dev, row_end_dev, num_heads, out,
