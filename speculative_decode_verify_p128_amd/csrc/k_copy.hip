@@ -11,6 +11,7 @@ namespace sdv {
 namespace {
 
 typedef unsigned int u32x4_copy __attribute__((ext_vector_type(4)));
+constexpr int kCopyUnroll = 4;
 
 __global__ void __launch_bounds__(256) sdv_copy_desc_kernel(
     const char* __restrict__ src, int64_t src_bytes, char* __restrict__ dst, int64_t dst_bytes,
@@ -27,8 +28,21 @@ __global__ void __launch_bounds__(256) sdv_copy_desc_kernel(
     const u32x4_copy* s = reinterpret_cast<const u32x4_copy*>(src + e.src_offset);
     u32x4_copy* d = reinterpret_cast<u32x4_copy*>(dst + e.dst_offset);
     const int64_t n16 = e.bytes / 16;
-    for (int64_t k = threadIdx.x; k < n16; k += blockDim.x)
-      d[k] = __builtin_nontemporal_load(s + k);
+    // kCopyUnroll loads in flight per thread before the stores (a 16 KiB descriptor in
+    // one round)
+    for (int64_t k0 = threadIdx.x; k0 < n16; k0 += kCopyUnroll * blockDim.x) {
+      u32x4_copy v[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t k = k0 + static_cast<int64_t>(u) * blockDim.x;
+        if (k < n16) v[u] = __builtin_nontemporal_load(s + k);
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t k = k0 + static_cast<int64_t>(u) * blockDim.x;
+        if (k < n16) d[k] = v[u];
+      }
+    }
   }
 }
 
