@@ -5,14 +5,15 @@
 // graphs compatibility", MSA verify commit).
 //
 //   1. sdv_argmax_kernel: one 1024-thread workgroup per verify row streams its vocab
-//      logits with 16-byte non-temporal loads, 16 in flight per thread (HBM-bound),
-//      and keeps, per lane, the largest value and its lowest index (NaN never
-//      selected); a wave then a workgroup reduction gives the target's greedy token
-//      after that row.  Lanes visit indices in increasing order and every reduction
-//      step prefers the lower index on equal values, so ties resolve to the lowest.
+//      logits with 16-byte non-temporal loads, 16 in flight per thread (HBM-bound):
+//      the row's largest non-NaN value, then the lowest index holding it, from the same
+//      registers — the target's greedy token after that row (ties to the lowest index,
+//      NaN never selected).
 //   2. sdv_accept_kernel: one thread per request takes the longest prefix of drafts
 //      equal to the targets of the rows before them, emits them and the bonus target,
 //      and writes the corrected kv_len (kv_len - qo_len + 1 + accepted).
+#include <climits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -21,80 +22,95 @@ namespace {
 
 typedef unsigned int u32x4_acc __attribute__((ext_vector_type(4)));
 
-// (v, i) beats (bv, bi): larger value, or equal value at a lower index; i < 0 = none.
-__device__ __forceinline__ bool beats(float v, int i, float bv, int bi) {
-  return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
-}
-
 constexpr int kArgmaxThreads = 1024;
 constexpr int kArgmaxUnroll = 16;     // 16-byte loads in flight per thread
 
+// Decoded logits of one 16-byte load.
+template <int DT>
+__device__ __forceinline__ void decode16(const u32x4_acc& w, float (&x)[16 / (DT == SDV_F32 ? 4 : 2)]) {
+  if constexpr (DT == SDV_F32) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(w[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+}
+
+// Two passes over the row, the loaded logits kept in registers between them: the row's
+// largest value M (fmaxf skips NaN; a row of NaN leaves M = -inf), reduced over the
+// workgroup, then the lowest index whose logit equals M (none when the row holds only
+// NaN).  This is exactly the argmax with ties to the lowest index and NaN never chosen.
 template <int DT>
 __global__ void __launch_bounds__(kArgmaxThreads) sdv_argmax_kernel(
     const char* __restrict__ logits, int32_t vocab, const int32_t* __restrict__ qo_indptr,
     int32_t B, int32_t* __restrict__ targets) {
   constexpr int EB = DT == SDV_F32 ? 4 : 2;
   constexpr int PER = 16 / EB;                 // elements per 16-byte load
+  constexpr int NW = kArgmaxThreads / kWave;
+  __shared__ float s_max[NW];
+  __shared__ int s_idx[NW];
   const int row = blockIdx.x;
   if (row >= qo_indptr[B]) return;
   const u32x4_acc* base = reinterpret_cast<const u32x4_acc*>(logits + static_cast<int64_t>(row) * vocab * EB);
   const int nvec = vocab / PER;
-  float bv = 0.f;
-  int bi = -1;
-  auto consider = [&](const u32x4_acc& w, int vec) {
-    float x[PER];
-    if constexpr (DT == SDV_F32) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(w[k]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-      if (!__builtin_isnan(x[k]) && beats(x[k], vec * PER + k, bv, bi)) {
-        bv = x[k];
-        bi = vec * PER + k;
-      }
-  };
-  constexpr int STEP = kArgmaxThreads * kArgmaxUnroll;
-  int v0 = threadIdx.x;
-  for (; v0 + (kArgmaxUnroll - 1) * kArgmaxThreads < nvec; v0 += STEP) {
-    u32x4_acc w[kArgmaxUnroll];
-#pragma unroll
-    for (int u = 0; u < kArgmaxUnroll; ++u)
-      w[u] = __builtin_nontemporal_load(base + v0 + u * kArgmaxThreads);
-#pragma unroll
-    for (int u = 0; u < kArgmaxUnroll; ++u) consider(w[u], v0 + u * kArgmaxThreads);
-  }
-  for (; v0 < nvec; v0 += kArgmaxThreads) consider(__builtin_nontemporal_load(base + v0), v0);
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off, kWave);
-    const int oi = __shfl_xor(bi, off, kWave);
-    if (beats(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-  __shared__ float sv[kArgmaxThreads / kWave];
-  __shared__ int si[kArgmaxThreads / kWave];
   const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-    sv[wave] = bv;
-    si[wave] = bi;
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = -INFINITY;
+  int best = INT_MAX;
+  // rows up to kArgmaxThreads * kArgmaxUnroll vectors: one register batch, both passes
+  // from registers; longer rows: the batches of pass 2 are loaded again
+  constexpr int STEP = kArgmaxThreads * kArgmaxUnroll;
+  u32x4_acc w[kArgmaxUnroll];
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int v0 = threadIdx.x; v0 - static_cast<int>(threadIdx.x) < nvec; v0 += STEP) {
+      if (pass == 0 || nvec > STEP) {
+#pragma unroll
+        for (int u = 0; u < kArgmaxUnroll; ++u) {
+          const int v = v0 + u * kArgmaxThreads;
+          w[u] = v < nvec ? __builtin_nontemporal_load(base + v) : u32x4_acc{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kArgmaxUnroll; ++u) {
+        const int v = v0 + u * kArgmaxThreads;
+        if (v >= nvec) continue;
+        float x[PER];
+        decode16<DT>(w[u], x);
+        if (pass == 0) {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) m = fmaxf(m, x[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < PER; ++k)
+            if (x[k] == m && v * PER + k < best) best = v * PER + k;
+        }
+      }
+    }
+    if (pass == 0) {
+      // workgroup maximum
+      m = wave_max(m);
+      if (lane == 0) s_max[wave] = m;
+      __syncthreads();
+      m = s_max[0];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) m = fmaxf(m, s_max[k]);
+    }
   }
+  // workgroup minimum of the indices holding the maximum (an all-NaN row keeps m = -inf,
+  // which no NaN equals, so best stays INT_MAX)
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) best = min(best, __shfl_xor(best, off, kWave));
+  if (lane == 0) s_idx[wave] = best;
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w)
-      if (beats(sv[w], si[w], bv, bi)) {
-        bv = sv[w];
-        bi = si[w];
-      }
-    targets[row] = bi;
+    int b = s_idx[0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) b = min(b, s_idx[k]);
+    targets[row] = b == INT_MAX ? -1 : b;
   }
 }
 
