@@ -1,10 +1,11 @@
 """Benchmark of the verify path on one MI355X.
 
 A step is one pass of the block-sparse target-layer verify path over one batch:
-proxy page scores -> ladder top-k -> sparse verify attention (+ split-KV combine),
-on the sparse bf16 workload (batch 64, qo_len 4, 16/4 heads, head_dim 128, kv_len
-uniform in [4096, 32768], top-k 16).  Inputs are generated on the GPU from a seed and
-are resident in HBM before timing starts.  The dense draft-layer path (P32 view
+proxy page scores, then the ladder top-k and the sparse verify attention in one launch
+(+ split-KV combine), on the sparse bf16 workload (batch 64, qo_len 4, 16/4 heads,
+head_dim 128, kv_len uniform in [4096, 32768], top-k 16).  The same path as three
+launches (standalone top-k) is timed after it and reported under "unfused".  Inputs are
+generated on the GPU from a seed and are resident in HBM before timing starts.  The dense draft-layer path (P32 view
 offsets + dense verify attention, batch 32, qo_len 4, 64/4 heads, kv_len uniform in
 [1024, 8192]) is timed in the same run and reported under "dense".
 
@@ -52,6 +53,9 @@ def parse():
                    help="time the headline step as one HIP graph replay instead of eager launches")
     p.add_argument("--warm", action="store_true",
                    help="no cache-evicting fill between steps (warm-cache numbers)")
+    p.add_argument("--no-unfused", action="store_true",
+                   help="skip timing the three-launch step (proxy, standalone top-k, sparse "
+                        "attention over its indices) reported under 'unfused'")
     return p.parse_args()
 
 
@@ -75,6 +79,8 @@ def sparse_algorithmic_bytes(case, idx_np):
         b = kv[r] - qo[r] + np.arange(qo[r]) + 1
         nv_sum += int((-(-b // 128)).sum())
     topk = nv_sum * Hkv * 4 + rows * Hkv * w.top_k * 4
+    scores_read = nv_sum * Hkv * 4
+    index_bytes = rows * Hkv * w.top_k * 4
     # sparse: valid K and V rows of the distinct pages any token of (r, h) selected
     kv_rows = 0
     for r in range(len(kv)):
@@ -92,7 +98,9 @@ def sparse_algorithmic_bytes(case, idx_np):
             for h in range(Hkv):
                 pages = sel[t, h][sel[t, h] >= 0]
                 rowexp += int(np.minimum(128, kv[r] - 128 * pages).sum())
-    return {"proxy": proxy, "topk": topk, "sparse": sparse,
+    # in-kernel selection: the valid scores read in place of the indices
+    select = sparse - index_bytes + scores_read
+    return {"proxy": proxy, "topk": topk, "sparse": sparse, "select": select,
             "sparse_row_expanded_kv": rowexp * d * e * 2}
 
 
@@ -113,6 +121,8 @@ KERNEL_SOURCES = {
     "ladder_topk_pages": ("k_topk.hip", "device.h"),
     "verify_attention_sparse": ("k_attn_waves.hip", "mfma_attn.h", "sparse_union.h", "k_small.hip",
                                 "device.h", "internal.h", "sdv_api.cpp"),
+    "verify_attention_sparse_select": ("k_attn_waves.hip", "mfma_attn.h", "sparse_union.h",
+                                       "k_small.hip", "device.h", "internal.h", "sdv_api.cpp"),
     "verify_attention_dense": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
                                "internal.h", "sdv_api.cpp"),
     "verify_attention_paged": ("k_attn_waves.hip", "mfma_attn.h", "k_small.hip", "device.h",
@@ -418,28 +428,53 @@ def main():
                                     max_qo_len=mq, softmax_scale=c.softmax_scale,
                                     num_splits=splits, workspace=ws, out=out)
 
-    fns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
-           ("verify_attention_sparse", k_sparse)]
+    def k_select():
+        sdv.verify_attention_sparse_select(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, scores,
+                                           max_qo_len=mq, top_k=w.top_k,
+                                           softmax_scale=c.softmax_scale, num_splits=splits,
+                                           workspace=ws, out=out)
+
+    fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
     eager_ms, per, wall = time_steps(fns, args.steps, args.warmup, torch, flush)
     ms = eager_ms
     if args.graph:
         # the step as one HIP graph (the path is capture-safe: no allocation, no host
         # synchronisation, lengths read on the device); its outputs must equal the eager ones
-        ref_out, ref_idx = out.clone(), idx.clone()
+        ref_out = out.clone()
         ms = time_graph(fns, args.steps, args.warmup, torch, flush)
-        if not (torch.equal(out.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(idx, ref_idx)):
+        if not torch.equal(out.view(torch.int16), ref_out.view(torch.int16)):
             raise RuntimeError("graph replay of the sparse path differs from its eager run")
-        del ref_out, ref_idx
+        del ref_out
+    # the selection the fused launch made (written out here, after timing) sizes the
+    # algorithmic bytes; the two-launch path must reach the same output
+    fused_out = out.clone()
+    k_proxy()
+    k_topk()
+    k_sparse()
+    torch.cuda.synchronize()
+    if not torch.equal(out.view(torch.int16), fused_out.view(torch.int16)):
+        raise RuntimeError("in-kernel selection and standalone top-k give different outputs")
+    del fused_out
     tokens = c.lengths.total_q
     idx_np = idx.cpu().numpy()
     ab = sparse_algorithmic_bytes(c, idx_np)
-    path_bytes = ab["proxy"] + ab["topk"] + ab["sparse"]
+    path_bytes = ab["proxy"] + ab["select"]
     kern = {}
-    for name, key in (("proxy_page_scores", "proxy"), ("ladder_topk_pages", "topk"),
-                      ("verify_attention_sparse", "sparse")):
+    for name, key in (("proxy_page_scores", "proxy"), ("verify_attention_sparse_select", "select")):
         gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
         kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
                       "frac_of_peak": gbs / HBM_PEAK_GBS}
+    unfused = None
+    if not args.no_unfused:
+        ufns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
+                ("verify_attention_sparse", k_sparse)]
+        u_ms, u_per, _ = time_steps(ufns, args.steps, args.warmup, torch, flush)
+        unfused = {"ms_per_step": u_ms, "kernels": {}}
+        for name, key in (("proxy_page_scores", "proxy"), ("ladder_topk_pages", "topk"),
+                          ("verify_attention_sparse", "sparse")):
+            gbs = ab[key] / (u_per[name]["avg_us"] * 1e-6) / 1e9
+            unfused["kernels"][name] = {**u_per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
+                                        "frac_of_peak": gbs / HBM_PEAK_GBS}
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
     traffic = load_traffic(dom, w.name, source_hash(*KERNEL_SOURCES[dom]))
     path_gbs = path_bytes / (ms * 1e-3) / 1e9
@@ -471,10 +506,11 @@ def main():
                      "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
                      "traffic": traffic},
         "kernels": kern,
-        "launch": ("one HIP graph replay per step (proxy, top-k, attention); the per-kernel "
+        "launch": ("one HIP graph replay per step (proxy, selection + attention); the per-kernel "
                    "times in kernels come from an eager pass with events around every launch"
                    if args.graph else "eager: one launch per kernel"),
         "eager_ms_per_step": eager_ms,
+        "unfused": unfused,
         "sparse_row_expanded_kv_bytes": ab["sparse_row_expanded_kv"],
         "wall_s_timed": wall,
         "cache": ("warm: consecutive steps, no eviction" if args.warm else

@@ -272,6 +272,31 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
                                 int32_t* dev_err, hipStream_t stream);
 
 /*
+ * verify_attention_sparse_select — ladder_topk_pages and verify_attention_sparse in one
+ * launch: each attention workgroup selects its (request, KV head)'s pages from scores
+ * itself (one wave per verify token, the same selection as ladder_topk_pages: score
+ * descending, page ascending on ties, among each token's own n_valid pages) and attends
+ * them.  (Sources: PR #3 MSA verify commit — per-token ladder top-k; the proxy pass and
+ * the selection feed the sparse attention of the same step.)
+ *
+ * scores    device float [B*max_qo_len][num_kv_heads][max_pages] (proxy_page_scores).
+ * topk_idx  device int32 [B*max_qo_len][num_kv_heads][top_k] OUT, nullable: the
+ *           selection as ladder_topk_pages writes it (required for kernel families 1
+ *           and 2, which run the selection as its own launch first).
+ * topk_cnt  device int32 [B*max_qo_len][num_kv_heads] OUT, nullable.
+ * Other arguments as in verify_attention_sparse; max_pages <= 1024.
+ */
+int32_t verify_attention_sparse_select(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                       const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                       int32_t num_q_heads, const sdv_paged_kv* kv,
+                                       const int32_t* block_table, int32_t max_pages,
+                                       int32_t bt_stride, const float* scores, int32_t top_k,
+                                       int32_t* topk_idx, int32_t* topk_cnt,
+                                       float softmax_scale, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* out, int32_t out_dt,
+                                       int32_t* dev_err, hipStream_t stream);
+
+/*
  * verify_attention_paged — dense GQA verify attention over ordinary head-major P128
  * pages, for the target model's dense layers: token t, query head hq of KV head h
  * attends every position j < bound(r,t) of its request (the ladder mask; at qo_len = 1

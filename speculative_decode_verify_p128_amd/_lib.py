@@ -72,6 +72,9 @@ SIGNATURES = {
     "ladder_topk_pages": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "verify_attention_sparse": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I,
                                      _P, _I, _F, _I, _P, _S, _P, _I, _P, _P]),
+    "verify_attention_sparse_select": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P,
+                                            _I, _I, _P, _I, _P, _P, _F, _I, _P, _S, _P, _I, _P,
+                                            _P]),
     "verify_attention_paged": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I,
                                     _F, _I, _P, _S, _P, _I, _P, _P]),
     "stage_verify_kv_paged": (_I, [_P, _P, _I, _P, _P, _I, _I, C.POINTER(PagedKV), _P, _I, _I,

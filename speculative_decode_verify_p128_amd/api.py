@@ -209,6 +209,40 @@ def verify_attention_sparse(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: to
     return out
 
 
+def verify_attention_sparse_select(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
+                                   kv: PagedKV, block_table: torch.Tensor, scores: torch.Tensor, *,
+                                   max_qo_len: int, top_k: int, softmax_scale: float,
+                                   num_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                                   out: Optional[torch.Tensor] = None, out_dtype=None,
+                                   topk_idx: Optional[torch.Tensor] = None,
+                                   topk_cnt: Optional[torch.Tensor] = None,
+                                   dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Ladder top-k of `scores` and sparse verify attention in one launch; the selection
+    is written to `topk_idx` / `topk_cnt` when given."""
+    _need(q, "q")
+    _need(scores, "scores", torch.float32)
+    if scores.shape[-1] != block_table.shape[1]:
+        raise ValueError("scores must have one entry per block-table page (proxy_page_scores)")
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", torch.int32)
+    if topk_cnt is not None:
+        _need(topk_cnt, "topk_cnt", torch.int32)
+    B = kv_len.numel()
+    rows_cap = B * max_qo_len
+    out = _out(out, q, rows_cap, out_dtype)
+    if workspace is None and num_splits > 1:
+        workspace = alloc_workspace(rows_cap, q.shape[1], q.shape[2], num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ckv = kv.c()
+    L.check(L.load().verify_attention_sparse_select(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(ckv), _ptr(block_table), block_table.shape[1], block_table.stride(0),
+        _ptr(scores), top_k, _ptr(topk_idx), _ptr(topk_cnt), softmax_scale, num_splits,
+        _ptr(workspace), ws_bytes, _ptr(out), dtype_code(out.dtype), _ptr(dev_err),
+        _stream(q.device)))
+    return out
+
+
 def verify_attention_paged(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
                            kv: PagedKV, block_table: torch.Tensor, *, max_qo_len: int,
                            softmax_scale: float, num_splits: int = 1,

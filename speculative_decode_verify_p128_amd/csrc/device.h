@@ -100,6 +100,83 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- ladder top-k of one verify token, by one wave ----
+// 64-bit keys (order-preserving score bits << 32 | ~page): the unsigned maximum picks the
+// best score and, among equal scores, the lowest page.
+
+// Maximum of v over the wave, the same in every lane: rotate-and-max inside each
+// 16-lane row (DPP row_ror, no LDS traffic), then the four row maxima read into scalar
+// registers.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  constexpr int kRowRor = 0x120;   // DPP row_ror:n, n = 1 .. 15
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 2, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 4, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 8, 0xF, 0xF, false)));
+  const uint32_t a = max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)),
+                         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)));
+  const uint32_t b = max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)),
+                         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48)));
+  return max(a, b);
+}
+
+// One wave selects the k_eff = min(top_k, n) best of the n scores srow[0 .. n-1] (score
+// descending, page ascending on ties) in rank order, and every lane calls emit(k, page)
+// with the same values.  Lane l holds pages l + 64 i, i < ITEMS (1 <= n <= 64 * ITEMS),
+// and caches its largest key.  Each round takes the wave maximum of the cached keys'
+// high (score) words; the lanes holding it are a ballot, and only when several lanes tie
+// on the score does a second maximum over their low (page) words pick the lowest page.
+// The owning lane retires its key and refreshes its cache.  Returns k_eff.
+template <int ITEMS, class Emit>
+__device__ __forceinline__ int wave_ladder_topk(const float* srow, int n, int top_k, int lane,
+                                                Emit&& emit) {
+  uint64_t keys[ITEMS];
+  uint64_t best = 0;
+  // Every lane loads all its items from an index clamped into [0, n) with no branch, so
+  // the loads are in flight together; the keys of pages at or beyond n are zeroed after.
+  float sv[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) sv[i] = srow[min(lane + kWave * i, n - 1)];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = lane + kWave * i;
+    keys[i] = p < n ? (static_cast<uint64_t>(ordered_key(sv[i])) << 32) |
+                          static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(p))
+                    : 0ull;
+    best = keys[i] > best ? keys[i] : best;
+  }
+  const int k_eff = top_k < n ? top_k : n;
+  for (int k = 0; k < k_eff; ++k) {
+    const uint32_t hi = static_cast<uint32_t>(best >> 32);
+    const uint32_t lo = static_cast<uint32_t>(best);
+    const uint32_t mhi = wave_max_u32(hi);
+    const bool top = hi == mhi;
+    const uint64_t tops = __builtin_amdgcn_ballot_w64(top);
+    uint32_t mlo;
+    int owner;
+    if (__builtin_popcountll(tops) == 1) {
+      owner = __builtin_ctzll(tops);
+      mlo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), owner));
+    } else {
+      // Equal scores in several lanes (an empty lane's key is 0, below any real key's
+      // low word): the largest low word is the lowest page; keys are unique.
+      mlo = wave_max_u32(top ? lo : 0u);
+      owner = __builtin_ctzll(__builtin_amdgcn_ballot_w64(top && lo == mlo));
+    }
+    if (lane == owner) {
+      uint64_t nb = 0;
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        keys[i] = keys[i] == best ? 0ull : keys[i];
+        nb = keys[i] > nb ? keys[i] : nb;
+      }
+      best = nb;
+    }
+    emit(k, static_cast<int>(0xffffffffu - mlo));
+  }
+  return k_eff;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

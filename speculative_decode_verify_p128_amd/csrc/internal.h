@@ -27,7 +27,15 @@ struct SparseSource {           // head-major P128 pages + selected page lists
   int32_t max_pages;
   const int32_t* topk_idx;      // [rows][Hkv][top_k]
   int32_t top_k;
+  // Selection inside the attention kernels instead of topk_idx (when scores != null):
+  // the ladder top-k of scores [rows][Hkv][max_pages], written to topk_out / cnt_out
+  // (each nullable) by the workgroups of split 0.
+  const float* scores;
+  int32_t* topk_out;
+  int32_t* cnt_out;
 };
+// Pages per token the in-kernel selection handles (64 lanes x 16 keys).
+constexpr int kFusedTopkMaxPages = 1024;
 
 struct AttnArgs {
   const void* q;

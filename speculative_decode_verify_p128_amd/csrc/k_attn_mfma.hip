@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(256) sdv_attn_mfma_kernel(AttnArgs a, DenseSou
   // This split's blocks; wave w takes blocks w, w + 4, ...
   int nblk, base;
   if constexpr (SPARSE) {
-    const int n_union = build_union(ul, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
+    const int n_union = build_union<false>(ul, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
     const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
     base = split * chunk;
     nblk = 4 * max(0, min(n_union, base + chunk) - base);

@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
   int blk_lo, blk_hi;     // dense: sub-pages; sparse: union entries (each 4 blocks)
   int n_union = 0;
   if constexpr (SPARSE) {
-    n_union = build_union(sm.u, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
+    n_union = build_union<false>(sm.u, ss, r, h, Hkv, row0, qo, kv, a.dev_err);
     const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
     blk_lo = split * chunk;
     blk_hi = min(n_union, blk_lo + chunk);

@@ -458,7 +458,7 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
 template <int RT, int D, int KDT, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sdv_attn_waves_persist_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
-  static_assert(MODE != kSrcSparse, "dense sources only");
+  static_assert(!is_sparse(MODE), "dense sources only");
   __shared__ WavesLds<RT, D, KDT, MODE> sh;
   __shared__ PersistLds pl;
   persistent_walk<MODE>(pl, a, ds, ss,
@@ -528,6 +528,7 @@ hipError_t launch_attn_dense_waves(const AttnArgs& a, const DenseSource& src, hi
 }
 
 hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
+  if (src.scores) return dispatch<kSrcSparseSelect, false>(a, DenseSource{}, src, 0, s);
   return dispatch<kSrcSparse, false>(a, DenseSource{}, src, 0, s);
 }
 

@@ -9,42 +9,15 @@
 // One wave per (token row, KV head).  Lane l holds pages l, l + 64, ... of the token's
 // n_valid pages as 64-bit keys (order-preserving score bits << 32 | ~page), so one
 // unsigned maximum picks the best score and, among equal scores, the lowest page.
-// Each round reduces the lanes' cached maxima across the wave — a rotate-and-max inside
-// each 16-lane row (DPP row rotations, no LDS traffic), then the four row maxima read
-// into scalar registers — and the owning lane retires the key and refreshes its cache.
+// Each round takes the wave maximum of the lanes' cached score words (DPP row rotations,
+// then the four row maxima in scalar registers), settles equal scores on the page word
+// only when a ballot shows a tie, and the owning lane retires the key and refreshes its
+// cache (wave_ladder_topk, shared with the selection inside the sparse attention
+// kernels).
 #include "device.h"
 #include "internal.h"
 
 namespace sdv {
-
-// Lane l's 64-bit value of lane (l - N) mod 16 of its row: DPP row_ror:N on each half.
-template <int N>
-__device__ __forceinline__ uint64_t row_rotate(uint64_t v) {
-  constexpr int kRowRor = 0x120;   // DPP row_ror:n, n = 1 .. 15
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(
-      static_cast<int>(static_cast<uint32_t>(v)), kRowRor + N, 0xF, 0xF, false));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(
-      static_cast<int>(static_cast<uint32_t>(v >> 32)), kRowRor + N, 0xF, 0xF, false));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t lane_value(uint64_t v, int lane) {
-  const int lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
-  const int hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane);
-  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
-}
-
-// Maximum of v over the wave, the same in every lane.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-  v = umax64(v, row_rotate<1>(v));
-  v = umax64(v, row_rotate<2>(v));
-  v = umax64(v, row_rotate<4>(v));
-  v = umax64(v, row_rotate<8>(v));     // every lane of a row holds the row's maximum
-  return umax64(umax64(lane_value(v, 0), lane_value(v, 16)),
-                umax64(lane_value(v, 32), lane_value(v, 48)));
-}
 
 template <int ITEMS>
 __global__ void __launch_bounds__(64) sdv_topk_kernel(
@@ -73,31 +46,10 @@ __global__ void __launch_bounds__(64) sdv_topk_kernel(
   const int64_t row = row0 + t;
   const float* srow = scores + (row * Hkv + h) * max_pages;
 
-  uint64_t keys[ITEMS];
-  uint64_t best = 0;
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int p = lane + kWave * i;
-    keys[i] = p < n ? (static_cast<uint64_t>(ordered_key(srow[p])) << 32) |
-                          static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(p))
-                    : 0ull;
-    best = keys[i] > best ? keys[i] : best;
-  }
-  const int k_eff = top_k < n ? top_k : n;
   int32_t* out = topk_idx + (row * Hkv + h) * top_k;
-  for (int k = 0; k < k_eff; ++k) {
-    const uint64_t m = wave_max64(best);
-    if (best == m) {                   // keys are unique: exactly one lane owns m
-      uint64_t nb = 0;
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        keys[i] = keys[i] == m ? 0ull : keys[i];
-        nb = keys[i] > nb ? keys[i] : nb;
-      }
-      best = nb;
-    }
-    if (lane == 0) out[k] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(m));
-  }
+  const int k_eff = wave_ladder_topk<ITEMS>(srow, n, top_k, lane, [&](int k, int page) {
+    if (lane == 0) out[k] = page;
+  });
   for (int k = k_eff + lane; k < top_k; k += kWave) out[k] = -1;
   if (topk_cnt && lane == 0) topk_cnt[row * Hkv + h] = k_eff;
 }

@@ -268,7 +268,12 @@ enum SourceMode : int {
   kSrcView = 0,     // dense, through the P32 sub-page view of the draft layer
   kSrcSparse = 1,   // sparse: the union of the P128 pages the tokens selected
   kSrcPaged = 2,    // dense over ordinary head-major P128 pages and a block table
+  kSrcSparseSelect = 3,  // sparse, each token's pages chosen in the kernel from page scores
 };
+
+__host__ __device__ constexpr bool is_sparse(int mode) {
+  return mode == kSrcSparse || mode == kSrcSparseSelect;
+}
 
 // Per dense split: for kSrcView the P32 page index of each block's K sub-page (the view
 // puts V one P128 page, four P32 pages, after K); for kSrcPaged the physical P128 page
@@ -284,7 +289,7 @@ struct DenseMeta {
 template <int MODE, int D, int KDT>
 struct BlockList {
   using Gm = Geo<D, KDT>;
-  using Lds = typename std::conditional<MODE == kSrcSparse, UnionLds, DenseMeta>::type;
+  using Lds = typename std::conditional<is_sparse(MODE), UnionLds, DenseMeta>::type;
   struct Raw {
     int a, b, c;
   };
@@ -296,8 +301,9 @@ struct BlockList {
   __device__ __forceinline__ void stage(Lds& ul, int* chunk_lds, const AttnArgs& a,
                                         const DenseSource& ds, const SparseSource& ss, int r,
                                         int h, int split, int row0, int qo, int kv) {
-    if constexpr (MODE == kSrcSparse) {
-      const int n_union = build_union(ul, ss, r, h, a.num_kv_heads, row0, qo, kv, a.dev_err);
+    if constexpr (is_sparse(MODE)) {
+      const int n_union = build_union<MODE == kSrcSparseSelect>(ul, ss, r, h, a.num_kv_heads, row0, qo, kv, a.dev_err,
+                                      split == 0);
       const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
       base = split * chunk;
       nblk = 4 * max(0, min(n_union, base + chunk) - base);
@@ -315,7 +321,7 @@ struct BlockList {
   // is read masked out).  All 256 threads call; ends with a barrier.
   __device__ __forceinline__ void stage_range(Lds& ul, const AttnArgs& a, const DenseSource& ds,
                                               const SparseSource& ss, int r, int first, int n) {
-    static_assert(MODE != kSrcSparse, "dense block lists only");
+    static_assert(!is_sparse(MODE), "dense block lists only");
     const int tid = threadIdx.x;
     base = first;
     nblk = n;
@@ -343,7 +349,7 @@ struct BlockList {
   // Metadata of split-local block b as stored (wave-uniform values in vector registers).
   __device__ __forceinline__ Raw fetch(const Lds& ul, int b) const {
     Raw m;
-    if constexpr (MODE == kSrcSparse) {
+    if constexpr (is_sparse(MODE)) {
       const int e = base + (b >> 2);
       m.a = ul.upage[e];
       m.b = ul.uphys[e];
@@ -361,7 +367,7 @@ struct BlockList {
                                           const DenseSource& ds, const SparseSource& ss,
                                           uint64_t& kbase, uint64_t& vbase, int& pos0,
                                           int& mask) const {
-    if constexpr (MODE == kSrcSparse) {
+    if constexpr (is_sparse(MODE)) {
       const int quarter = b & 3;
       const int p = __builtin_amdgcn_readfirstlane(m.a);
       const int phys = __builtin_amdgcn_readfirstlane(m.b);

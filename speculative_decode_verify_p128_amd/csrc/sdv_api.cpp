@@ -510,14 +510,19 @@ int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_in
   return ok();
 }
 
-int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+}  // extern "C"
+
+// Sparse verify attention over the pages in topk_idx, or (scores non-null) over the
+// ladder top-k of scores selected inside the attention kernels.
+static int32_t sparse_attention(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                 const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                 int32_t num_q_heads, const sdv_paged_kv* kv,
                                 const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
-                                const int32_t* topk_idx, int32_t top_k, float softmax_scale,
+                                const int32_t* topk_idx, const float* scores, int32_t* topk_out,
+                                int32_t* cnt_out, int32_t top_k, float softmax_scale,
                                 int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                void* out, int32_t out_dt, int32_t* dev_err,
-                                hipStream_t stream) {
+                                void* out, int32_t out_dt, int32_t* dev_err, hipStream_t stream,
+                                const char* name) {
   int32_t st = check_paged_kv(kv);
   if (st) return st;
   st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv->num_kv_heads);
@@ -533,41 +538,88 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
     return fail(SDV_ERR_SHAPE, "top_k %d x max_qo_len %d outside [1, 512]", top_k, max_qo_len);
   if (max_pages < 1 || max_pages > 16384 || bt_stride < max_pages)
     return fail(SDV_ERR_SHAPE, "max_pages %d (<= 16384), bt_stride %d", max_pages, bt_stride);
+  if (scores && max_pages > sdv::kFusedTopkMaxPages)
+    return fail(SDV_ERR_SHAPE, "max_pages %d > %d for the in-kernel selection", max_pages,
+                sdv::kFusedTopkMaxPages);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
     return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
   if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
   st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, kv->head_dim, num_splits);
   if (st) return st;
-  if (B > 0 && (!block_table || !topk_idx || !out))
-    return fail(SDV_ERR_NULL_POINTER, "block_table, topk_idx and out must be non-null");
+  if (B > 0 && (!block_table || !out || (!scores && !topk_idx)))
+    return fail(SDV_ERR_NULL_POINTER, "block_table, %s and out must be non-null",
+                scores ? "scores" : "topk_idx");
   if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return fail(SDV_ERR_SHAPE, "out must be 16-byte aligned");
-  if (B == 0) return ok();
-
+  const int32_t fam = g_family.load();
   sdv::AttnArgs a{};
   a.q = q; a.q_dt = q_dt; a.qo_indptr = qo_indptr; a.kv_len = kv_len; a.B = B;
   a.max_qo_len = max_qo_len; a.num_q_heads = num_q_heads; a.num_kv_heads = kv->num_kv_heads;
   a.head_dim = kv->head_dim; a.kv_dt = kv->kv_dtype; a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale; a.softmax_scale = softmax_scale; a.num_splits = num_splits;
   a.out = out; a.out_dt = out_dt; a.dev_err = dev_err;
+  const bool select_in_kernel = scores && fam != 1 && fam != 2 && sdv::mfma_supported(a);
+  if (scores && !select_in_kernel && B > 0 && !topk_out)
+    return fail(SDV_ERR_NULL_POINTER, "the vector-ALU and register-prefetch kernels need "
+                "topk_idx to hold the selection");
+  if (B == 0) return ok();
+  hipError_t e;
+  if (scores && !select_in_kernel) {
+    // the selection as its own launch, then the attention over it
+    e = sdv::launch_topk(scores, qo_indptr, kv_len, B, max_qo_len, kv->num_kv_heads, max_pages,
+                         top_k, topk_out, cnt_out, dev_err, stream);
+    if (e != hipSuccess) return hip_status(e, name);
+    topk_idx = topk_out;
+  }
   split_workspace(workspace, rows_cap, num_q_heads, kv->head_dim, num_splits, &a.part_o, &a.part_lse);
   sdv::SparseSource src{kv->k, kv->v, kv->page_stride, kv->num_pages, block_table, bt_stride,
-                        max_pages, topk_idx, top_k};
-  const int32_t fam = g_family.load();
-  hipError_t e;
+                        max_pages, select_in_kernel ? nullptr : topk_idx, top_k,
+                        select_in_kernel ? scores : nullptr, topk_out, cnt_out};
   if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_sparse_valu(a, src, stream);
   else if (fam == 2) e = sdv::launch_attn_sparse_mfma(a, src, stream);
   else if (fam == 4) e = sdv::launch_attn_sparse_stream(a, src, stream);
   else e = sdv::launch_attn_sparse_waves(a, src, stream);
-  if (e != hipSuccess) return hip_status(e, "verify_attention_sparse launch");
+  if (e != hipSuccess) return hip_status(e, name);
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
                             qo_indptr, qo_indptr + B, num_q_heads, kv->head_dim, out, out_dt,
                             nullptr, stream);
-    if (e != hipSuccess) return hip_status(e, "verify_attention_sparse combine launch");
+    if (e != hipSuccess) return hip_status(e, name);
   }
   return ok();
+}
+
+extern "C" {
+
+int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                int32_t num_q_heads, const sdv_paged_kv* kv,
+                                const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                                const int32_t* topk_idx, int32_t top_k, float softmax_scale,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                void* out, int32_t out_dt, int32_t* dev_err,
+                                hipStream_t stream) {
+  return sparse_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
+                          max_pages, bt_stride, topk_idx, nullptr, nullptr, nullptr, top_k,
+                          softmax_scale, num_splits, workspace, workspace_bytes, out, out_dt,
+                          dev_err, stream, "verify_attention_sparse launch");
+}
+
+int32_t verify_attention_sparse_select(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                       const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                       int32_t num_q_heads, const sdv_paged_kv* kv,
+                                       const int32_t* block_table, int32_t max_pages,
+                                       int32_t bt_stride, const float* scores, int32_t top_k,
+                                       int32_t* topk_idx, int32_t* topk_cnt,
+                                       float softmax_scale, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* out, int32_t out_dt,
+                                       int32_t* dev_err, hipStream_t stream) {
+  if (B > 0 && !scores) return fail(SDV_ERR_NULL_POINTER, "scores must be non-null");
+  return sparse_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
+                          max_pages, bt_stride, nullptr, scores, topk_idx, topk_cnt, top_k,
+                          softmax_scale, num_splits, workspace, workspace_bytes, out, out_dt,
+                          dev_err, stream, "verify_attention_sparse_select launch");
 }
 
 int32_t lse_combine(const float* partial_out, const float* partial_lse, int32_t num_splits,

@@ -21,22 +21,69 @@ struct UnionLds {
   int32_t upage[kMaxUnion];     // request-local page number
   int32_t uphys[kMaxUnion];     // physical page (0 when out of range, then umask = 0)
   int32_t umask[kMaxUnion];     // bit t: verify token t selected the page
+  int32_t sel[kMaxUnion];       // in-kernel selection: [t][k] page, -1 padded
   int32_t scan[256];
 };
 
+// The ladder top-k of every verify token of (r, h) from ss.scores, one wave per token,
+// into u.sel (and ss.topk_out / ss.cnt_out when non-null and write_out): the same
+// selection as the top-k kernel.  All 256 threads call; ends with a barrier.
+__device__ inline void select_topk(UnionLds& u, const SparseSource& ss, int h, int Hkv, int row0,
+                                   int qo, int kv, bool write_out) {
+  static_assert(kFusedTopkMaxPages == 16 * kWave, "item counts below");
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int t = wave; t < qo; t += 256 / kWave) {
+    const int n = (kv - qo + t + 1 + kPage - 1) / kPage;
+    const int64_t unit = static_cast<int64_t>(row0 + t) * Hkv + h;
+    const float* srow = ss.scores + unit * ss.max_pages;
+    int32_t* gout = write_out && ss.topk_out ? ss.topk_out + unit * ss.top_k : nullptr;
+    int32_t* lout = u.sel + t * ss.top_k;
+    auto emit = [&](int k, int page) {
+      if (lane == 0) {
+        lout[k] = page;
+        if (gout) gout[k] = page;
+      }
+    };
+    // register slots per lane sized to this token's pages (each round rescans them)
+    const int items = (n + kWave - 1) / kWave;
+    int k_eff;
+    if (items <= 1) k_eff = wave_ladder_topk<1>(srow, n, ss.top_k, lane, emit);
+    else if (items <= 2) k_eff = wave_ladder_topk<2>(srow, n, ss.top_k, lane, emit);
+    else if (items <= 4) k_eff = wave_ladder_topk<4>(srow, n, ss.top_k, lane, emit);
+    else if (items <= 8) k_eff = wave_ladder_topk<8>(srow, n, ss.top_k, lane, emit);
+    else k_eff = wave_ladder_topk<16>(srow, n, ss.top_k, lane, emit);
+    for (int k = k_eff + lane; k < ss.top_k; k += kWave) {
+      lout[k] = -1;
+      if (gout) gout[k] = -1;
+    }
+    if (write_out && ss.cnt_out && lane == 0) ss.cnt_out[unit] = k_eff;
+  }
+  __syncthreads();
+}
+
 // All 256 threads must call.  Returns the number of distinct selected pages; flags
-// (and ignores) indices at or beyond a token's valid-page count.
+// (and ignores) indices at or beyond a token's valid-page count.  The pages come from
+// ss.topk_idx, or (SELECT) from the in-kernel selection of ss.scores, written out to
+// ss.topk_out / ss.cnt_out when write_out.
+template <bool SELECT>
 __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, int h, int Hkv,
-                                  int row0, int qo, int kv, int32_t* dev_err) {
+                                  int row0, int qo, int kv, int32_t* dev_err,
+                                  bool write_out = false) {
   const int tid = threadIdx.x;
   const int words = (ss.max_pages + 31) / 32;
+  if constexpr (SELECT) select_topk(u, ss, h, Hkv, row0, qo, kv, write_out);
+  auto selected = [&](int t, int k) {
+    if constexpr (SELECT) return u.sel[t * ss.top_k + k];
+    else return ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+  };
   for (int w = tid; w < words; w += 256) u.bitmap[w] = 0u;
   __syncthreads();
   const int n_el = qo * ss.top_k;
   for (int e = tid; e < n_el; e += 256) {
     const int t = e / ss.top_k;
     const int k = e - t * ss.top_k;
-    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+    const int p = selected(t, k);
     if (p < 0) continue;
     const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
     if (p >= nvalid) {
@@ -85,7 +132,7 @@ __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, in
   for (int e = tid; e < n_el; e += 256) {
     const int t = e / ss.top_k;
     const int k = e - t * ss.top_k;
-    const int p = ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
+    const int p = selected(t, k);
     const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
     if (p < 0 || p >= nvalid) continue;
     const int w = p >> 5;
