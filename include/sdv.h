@@ -477,6 +477,10 @@ const char* sdv_last_error(void);
  * pairs (split slots are then consecutive pieces of a pair; needs B <= 2048 and
  * ceil(block capacity / (num_splits - 1)) <= 1024, else as 0).  Automatic selection
  * uses it for verify_attention_paged when it applies, the per-wave kernel otherwise.
+ * 6 = the same persistent partition over one workgroup-shared LDS ring per workgroup
+ * that runs through the boundaries between (request, KV head) pieces (each piece's
+ * query rows staged through LDS by the same asynchronous copies), for dense and paged
+ * attention under the same conditions.
  * Process-wide; returns the previous value. */
 int32_t sdv_set_kernel_family(int32_t family);
 

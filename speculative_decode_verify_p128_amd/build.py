@@ -26,6 +26,14 @@ COMMON = [
 ]
 
 
+# Per-file additions.  The flat persistent kernel holds its accumulators in ordinary
+# VGPRs: at one workgroup per CU the compiler otherwise parks them in AGPRs and copies
+# them back and forth around every block's products.
+EXTRA = {
+    "k_attn_flat.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -40,7 +48,8 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src,
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "not a recognized feature" not in l)

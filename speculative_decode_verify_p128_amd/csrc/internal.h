@@ -137,6 +137,10 @@ constexpr int kPersistMaxRequests = 2048;
 bool persist_supported(const AttnArgs& a, int64_t cap_blocks);
 hipError_t launch_attn_dense_persist(const AttnArgs& a, const DenseSource& src, hipStream_t s);
 hipError_t launch_attn_paged_persist(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+// The same partition over one LDS block ring per workgroup that runs through the
+// boundaries between pieces (same conditions as persist_supported).
+hipError_t launch_attn_dense_flat(const AttnArgs& a, const DenseSource& src, hipStream_t s);
+hipError_t launch_attn_paged_flat(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 hipError_t launch_attn_paged_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 
 // Rows [*row_begin_dev, *row_end_dev) are combined (all rows_cap rows when null).

@@ -37,69 +37,20 @@
 namespace sdv {
 namespace {
 
-// A wave's share of one block copy: LPT asynchronous 16-byte-per-lane loads that
-// together copy one block (K then V) into a ring slot; lane l of instruction n lands at
-// slot + (n * 64 + l) * 16.  The per-lane source offsets inside the block's K or V run
-// and the LDS offsets inside the slot do not change from block to block, so a copy is
-// a scalar block base, a constant 32-bit lane offset and M0.
-template <int D, int KDT>
-struct BlockCopier {
-  using Gm = Geo<D, KDT>;
-  uint32_t off[Gm::LPT];      // lane's byte offset in the K or V run of the block
-  uint32_t lds[Gm::LPT];      // LDS byte offset of the instruction in the slot (uniform)
-  bool is_v[Gm::LPT];         // copies V rather than K (uniform)
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int n = 0; n < Gm::LPT; ++n) {
-      const int ins = wave * Gm::LPT + n;               // 0 .. 2 * 32 / RPI - 1
-      const int half = ins / (32 / Gm::RPI);            // 0 = K, 1 = V
-      const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
-      const int gchunk = ((lane % Gm::CPR) ^ Gm::swz(row)) & (Gm::CPR - 1);
-      off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
-      lds[n] = static_cast<uint32_t>(half * Gm::HALF + (ins % (32 / Gm::RPI)) * 64 * 16);
-      is_v[n] = half != 0;
-    }
-  }
-
-  // kbase, vbase: first byte of the block's K and V runs; slot_lds: LDS address of the
-  // ring slot.  All three are wave-uniform.
-  __device__ __forceinline__ void issue(uint64_t kbase, uint64_t vbase, uint32_t slot_lds) const {
-#pragma unroll
-    for (int n = 0; n < Gm::LPT; ++n) {
-      const uint64_t base = is_v[n] ? vbase : kbase;
-      const uint32_t m0 = slot_lds + lds[n];
-      // Inline assembly, so that the compiler's wait insertion, which cannot tell ring
-      // slots apart, does not drain the copies in flight before every LDS read; the
-      // ring's own vmcnt waits and barriers order copies and reads.  M0 (the copy's
-      // LDS base) is reserved by the compiler, which uses it in this kernel for
-      // nothing else; the clobber records that it is overwritten.  The copies are
-      // non-temporal: every K/V byte is read once.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                   :
-                   : "s"(m0), "v"(off[n]), "s"(base)
-                   : "memory", "m0");
-#pragma clang diagnostic pop
-    }
-  }
-};
-
-// Ring depth (blocks) per row-tile count: STAGES - 1 blocks are in flight while one is
-// computed, so a deeper ring hides more memory latency per workgroup, at the price of
-// LDS and so of workgroups per CU.
-template <int RT>
-constexpr int ring_stages() { return 4; }
+// Ring depth (blocks): ST - 1 blocks are in flight while one is computed, so a deeper
+// ring hides more memory latency per workgroup, at the price of LDS and so of
+// workgroups per CU (measured: 6 and 8 slots at one workgroup per CU are slower than 4
+// at two).
+constexpr int kRingStages = 4;
 
 // LDS of the ring kernels: the block ring (after the last block the same bytes stage
 // the output rows), the rows' maxima and sums, and the staged block list.
-template <int RT, int D, int KDT, int MODE>
+template <int RT, int D, int KDT, int MODE, int ST>
 struct RingLds {
   using Gm = Geo<D, KDT>;
   static constexpr int ROWS = RT * 16;
   static constexpr int OPAD = D + 4;
-  static constexpr int RING = ring_stages<RT>() * Gm::BLOCK;
+  static constexpr int RING = ST * Gm::BLOCK;
   static constexpr int OUTB = ROWS * OPAD * 4;
   __attribute__((aligned(16))) char ring[RING > OUTB ? RING : OUTB];
   float L[ROWS];
@@ -112,8 +63,8 @@ struct RingLds {
 // range `bl` (metadata in sh.ul), written as the final rows (out_slot < 0) or as the
 // normalised partial and log-sum-exp of split slot out_slot.  All 256 threads call; LDS
 // is free again only after a barrier that follows the call.
-template <int RT, int D, int KDT, int MODE>
-__device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE>& sh, const AttnArgs& a,
+template <int RT, int D, int KDT, int MODE, int ST>
+__device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE, ST>& sh, const AttnArgs& a,
                                             const DenseSource& ds, const SparseSource& ss,
                                             const BlockList<MODE, D, KDT>& bl, int r, int h,
                                             int row0, int qo, int kv, int out_slot) {
@@ -124,7 +75,7 @@ __device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE>& sh, const
   constexpr int NCP = 4 / RT;          // output-channel parts
   constexpr int NTW = NT / NCP;        // output tiles per wave
   constexpr int OPAD = D + 4;
-  constexpr int kStages = ring_stages<RT>();
+  constexpr int kStages = ST;
   static_assert(NTW >= 1, "tiles per wave");
   float (*o_lds)[OPAD] = reinterpret_cast<float (*)[OPAD]>(sh.ring);
   const int tid = threadIdx.x;
@@ -145,22 +96,6 @@ __device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE>& sh, const
   const int t_row = row_live ? row / G : 0;
   const int g_row = row_live ? row - t_row * G : 0;
   const int bound_row = row_live ? kv - qo + t_row + 1 : 0;
-  bf16x8 qb[STEPS];
-  {
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     ((static_cast<int64_t>(row0 + t_row) * a.num_q_heads + h * G + g_row) * D +
-                      q * (D / 4)) * 2;
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const uint4 w = row_live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
-      qb[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-  // Q is complete before any copy is issued, so no wait inside the block loop has to
-  // account for it (the compiler does not see the copies).
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  wait_vmcnt<0>();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
 
   const int nblk = bl.nblk;
@@ -200,6 +135,24 @@ __device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE>& sh, const
   }
   typename BL::Raw next{0, 0, 0};
   if (kStages - 1 < nblk) next = fetch(kStages - 1);
+
+  // The query rows load while the first blocks' copies are in flight; one wait then
+  // covers both, so no wait inside the block loop has to account for Q (the compiler,
+  // which does not see the copies, would otherwise wait for everything in flight there).
+  bf16x8 qb[STEPS];
+  {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(row0 + t_row) * a.num_q_heads + h * G + g_row) * D +
+                      q * (D / 4)) * 2;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const uint4 w = row_live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // Block b lives in slot b % kStages; the loop runs kStages blocks per trip so that every
   // slot offset and slot register index is a compile-time constant.
@@ -367,7 +320,7 @@ __device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE>& sh, const
 template <int RT, int D, int KDT, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 sdv_attn_stream_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
-  __shared__ RingLds<RT, D, KDT, MODE> sh;
+  __shared__ RingLds<RT, D, KDT, MODE, kRingStages> sh;
   // Grid x = (request, KV head), y = split: consecutive workgroups, which the hardware
   // deals round-robin to the eight XCDs, are different (request, head) pairs of the same
   // split, so long and short requests spread evenly over the XCDs, and the high splits
@@ -391,7 +344,8 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   }
   BlockList<MODE, D, KDT> bl;
   bl.stage(sh.ul, &sh.chunk, a, ds, ss, r, h, split, row0, qo, kv);
-  ring_attend<RT, D, KDT, MODE>(sh, a, ds, ss, bl, r, h, row0, qo, kv, a.num_splits > 1 ? split : -1);
+  ring_attend<RT, D, KDT, MODE, kRingStages>(sh, a, ds, ss, bl, r, h, row0, qo, kv,
+                                             a.num_splits > 1 ? split : -1);
 }
 
 template <int RT, int D, int KDT, int MODE>

@@ -131,7 +131,8 @@ __device__ __forceinline__ void waves_attend(WavesLds<RT, D, KDT, MODE>& sh, con
   const int G = a.num_q_heads / Hkv;
   const int nrows = qo * G;
 
-  // This lane's query row of every row tile (lane i of the tile), its token and bound.
+  // This lane's query row of every row tile (lane i of the tile), its token and bound
+  // (the rows' query values load after the first copies are issued, below).
   int t_row[RT], bound_row[RT];
   bf16x8 qb[RT][STEPS];
 #pragma unroll
@@ -139,22 +140,8 @@ __device__ __forceinline__ void waves_attend(WavesLds<RT, D, KDT, MODE>& sh, con
     const int row = rt * 16 + i;
     const bool live = row < nrows;
     t_row[rt] = live ? row / G : 0;
-    const int g_row = live ? row - t_row[rt] * G : 0;
     bound_row[rt] = live ? kv - qo + t_row[rt] + 1 : 0;
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     ((static_cast<int64_t>(row0 + t_row[rt]) * a.num_q_heads + h * G + g_row) * D +
-                      q * (D / 4)) * 2;
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const uint4 w = live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
-      qb[rt][s] = __builtin_bit_cast(bf16x8, w);
-    }
   }
-  // Q is complete before any copy is issued, so no wait inside the block loop has to
-  // account for it (the compiler does not see the copies).
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  wait_vmcnt<0>();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const float qk_scale = a.softmax_scale * a.k_scale * kLog2e;
 
   // This wave's blocks: split-local b = wave + 4 j, j < nbw.
@@ -194,6 +181,27 @@ __device__ __forceinline__ void waves_attend(WavesLds<RT, D, KDT, MODE>& sh, con
   }
   typename BL::Raw next{0, 0, 0};
   if (A < nbw) next = fetch(wave + 4 * A);
+
+  // The query rows load while the first blocks' copies are in flight; one wait then
+  // covers both, so no wait inside the block loop has to account for Q (the compiler,
+  // which does not see the copies, would otherwise wait for everything in flight there).
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + i;
+    const bool live = row < nrows;
+    const int g_row = live ? row - t_row[rt] * G : 0;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(row0 + t_row[rt]) * a.num_q_heads + h * G + g_row) * D +
+                      q * (D / 4)) * 2;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const uint4 w = live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      qb[rt][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   auto step = [&](auto slot_c, int j) {
     constexpr int u = decltype(slot_c)::value;

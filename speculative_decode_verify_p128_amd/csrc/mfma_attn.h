@@ -199,6 +199,55 @@ __device__ __forceinline__ bf16x8 v_operand(const uint32_t (&raw)[8][4], int n) 
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// A wave's share of one block copy: LPT asynchronous 16-byte-per-lane loads that
+// together copy one block (K then V) into a ring slot; lane l of instruction n lands at
+// slot + (n * 64 + l) * 16.  The per-lane source offsets inside the block's K or V run
+// and the LDS offsets inside the slot do not change from block to block, so a copy is
+// a scalar block base, a constant 32-bit lane offset and M0.
+template <int D, int KDT>
+struct BlockCopier {
+  using Gm = Geo<D, KDT>;
+  uint32_t off[Gm::LPT];      // lane's byte offset in the K or V run of the block
+  uint32_t lds[Gm::LPT];      // LDS byte offset of the instruction in the slot (uniform)
+  bool is_v[Gm::LPT];         // copies V rather than K (uniform)
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < Gm::LPT; ++n) {
+      const int ins = wave * Gm::LPT + n;               // 0 .. 2 * 32 / RPI - 1
+      const int half = ins / (32 / Gm::RPI);            // 0 = K, 1 = V
+      const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
+      const int gchunk = ((lane % Gm::CPR) ^ Gm::swz(row)) & (Gm::CPR - 1);
+      off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
+      lds[n] = static_cast<uint32_t>(half * Gm::HALF + (ins % (32 / Gm::RPI)) * 64 * 16);
+      is_v[n] = half != 0;
+    }
+  }
+
+  // kbase, vbase: first byte of the block's K and V runs; slot_lds: LDS address of the
+  // ring slot.  All three are wave-uniform.
+  __device__ __forceinline__ void issue(uint64_t kbase, uint64_t vbase, uint32_t slot_lds) const {
+#pragma unroll
+    for (int n = 0; n < Gm::LPT; ++n) {
+      const uint64_t base = is_v[n] ? vbase : kbase;
+      const uint32_t m0 = slot_lds + lds[n];
+      // Inline assembly, so that the compiler's wait insertion, which cannot tell ring
+      // slots apart, does not drain the copies in flight before every LDS read; the
+      // ring's own vmcnt waits and barriers order copies and reads.  M0 (the copy's
+      // LDS base) is reserved by the compiler, which uses it in this kernel for
+      // nothing else; the clobber records that it is overwritten.  The copies are
+      // non-temporal: every K/V byte is read once.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                   :
+                   : "s"(m0), "v"(off[n]), "s"(base)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  }
+};
+
 constexpr int kMaxDenseBlocks = 1024;   // 32-token blocks per dense split
 
 // f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
@@ -418,15 +467,14 @@ struct PersistLds {
   int seg_len;
 };
 
-// All 256 threads call.  attend(r, h, row0, qo, kv, first, n, slot) attends blocks
-// [first, first + n) of pair (r, h) into split slot `slot`; a barrier follows each call.
-template <int MODE, class Attend>
-__device__ __forceinline__ void persistent_walk(PersistLds& pl, const AttnArgs& a,
-                                                const DenseSource& ds, const SparseSource& ss,
-                                                Attend&& attend) {
+// All 256 threads call.  Fills pl.cum with the exclusive prefix of every request's
+// 32-token block count (cum[B] = total; inconsistent requests count 0 and workgroup 0
+// flags them) and pl.seg_len with the range length L.  Ends with a barrier.
+template <int MODE>
+__device__ __forceinline__ void persistent_prefix(PersistLds& pl, const AttnArgs& a,
+                                                  const DenseSource& ds, const SparseSource& ss) {
   const int tid = threadIdx.x;
   const int Hkv = a.num_kv_heads;
-  const int G = a.num_q_heads / Hkv;
   const int S = a.num_splits;
   const int cap = MODE == kSrcView ? ds.max_sub_pages : 4 * ss.max_pages;
   const int64_t kv_cap = static_cast<int64_t>(cap) * kSub;
@@ -471,6 +519,31 @@ __device__ __forceinline__ void persistent_walk(PersistLds& pl, const AttnArgs& 
     }
   }
   __syncthreads();
+}
+
+// The request holding flat block `pos` (< W): the last r with Hkv * cum[r] <= pos (it is
+// not empty).  Wave-uniform.
+__device__ __forceinline__ int persistent_request(const PersistLds& pl, int B, int Hkv, int pos) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(pl.cum[mid]) * Hkv <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// All 256 threads call.  attend(r, h, row0, qo, kv, first, n, slot) attends blocks
+// [first, first + n) of pair (r, h) into split slot `slot`; a barrier follows each call.
+template <int MODE, class Attend>
+__device__ __forceinline__ void persistent_walk(PersistLds& pl, const AttnArgs& a,
+                                                const DenseSource& ds, const SparseSource& ss,
+                                                Attend&& attend) {
+  const int tid = threadIdx.x;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int S = a.num_splits;
+  persistent_prefix<MODE>(pl, a, ds, ss);
   // values read from LDS are uniform: keep them in scalar registers
   const int L = __builtin_amdgcn_readfirstlane(pl.seg_len);
   const int W = __builtin_amdgcn_readfirstlane(pl.cum[a.B]) * Hkv;
@@ -478,14 +551,7 @@ __device__ __forceinline__ void persistent_walk(PersistLds& pl, const AttnArgs& 
   if (static_cast<int64_t>(g) * L >= W) return;
   const int begin = g * L;
   const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(begin) + L, W));
-  // the request holding `begin`: the last r with Hkv * cum[r] <= begin (it is not empty)
-  int lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(pl.cum[mid]) * Hkv <= begin) lo = mid;
-    else hi = mid - 1;
-  }
-  int r = lo;
+  int r = persistent_request(pl, a.B, Hkv, begin);
   int pos = begin;
   const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
   while (pos < end) {

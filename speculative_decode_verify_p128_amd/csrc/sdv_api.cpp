@@ -125,7 +125,7 @@ const char* sdv_status_string(int32_t status) {
 const char* sdv_last_error(void) { return g_last_error.c_str(); }
 
 int32_t sdv_set_kernel_family(int32_t family) {
-  return g_family.exchange(family >= 0 && family <= 5 ? family : 0);
+  return g_family.exchange(family >= 0 && family <= 6 ? family : 0);
 }
 
 int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_table,
@@ -242,7 +242,9 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   else if (fam == 3) e = sdv::launch_attn_dense_waves(a, src, stream);
   else if (fam == 5 && sdv::persist_supported(a, max_sub_pages))
     e = sdv::launch_attn_dense_persist(a, src, stream);
-  else e = sdv::launch_attn_dense_stream(a, src, stream);   // 0 (automatic), 4 and 5
+  else if (fam == 6 && sdv::persist_supported(a, max_sub_pages))
+    e = sdv::launch_attn_dense_flat(a, src, stream);
+  else e = sdv::launch_attn_dense_stream(a, src, stream);   // 0 (automatic), 4, 5 and 6
   if (e != hipSuccess) return hip_status(e, "verify_attention_dense launch");
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
@@ -499,6 +501,7 @@ int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_in
   if (fam == 4) e = sdv::launch_attn_paged_stream(a, src, stream);
   else if (fam == 3 || !sdv::persist_supported(a, 4ll * max_pages))
     e = sdv::launch_attn_paged_waves(a, src, stream);
+  else if (fam == 6) e = sdv::launch_attn_paged_flat(a, src, stream);
   else e = sdv::launch_attn_paged_persist(a, src, stream);   // 0 (automatic) and 5
   if (e != hipSuccess) return hip_status(e, "verify_attention_paged launch");
   if (num_splits > 1) {

@@ -33,7 +33,7 @@ def _announce(request):
     sdv.set_kernel_family(0)
 
 
-@pytest.mark.parametrize("family", [0, 3, 4, 5])
+@pytest.mark.parametrize("family", [0, 3, 4, 5, 6])
 @pytest.mark.parametrize("splits", [1, 2, 16])
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_paged_parity(w, splits, family):
@@ -49,7 +49,7 @@ def test_paged_parity(w, splits, family):
     assert ok, f"max abs err {worst}"
 
 
-@pytest.mark.parametrize("family", [0, 3, 4, 5])
+@pytest.mark.parametrize("family", [0, 3, 4, 5, 6])
 def test_paged_poison_never_read(family):
     """NaN beyond every request's kv_len in its last page and in every page it does not
     own: no output may see them."""

@@ -71,7 +71,7 @@ def test_subpage_offsets_bad_slot_flags_and_maps_to_slot0():
     assert list(o[1, 0, 0:4]) == [0, 1, 2, 3] and list(o[0, 1, 4:8]) == [4, 5, 6, 7]
 
 
-@pytest.mark.parametrize("family", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("family", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("splits", [1, 2, 16])
 @pytest.mark.parametrize("w", DENSE_CASES, ids=lambda w: w.name)
 def test_dense_parity(w, splits, family):
@@ -224,7 +224,7 @@ def test_sparse_poison_never_read(w, family):
     assert ok, worst
 
 
-@pytest.mark.parametrize("family", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("family", [0, 1, 2, 3, 4, 5, 6])
 def test_dense_poison_never_read(family):
     sdv.set_kernel_family(family)
     w = DENSE_S

@@ -19,7 +19,7 @@ if torch.cuda.is_available():
     from _parity import (DEV, DenseRun, PagedRun, dense_oracle, out_numpy, paged_oracle,
                          rows_of, tol_ok)
 
-FAMILIES = [5]   # the per-wave kernel under the persistent partition
+FAMILIES = [5, 6]   # the per-wave and the LDS-ring kernels under the persistent partition
 
 MANY_SHORT_VIEW = W.DENSE_BF16.scaled(name="many_short_view", batch=600, kv=("uniform", 4, 100),
                                       kv_capacity=128, num_q_heads=16)
