@@ -25,7 +25,9 @@
 //   The halving tree first pairs channels c and c + d/2, which live in different
 //   lanes of the group (DPP row shifts inside 16-lane rows), and ends inside the lane.
 //   Granularity matters more than per-wave start-up: four pages per wave measured
-//   faster than eight or sixteen streamed one after another by the same lanes.
+//   faster than eight or sixteen streamed one after another by the same lanes, and
+//   keeping the next 8 rows in flight while 8 are added (up to 24 per lane) measured
+//   no faster than batches of 16.
 #include "device.h"
 #include "internal.h"
 
@@ -81,9 +83,9 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   constexpr int U = 16;              // positions per unrolled step
   extern __shared__ float q_lds[];   // [qo][G][D] float
 
-  const int r = blockIdx.z;
-  const int h = blockIdx.y;
-  const int Hkv = gridDim.y;
+  const int r = blockIdx.y;
+  const int h = blockIdx.x;
+  const int Hkv = gridDim.x;
   const int row0 = qo_indptr[r];
   const int qo = qo_indptr[r + 1] - row0;
   const int kv = kv_len[r];
@@ -91,12 +93,12 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
                        static_cast<int64_t>(row0) + qo > static_cast<int64_t>(B) * max_qo_len;
   const bool bad_cap = !bad_len && static_cast<int64_t>(kv) > static_cast<int64_t>(max_pages) * kPage;
   if (bad_len || bad_cap) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0)
+    if (threadIdx.x == 0 && blockIdx.z == 0 && h == 0)
       set_err(dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
     return;
   }
   const int n_pages_r = (kv + kPage - 1) / kPage;
-  const int p_first = blockIdx.x * PPB;
+  const int p_first = blockIdx.z * PPB;
   if (p_first >= n_pages_r) return;
 
   // This lane group's page: its block-table entry is loaded first, so that its latency
@@ -254,7 +256,10 @@ static hipError_t launch_proxy_t(const void* q, int32_t q_dt, const int32_t* qo_
   constexpr int PPB = (kWave / (D / V)) * kProxyWaves;
   const int G = num_q_heads / kv.num_kv_heads;
   const size_t lds = static_cast<size_t>(max_qo_len) * G * D * sizeof(float);
-  dim3 grid((max_pages + PPB - 1) / PPB, kv.num_kv_heads, B);
+  // Grid x = KV head, y = request, z = run of pages: workgroups are dispatched x fastest,
+  // so the runs past a request's last page (empty, they exit at once) come at the end of
+  // the grid rather than between busy ones (≈ 1% faster on sparse_bf16).
+  dim3 grid(kv.num_kv_heads, B, (max_pages + PPB - 1) / PPB);
   hipLaunchKernelGGL((sdv_proxy_scores_kernel<KDT, D>), grid, dim3(64 * kProxyWaves), lds, s, q, q_dt,
                      qo_indptr, kv_len, B, max_qo_len, num_q_heads, G, kv.k, kv.page_stride,
                      kv.num_pages, block_table, bt_stride, max_pages, scores, dev_err);

@@ -292,6 +292,9 @@ int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
     return fail(SDV_ERR_SHAPE, "max_qo_len x group x head_dim exceeds 8192");
   if (max_pages < 1 || bt_stride < max_pages)
     return fail(SDV_ERR_SHAPE, "max_pages %d, bt_stride %d", max_pages, bt_stride);
+  // launch grid: y = request, z = run of four pages (each at most 65535)
+  if (B > 65535 || max_pages > 4 * 65535)
+    return fail(SDV_ERR_SHAPE, "batch %d (<= 65535) or max_pages %d (<= 262140)", B, max_pages);
   if (B > 0 && (!block_table || !scores))
     return fail(SDV_ERR_NULL_POINTER, "block_table and scores must be non-null");
   if (B == 0) return ok();

@@ -140,6 +140,8 @@ def test_proxy_rejections():
     assert _proxy(_kv(), bt_stride=4) == L.SDV_ERR_SHAPE
     assert _proxy(_kv(), max_qo=64) == L.SDV_ERR_SHAPE              # q staging too large
     assert _proxy(_kv(), scores=None) == L.SDV_ERR_NULL_POINTER
+    assert _proxy(_kv(), B=65536) == L.SDV_ERR_SHAPE                # launch grid limits
+    assert _proxy(_kv(), max_pages=4 * 65535 + 1, bt_stride=4 * 65535 + 1) == L.SDV_ERR_SHAPE
     assert _proxy(_kv(), B=0) == L.SDV_OK
 
 
