@@ -233,6 +233,18 @@ def time_graph(step_fns, steps, warmup, torch, flush=None):
     return ms
 
 
+def host_cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, n_req):
     """The oracle, untuned, on a bounded sample of the same workload, one thread."""
     import oracle
@@ -688,6 +700,7 @@ def main():
     if not args.no_cpu_baseline:
         c_cpu = W.SparseCase(**{**c.__dict__})
         result["cpu_baseline"] = cpu_baseline(c_cpu, args.cpu_sample)
+        result["cpu_baseline"]["cpu_model"] = host_cpu_model()
         pool, procs = oracle_pool
         try:
             result["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(c_cpu, args.cpu_sample,
