@@ -112,8 +112,11 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   int32_t phys = 0;
   if (active) phys = block_table[static_cast<int64_t>(r) * bt_stride + p];
 
-  // Stage this request's queries of KV head h as float: q_lds[(t * G + g) * D + c], eight
-  // channels (one 16- or 32-byte load) per item, QB items per thread in flight at once.
+  // Stage this request's queries of KV head h as float, row (t * G + g) of D channels,
+  // eight channels (one 16- or 32-byte load) per item, QB items per thread in flight at
+  // once.  Within a row, channel chunk k (channels 4k .. 4k + 3) sits at chunk position
+  // (k % (V/4)) * LPR + k / (V/4): the e-th chunk of every lane of a page group is
+  // contiguous, so the score step's reads (one chunk per lane) are free of bank conflicts.
   constexpr int QB = 4;
   const int q_items = qo * G * (D / 8);
   for (int i0 = threadIdx.x; i0 < q_items; i0 += QB * blockDim.x) {
@@ -143,9 +146,11 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     for (int k = 0; k < QB; ++k) {
       const int i8 = i0 + k * blockDim.x;
       if (i8 >= q_items) continue;
-      float4* dst = reinterpret_cast<float4*>(q_lds + static_cast<int64_t>(i8) * 8);
-      dst[0] = x[k][0];
-      dst[1] = x[k][1];
+      const int tg = i8 / (D / 8);
+      const int k0 = 2 * (i8 - tg * (D / 8));
+      float4* row = reinterpret_cast<float4*>(q_lds + static_cast<int64_t>(tg) * D);
+      row[(k0 % (V / 4)) * LPR + k0 / (V / 4)] = x[k][0];
+      row[((k0 + 1) % (V / 4)) * LPR + (k0 + 1) / (V / 4)] = x[k][1];
     }
   }
   __syncthreads();
@@ -218,11 +223,11 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     // Steps 2-4 for every query head of the group.
     float best = -INFINITY;
     for (int g = 0; g < G; ++g) {
-      const float4* qv = reinterpret_cast<const float4*>(q_lds + (t * G + g) * D + sub * V);
+      const float4* qv = reinterpret_cast<const float4*>(q_lds + (t * G + g) * D) + sub;
       float u[V];
 #pragma unroll
       for (int e4 = 0; e4 < V / 4; ++e4) {
-        const float4 q4 = qv[e4];
+        const float4 q4 = qv[e4 * LPR];
         u[4 * e4 + 0] = q4.x * acc[4 * e4 + 0];
         u[4 * e4 + 1] = q4.y * acc[4 * e4 + 1];
         u[4 * e4 + 2] = q4.z * acc[4 * e4 + 2];
