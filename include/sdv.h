@@ -190,6 +190,32 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
                                size_t workspace_bytes, void* out, int32_t out_dt,
                                int32_t* dev_err, hipStream_t stream);
 
+/*
+ * verify_attention_dense_view — kv_subpage_view_init's page indices and
+ * verify_attention_dense in one launch: the attention kernels compute each 32-token
+ * sub-page's P32 K and V indices from the block table as the view defines them
+ * (slot = block_table[r * bt_stride + i / 4], K = 4 * index_scale * slot + i % 4,
+ * V = K + 4), so no sub_offsets array is written or read.  (Sources: PR #17835
+ * Description and item 2 — the non-owning P32 view of the P128 pages; PR #18066
+ * draft-view index-scale commit.)
+ *
+ * view         host: a view validated by kv_subpage_view_init (a call with B = 0 only
+ *              validates the geometry and fills the view, launching nothing).
+ * block_table  device int32 [B][bt_stride] P128 slot ids; columns >= max_blocks unused;
+ *              kv_len[r] <= 128 * max_blocks.
+ * A slot id outside [0, num_slots) sets SDV_DEVERR_PAGE_RANGE in dev_err and its
+ * sub-pages are left out (the two-call path reads slot 0 there; both outputs are then
+ * unspecified for that request).  Other arguments, limits and results as in
+ * verify_attention_dense with max_sub_pages = 4 * max_blocks.
+ */
+int32_t verify_attention_dense_view(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                    const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                    int32_t num_q_heads, const sdv_subpage_view* view,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    int32_t bt_stride, float softmax_scale, int32_t num_splits,
+                                    void* workspace, size_t workspace_bytes, void* out,
+                                    int32_t out_dt, int32_t* dev_err, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------
  * Sparse target layer over ordinary head-major 128-token pages: page p of K holds
  * [num_kv_heads][128][head_dim] contiguous elements at k + p * page_stride (V alike).

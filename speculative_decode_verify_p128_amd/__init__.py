@@ -5,8 +5,8 @@ from .api import (PagedKV, SubpageView, alloc_workspace, copy_descriptors, dtype
                   greedy_accept, hnd_head_slice_descriptors,
                   kv_subpage_view_init, ladder_topk_pages, lse_combine, proxy_page_scores,
                   read_probe, set_kernel_family, stage_verify_kv_paged, stage_verify_kv_view,
-                  verify_attention_dense, verify_attention_paged, verify_attention_sparse,
-                  verify_attention_sparse_select,
+                  verify_attention_dense, verify_attention_dense_view, verify_attention_paged,
+                  verify_attention_sparse, verify_attention_sparse_select,
                   workspace_bytes)
 from ._lib import LIB_PATH, SdvError, load
 
@@ -15,7 +15,7 @@ __all__ = [
     "greedy_accept", "hnd_head_slice_descriptors",
     "kv_subpage_view_init", "ladder_topk_pages", "lse_combine", "proxy_page_scores", "read_probe",
     "set_kernel_family", "stage_verify_kv_paged", "stage_verify_kv_view",
-    "verify_attention_dense", "verify_attention_paged",
+    "verify_attention_dense", "verify_attention_dense_view", "verify_attention_paged",
     "verify_attention_sparse",
     "verify_attention_sparse_select",
     "workspace_bytes", "LIB_PATH", "SdvError", "load",

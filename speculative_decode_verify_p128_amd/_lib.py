@@ -67,6 +67,8 @@ SIGNATURES = {
                                   C.POINTER(SubpageView), _P, _P]),
     "verify_attention_dense": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(SubpageView), _P, _I,
                                     _F, _I, _P, _S, _P, _I, _P, _P]),
+    "verify_attention_dense_view": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(SubpageView), _P,
+                                         _I, _I, _F, _I, _P, _S, _P, _I, _P, _P]),
     "proxy_page_scores": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I, _P,
                                _P, _P]),
     "ladder_topk_pages": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),

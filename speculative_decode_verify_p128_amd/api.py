@@ -62,18 +62,22 @@ def kv_subpage_view_init(k_root: torch.Tensor, block_table: torch.Tensor, *, num
                          kv_offset: int = 1, num_layers: int = 1, phys_page: int = 128,
                          sub_page: int = 32, max_blocks: Optional[int] = None,
                          sub_offsets: Optional[torch.Tensor] = None,
-                         dev_err: Optional[torch.Tensor] = None):
+                         dev_err: Optional[torch.Tensor] = None, stage_offsets: bool = True):
     """k_root: tensor whose first element is slot 0's draft-layer K page.
     block_table: int32 [B, W] P128 slot ids.  Returns (SubpageView, sub_offsets
-    int32 [B, 2, 4 * max_blocks])."""
+    int32 [B, 2, 4 * max_blocks]); with stage_offsets=False only the geometry is
+    validated (for verify_attention_dense_view) and sub_offsets is None."""
     _need(block_table, "block_table", torch.int32, contiguous=False)
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be contiguous")
     B, W = block_table.shape
     mb = W if max_blocks is None else max_blocks
-    if sub_offsets is None:
+    if not stage_offsets:
+        B = 0
+    elif sub_offsets is None:
         sub_offsets = torch.empty((B, 2, 4 * mb), dtype=torch.int32, device=block_table.device)
-    _need(sub_offsets, "sub_offsets", torch.int32)
+    if stage_offsets:
+        _need(sub_offsets, "sub_offsets", torch.int32)
     geom = L.SubpageGeom(phys_page, sub_page, num_kv_heads, head_dim, slot_stride, kv_offset,
                          num_layers, num_slots, pool_index_scale, dtype_code(k_root.dtype),
                          k_scale, v_scale, k_root.data_ptr())
@@ -123,6 +127,36 @@ def verify_attention_dense(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: tor
     L.check(L.load().verify_attention_dense(
         _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
         C.byref(view.c), _ptr(sub_offsets), sub_offsets.shape[-1], softmax_scale, num_splits,
+        _ptr(workspace), ws_bytes, _ptr(out), dtype_code(out.dtype), _ptr(dev_err),
+        _stream(q.device)))
+    return out
+
+
+def verify_attention_dense_view(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len: torch.Tensor,
+                                view: SubpageView, block_table: torch.Tensor, *, max_qo_len: int,
+                                softmax_scale: float, num_splits: int = 1,
+                                max_blocks: Optional[int] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                out: Optional[torch.Tensor] = None, out_dtype=None,
+                                dev_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """verify_attention_dense with the view's page indices computed in the attention
+    launch from block_table (int32 [B, W] P128 slot ids)."""
+    _need(q, "q")
+    _need(qo_indptr, "qo_indptr", torch.int32)
+    _need(kv_len, "kv_len", torch.int32)
+    _need(block_table, "block_table", torch.int32, contiguous=False)
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    B = kv_len.numel()
+    mb = block_table.shape[1] if max_blocks is None else max_blocks
+    rows_cap = B * max_qo_len
+    out = _out(out, q, rows_cap, out_dtype)
+    if workspace is None and num_splits > 1:
+        workspace = alloc_workspace(rows_cap, q.shape[1], q.shape[2], num_splits, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().verify_attention_dense_view(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(view.c), _ptr(block_table), mb, block_table.stride(0), softmax_scale, num_splits,
         _ptr(workspace), ws_bytes, _ptr(out), dtype_code(out.dtype), _ptr(dev_err),
         _stream(q.device)))
     return out

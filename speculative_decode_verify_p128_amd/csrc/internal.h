@@ -12,10 +12,36 @@ namespace sdv {
 // Where a (request, KV head)'s 32-token K/V blocks live.
 struct DenseSource {            // P32 sub-page view
   const void* root;             // element 0 of P32 page 0
-  const int32_t* sub_offsets;   // [B][2][max_sub_pages]
+  const int32_t* sub_offsets;   // [B][2][max_sub_pages], or null: from the block table
   int32_t max_sub_pages;
   int64_t num_sub_pages;        // valid P32 page range from root
+  const int32_t* block_table;   // [B][bt_stride] slot ids (when sub_offsets is null)
+  int32_t bt_stride;
+  int32_t slot_stride;          // the view's index scale
+  int32_t num_slots;
 };
+
+// P32 page indices of K and V of 32-token block i of request r through the view: from
+// the staged offsets, or without them from the block table as the view defines them
+// (slot = block_table[r][i / 4], K = 4 * slot_stride * slot + i % 4, V = K + 4).
+// False when an index leaves the view (the caller flags it and masks the block out).
+__device__ __forceinline__ bool view_pages(const DenseSource& ds, int64_t r, int i, int64_t& xk,
+                                           int64_t& xv) {
+  if (ds.sub_offsets) {
+    const int32_t* offs = ds.sub_offsets + r * 2 * ds.max_sub_pages;
+    xk = offs[i];
+    xv = offs[ds.max_sub_pages + i];
+  } else {
+    const int32_t slot = ds.block_table[r * ds.bt_stride + (i >> 2)];
+    if (slot < 0 || slot >= ds.num_slots) {
+      xk = xv = -1;
+      return false;
+    }
+    xk = 4ll * ds.slot_stride * slot + (i & 3);
+    xv = xk + 4;
+  }
+  return xk >= 0 && xk < ds.num_sub_pages && xv >= 0 && xv < ds.num_sub_pages;
+}
 
 struct SparseSource {           // head-major P128 pages + selected page lists
   const void* k;

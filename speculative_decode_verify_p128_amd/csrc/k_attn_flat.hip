@@ -438,12 +438,10 @@ sdv_attn_flat_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
       const int pb = sh.piece[lo].first + (b - sh.piece[lo].start);
       int32_t xb;
       if constexpr (MODE == kSrcView) {
-        const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(rr) * 2 * ds.max_sub_pages;
-        const int32_t xk = offs[pb];
-        const int32_t xv = offs[ds.max_sub_pages + pb];
-        const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
+        int64_t xk, xv;
+        const bool ok = view_pages(ds, rr, pb, xk, xv) && xv == xk + 4;
         if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
-        xb = ok ? xk : -1;
+        xb = ok ? static_cast<int32_t>(xk) : -1;
       } else {
         const int32_t phys = ss.block_table[static_cast<int64_t>(rr) * ss.bt_stride + (pb >> 2)];
         const bool ok = phys >= 0 && phys < ss.num_pages;

@@ -323,12 +323,10 @@ __global__ void __launch_bounds__(256) sdv_attn_mfma_kernel(AttnArgs a, DenseSou
       return true;
     } else {
       const int x = base + j;
-      const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
-      const int64_t xk = offs[x];
-      const int64_t xv = offs[ds.max_sub_pages + x];
+      int64_t xk, xv;
       mask = ~0;
       pos0 = x * kSub;
-      if (xk < 0 || xk >= ds.num_sub_pages || xv < 0 || xv >= ds.num_sub_pages) {
+      if (!view_pages(ds, r, x, xk, xv)) {
         set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
         return false;
       }

@@ -115,10 +115,8 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
       vofs = kofs;
       pos_base = p * kPage;
     } else {
-      const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
-      const int64_t xk = offs[item];
-      const int64_t xv = offs[ds.max_sub_pages + item];
-      if (xk < 0 || xk >= ds.num_sub_pages || xv < 0 || xv >= ds.num_sub_pages) ok = false;
+      int64_t xk, xv;
+      if (!view_pages(ds, r, item, xk, xv)) ok = false;
       kb = ds.root;
       vb = ds.root;
       kofs = (xk * Hkv + h) * kSub * D;

@@ -375,13 +375,11 @@ struct BlockList {
     base = first;
     nblk = n;
     if constexpr (MODE == kSrcView) {
-      const int32_t* offs = ds.sub_offsets + static_cast<int64_t>(r) * 2 * ds.max_sub_pages;
       for (int b = tid; b < nblk; b += 256) {
-        const int32_t xk = offs[base + b];
-        const int32_t xv = offs[ds.max_sub_pages + base + b];
-        const bool ok = xk >= 0 && xk + 4 < ds.num_sub_pages && xv == xk + 4;
+        int64_t xk, xv;
+        const bool ok = view_pages(ds, r, base + b, xk, xv) && xv == xk + 4;
         if (!ok) set_err(a.dev_err, SDV_DEVERR_PAGE_RANGE);
-        ul.x[b] = ok ? xk : -1;
+        ul.x[b] = ok ? static_cast<int32_t>(xk) : -1;
       }
     } else {
       const int32_t* bt = ss.block_table + static_cast<int64_t>(r) * ss.bt_stride;

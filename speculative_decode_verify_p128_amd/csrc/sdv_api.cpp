@@ -192,13 +192,18 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
                     "kv_subpage_view_init launch");
 }
 
-int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+}  // extern "C"
+
+// Dense verify attention through the P32 view: block indices from sub_offsets, or (null)
+// from block_table as the view defines them.
+static int32_t dense_attention(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                int32_t num_q_heads, const sdv_subpage_view* view,
                                const int32_t* sub_offsets, int32_t max_sub_pages,
+                               const int32_t* block_table, int32_t bt_stride,
                                float softmax_scale, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, void* out, int32_t out_dt,
-                               int32_t* dev_err, hipStream_t stream) {
+                               int32_t* dev_err, hipStream_t stream, const char* name) {
   if (!view) return fail(SDV_ERR_NULL_POINTER, "view must be non-null");
   const sdv_subpage_view& v = *view;
   int32_t st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, v.num_kv_heads);
@@ -219,8 +224,9 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
   st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, v.head_dim, num_splits);
   if (st) return st;
-  if (B > 0 && (!sub_offsets || !out))
-    return fail(SDV_ERR_NULL_POINTER, "sub_offsets and out must be non-null");
+  if (B > 0 && ((!sub_offsets && !block_table) || !out))
+    return fail(SDV_ERR_NULL_POINTER, "%s and out must be non-null",
+                block_table ? "block_table" : "sub_offsets");
   if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return fail(SDV_ERR_SHAPE, "out must be 16-byte aligned");
   if (B == 0) return ok();
@@ -232,7 +238,8 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   a.softmax_scale = softmax_scale; a.num_splits = num_splits; a.out = out; a.out_dt = out_dt;
   a.dev_err = dev_err;
   split_workspace(workspace, rows_cap, num_q_heads, v.head_dim, num_splits, &a.part_o, &a.part_lse);
-  sdv::DenseSource src{v.k_root, sub_offsets, max_sub_pages, v.num_sub_pages};
+  sdv::DenseSource src{v.k_root, sub_offsets, max_sub_pages, v.num_sub_pages,
+                       sub_offsets ? nullptr : block_table, bt_stride, v.index_scale, v.num_slots};
   const int32_t fam = g_family.load();
   const bool stream_ok =
       (max_sub_pages + num_splits - 1) / num_splits <= sdv::kStreamMaxDenseBlocks;
@@ -245,14 +252,48 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
   else if (fam == 6 && sdv::persist_supported(a, max_sub_pages))
     e = sdv::launch_attn_dense_flat(a, src, stream);
   else e = sdv::launch_attn_dense_stream(a, src, stream);   // 0 (automatic), 4, 5 and 6
-  if (e != hipSuccess) return hip_status(e, "verify_attention_dense launch");
+  if (e != hipSuccess) return hip_status(e, name);
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
                             qo_indptr, qo_indptr + B, num_q_heads, v.head_dim, out, out_dt,
                             nullptr, stream);
-    if (e != hipSuccess) return hip_status(e, "verify_attention_dense combine launch");
+    if (e != hipSuccess) return hip_status(e, name);
   }
   return ok();
+}
+
+extern "C" {
+
+int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_subpage_view* view,
+                               const int32_t* sub_offsets, int32_t max_sub_pages,
+                               float softmax_scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* out, int32_t out_dt,
+                               int32_t* dev_err, hipStream_t stream) {
+  if (B > 0 && !sub_offsets) return fail(SDV_ERR_NULL_POINTER, "sub_offsets must be non-null");
+  return dense_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                         sub_offsets, max_sub_pages, nullptr, 0, softmax_scale, num_splits,
+                         workspace, workspace_bytes, out, out_dt, dev_err, stream,
+                         "verify_attention_dense launch");
+}
+
+int32_t verify_attention_dense_view(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                    const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                    int32_t num_q_heads, const sdv_subpage_view* view,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    int32_t bt_stride, float softmax_scale, int32_t num_splits,
+                                    void* workspace, size_t workspace_bytes, void* out,
+                                    int32_t out_dt, int32_t* dev_err, hipStream_t stream) {
+  if (max_blocks < 1 || bt_stride < max_blocks)
+    return fail(SDV_ERR_SHAPE, "max_blocks %d, bt_stride %d", max_blocks, bt_stride);
+  if (static_cast<int64_t>(max_blocks) * 4 > INT32_MAX / 32)
+    return fail(SDV_ERR_SHAPE, "max_blocks %d too large", max_blocks);
+  if (B > 0 && !block_table) return fail(SDV_ERR_NULL_POINTER, "block_table must be non-null");
+  return dense_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view, nullptr,
+                         4 * max_blocks, block_table, bt_stride, softmax_scale, num_splits,
+                         workspace, workspace_bytes, out, out_dt, dev_err, stream,
+                         "verify_attention_dense_view launch");
 }
 
 static int32_t check_paged_kv(const sdv_paged_kv* kv) {

@@ -110,8 +110,33 @@ def test_dense_rejections():
     assert _dense(v, q=C.c_void_p(0x10008)) == L.SDV_ERR_SHAPE    # q not 16-byte aligned
     assert _dense(v, out=C.c_void_p(0x10004)) == L.SDV_ERR_SHAPE  # out not 16-byte aligned
     assert _dense(v, B=0) == L.SDV_OK                             # nothing to do
+    assert _dense(v, offs=None) == L.SDV_ERR_NULL_POINTER
     empty = L.SubpageView()
     assert _dense(empty) != L.SDV_OK
+
+
+def _dense_view(view, **kw):
+    a = dict(q=FAKE, q_dt=L.SDV_BF16, qo=FAKE, kv=FAKE, B=2, max_qo=4, Hq=64, bt=FAKE, mb=16,
+             bts=16, scale=0.088, splits=1, ws=None, ws_bytes=0, out=FAKE, out_dt=L.SDV_BF16)
+    a.update(kw)
+    return L.load().verify_attention_dense_view(
+        a["q"], a["q_dt"], a["qo"], a["kv"], a["B"], a["max_qo"], a["Hq"], C.byref(view),
+        a["bt"], a["mb"], a["bts"], a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["out"],
+        a["out_dt"], None, None)
+
+
+def test_dense_view_rejections():
+    v = _good_view()
+    assert _dense_view(v, mb=0) == L.SDV_ERR_SHAPE
+    assert _dense_view(v, bts=8) == L.SDV_ERR_SHAPE               # row stride below width
+    assert _dense_view(v, mb=1 << 25, bts=1 << 25) == L.SDV_ERR_SHAPE
+    assert _dense_view(v, bt=None) == L.SDV_ERR_NULL_POINTER
+    assert _dense_view(v, q_dt=L.SDV_F32) == L.SDV_ERR_DTYPE
+    assert _dense_view(v, max_qo=5) == L.SDV_ERR_SHAPE
+    assert _dense_view(v, splits=4) == L.SDV_ERR_WORKSPACE
+    assert _dense_view(v, out=None) == L.SDV_ERR_NULL_POINTER
+    assert _dense_view(v, B=0) == L.SDV_OK
+    assert _dense_view(L.SubpageView()) != L.SDV_OK
 
 
 def _kv(**kw):
