@@ -5,8 +5,9 @@ proxy page scores, then the ladder top-k and the sparse verify attention in one 
 (+ split-KV combine), on the sparse bf16 workload (batch 64, qo_len 4, 16/4 heads,
 head_dim 128, kv_len uniform in [4096, 32768], top-k 16).  The same path as three
 launches (standalone top-k) is timed after it and reported under "unfused".  Inputs are
-generated on the GPU from a seed and are resident in HBM before timing starts.  The dense draft-layer path (P32 view
-offsets + dense verify attention, batch 32, qo_len 4, 64/4 heads, kv_len uniform in
+generated on the GPU from a seed and are resident in HBM before timing starts.  The
+dense draft-layer path (dense verify attention through the P32 view, its page indices
+computed in the same launch; batch 32, qo_len 4, 64/4 heads, kv_len uniform in
 [1024, 8192]) is timed in the same run and reported under "dense".
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on the
@@ -53,6 +54,9 @@ def parse():
                    help="time the headline step as one HIP graph replay instead of eager launches")
     p.add_argument("--warm", action="store_true",
                    help="no cache-evicting fill between steps (warm-cache numbers)")
+    p.add_argument("--dense-two-call", action="store_true",
+                   help="also time the draft-layer step as two calls (view offsets, then "
+                        "attention over them), reported under dense.two_call")
     p.add_argument("--no-unfused", action="store_true",
                    help="skip timing the three-launch step (proxy, standalone top-k, sparse "
                         "attention over its indices) reported under 'unfused'")
@@ -104,14 +108,18 @@ def sparse_algorithmic_bytes(case, idx_np):
             "sparse_row_expanded_kv": rowexp * d * e * 2}
 
 
-def dense_algorithmic_bytes(case):
+def dense_algorithmic_bytes(case, staged_offsets=False):
+    """Every valid K and V row once, Q and O, and the page indices: the block-table
+    entries (one per 128-token page) when the attention computes the view's indices,
+    the staged K and V offsets (one each per 32-token sub-page) otherwise."""
     w = case.w
     e = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
     eq = {"f32": 4, "bf16": 2}[w.q_dtype]
     rows = case.lengths.total_q
     kv = case.lengths.kv
+    idx = int((-(-kv // 32)).sum()) * 2 * 4 if staged_offsets else int((-(-kv // 128)).sum()) * 4
     return int(kv.sum()) * w.num_kv_heads * w.head_dim * e * 2 + \
-        2 * rows * w.num_q_heads * w.head_dim * eq + int((-(-kv // 32)).sum()) * 2 * 4
+        2 * rows * w.num_q_heads * w.head_dim * eq + idx
 
 
 # Sources that decide each timed kernel's memory traffic: a counter summary taken on
@@ -125,6 +133,8 @@ KERNEL_SOURCES = {
                                        "k_small.hip", "device.h", "internal.h", "sdv_api.cpp"),
     "verify_attention_dense": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
                                "internal.h", "sdv_api.cpp"),
+    "verify_attention_dense_view": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
+                                    "internal.h", "sdv_api.cpp"),
     "verify_attention_paged": ("k_attn_waves.hip", "mfma_attn.h", "k_small.hip", "device.h",
                                "internal.h", "sdv_api.cpp"),
     "greedy_accept": ("k_accept.hip", "device.h", "internal.h", "sdv_api.cpp"),
@@ -540,6 +550,15 @@ def main():
         wsd = sdv.alloc_workspace(rows_d, wd.num_q_heads, wd.head_dim, dsplits, dev)
         offs = torch.empty((wd.batch, 2, 4 * wd.max_pages()), dtype=torch.int32, device=dev)
         holder = {}
+        view_only, _ = sdv.kv_subpage_view_init(
+            d.pool[wd.root_page], d.block_table, num_kv_heads=wd.num_kv_heads,
+            head_dim=wd.head_dim, slot_stride=wd.slot_stride, num_slots=d.num_slots,
+            pool_index_scale=wd.pool_index_scale, stage_offsets=False)
+
+        def k_dview():
+            sdv.verify_attention_dense_view(d.q, d.qo_indptr, d.kv_len, view_only, d.block_table,
+                                            max_qo_len=wd.max_qo(), softmax_scale=d.softmax_scale,
+                                            num_splits=dsplits, workspace=wsd, out=outd)
 
         def k_view():
             holder["view"], _ = sdv.kv_subpage_view_init(
@@ -547,29 +566,41 @@ def main():
                 head_dim=wd.head_dim, slot_stride=wd.slot_stride, num_slots=d.num_slots,
                 pool_index_scale=wd.pool_index_scale, sub_offsets=offs)
 
-        k_view()
-
         def k_dense():
             sdv.verify_attention_dense(d.q, d.qo_indptr, d.kv_len, holder["view"], offs,
                                        max_qo_len=wd.max_qo(), softmax_scale=d.softmax_scale,
                                        num_splits=dsplits, workspace=wsd, out=outd)
 
-        msd, perd, _ = time_steps([("kv_subpage_view_init", k_view),
-                                   ("verify_attention_dense", k_dense)],
+        # the step: the view's page indices computed inside the attention launch
+        msd, perd, _ = time_steps([("verify_attention_dense_view", k_dview)],
                                   args.steps, args.warmup, torch, flush)
+        # the two-call path (view offsets, then attention over them) must give the same bits
+        fused_out = outd.clone()
+        k_view()
+        k_dense()
+        torch.cuda.synchronize()
+        if not torch.equal(outd.view(torch.int16), fused_out.view(torch.int16)):
+            raise RuntimeError("dense view in the attention launch and the two-call path differ")
+        del fused_out
         db = dense_algorithmic_bytes(d)
-        gbs = db / (perd["verify_attention_dense"]["avg_us"] * 1e-6) / 1e9
+        gbs = db / (perd["verify_attention_dense_view"]["avg_us"] * 1e-6) / 1e9
         result["dense"] = {
             "workload": "dense_bf16: draft-layer verify through the P32 view, batch 32, qo_len 4, "
                         "64 q / 4 kv heads, head_dim 128, kv_len U[1024, 8192], slot stride 8",
             "value": d.lengths.total_q / (msd * 1e-3), "unit": "verify tokens/s",
             "ms_per_step": msd, "num_splits": dsplits, "algorithmic_bytes": db,
             "kernels": perd,
-            "roofline": {"bound": "hbm", "kernel": "verify_attention_dense", "achieved": gbs,
+            "roofline": {"bound": "hbm", "kernel": "verify_attention_dense_view", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": load_traffic("verify_attention_dense", wd.name,
-                                                 source_hash(*KERNEL_SOURCES["verify_attention_dense"]))},
+                         "traffic": load_traffic("verify_attention_dense_view", wd.name,
+                                                 source_hash(*KERNEL_SOURCES["verify_attention_dense_view"]))},
         }
+        if args.dense_two_call:
+            ms2, per2, _ = time_steps([("kv_subpage_view_init", k_view),
+                                       ("verify_attention_dense", k_dense)],
+                                      args.steps, args.warmup, torch, flush)
+            result["dense"]["two_call"] = {"ms_per_step": ms2, "kernels": per2,
+                                           "algorithmic_bytes": dense_algorithmic_bytes(d, True)}
         del d, outd, wsd
 
     # ---- target dense layers: ladder attention over ordinary head-major P128 pages ----
