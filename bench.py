@@ -10,8 +10,10 @@ dense draft-layer path (dense verify attention through the P32 view, its page in
 computed in the same launch; batch 32, qo_len 4, 64/4 heads, kv_len uniform in
 [1024, 8192]) is timed in the same run and reported under "dense".
 
-Prints one JSON line.  Per-kernel durations come from HIP events recorded on the
-launch stream around every kernel inside the timed loop.
+Prints one JSON line.  The step time comes from one pair of HIP events around each
+timed step; per-kernel durations come from HIP events recorded on the launch stream
+around every kernel in a second timed loop of the same steps (an event between two
+launches delays the second, so it stays out of the step time).
 """
 from __future__ import annotations
 
@@ -175,30 +177,46 @@ def load_traffic(kernel, workload, src_hash):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_steps(step_fns, steps, warmup, torch, flush=None):
-    """Runs warmup + timed steps; events around each kernel on the current stream.  With
-    `flush`, a cache-evicting fill runs before every step outside the timed span (the
-    step time is the event span from the step's first kernel to its last)."""
-    for _ in range(warmup):
-        if flush:
-            flush()
-        for _, fn in step_fns:
-            fn()
-    torch.cuda.synchronize()
+def time_steps(step_fns, steps, warmup, torch, flush=None, stats=None):
+    """Runs warmup + timed steps.  With `flush`, a cache-evicting fill runs before every
+    step outside the timed span.  The step time comes from one pair of events around each
+    step's launches; an event recorded between two launches delays the second by several
+    microseconds, so when a step has more than one launch the per-launch durations come
+    from a second timed pass with events around every launch (`stats`, if given, receives
+    that pass's mean step time).  Returns (ms per step, per-launch stats, wall seconds
+    of the first pass)."""
     n = len(step_fns)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        if flush:
-            flush()
-        ev[s][0].record()
-        for i, (_, fn) in enumerate(step_fns):
-            fn()
-            ev[s][i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = [ev[s][0].elapsed_time(ev[s][n]) for s in range(steps)]
+
+    def run_pass(per_launch):
+        for _ in range(warmup):
+            if flush:
+                flush()
+            for _, fn in step_fns:
+                fn()
+        torch.cuda.synchronize()
+        marks = n + 1 if per_launch else 2
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s in range(steps):
+            if flush:
+                flush()
+            ev[s][0].record()
+            for i, (_, fn) in enumerate(step_fns):
+                fn()
+                if per_launch:
+                    ev[s][i + 1].record()
+            if not per_launch:
+                ev[s][1].record()
+        torch.cuda.synchronize()
+        return ev, time.perf_counter() - t0
+
+    ev, wall = run_pass(per_launch=(n == 1))
+    step_ms = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]
+    if n > 1:
+        ev, _ = run_pass(per_launch=True)
+        if stats is not None:
+            stats["ms_per_step_with_launch_events"] = float(np.mean(
+                [ev[s][0].elapsed_time(ev[s][n]) for s in range(steps)]))
     per = {}
     for i, (name, _) in enumerate(step_fns):
         ts = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]
@@ -457,7 +475,8 @@ def main():
                                            workspace=ws, out=out)
 
     fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
-    eager_ms, per, wall = time_steps(fns, args.steps, args.warmup, torch, flush)
+    launch_stats = {}
+    eager_ms, per, wall = time_steps(fns, args.steps, args.warmup, torch, flush, launch_stats)
     ms = eager_ms
     if args.graph:
         # the step as one HIP graph (the path is capture-safe: no allocation, no host
@@ -532,6 +551,7 @@ def main():
                    "times in kernels come from an eager pass with events around every launch"
                    if args.graph else "eager: one launch per kernel"),
         "eager_ms_per_step": eager_ms,
+        "ms_per_step_with_launch_events": launch_stats.get("ms_per_step_with_launch_events"),
         "unfused": unfused,
         "sparse_row_expanded_kv_bytes": ab["sparse_row_expanded_kv"],
         "wall_s_timed": wall,
