@@ -17,9 +17,9 @@
 // of a pair becomes the partial of split slot (g - first workgroup of the pair), merged
 // by the ordinary combine.
 //
-// Where the partition kernel over the ring restarts its pipeline for every piece (a
-// query load, a block-list load, the ring's fill and an output pass through LDS, each a
-// memory round trip), this kernel plans the whole range first: the pieces, their
+// Restarting the ring for every piece costs a query load, a block-list load, the ring's
+// fill and an output pass through LDS, each a memory round trip (measured slower than the
+// per-split grid).  This kernel plans the whole range first instead: the pieces, their
 // requests' lengths and every block's page index go to LDS, and then the ring runs over
 // the range without a break.  A piece's query rows are copied into LDS by the same
 // asynchronous copies as the K/V blocks, issued with the copies of the piece's first
