@@ -308,11 +308,12 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
  * scores    device float [B*max_qo_len][num_kv_heads][max_pages] (proxy_page_scores).
  * topk_idx  device int32 [B*max_qo_len][num_kv_heads][top_k] OUT, nullable: the
  *           selection as ladder_topk_pages writes it.  Required (SDV_ERR_NULL_POINTER
- *           otherwise) when the vector-ALU or register-streaming kernels run — kernel
- *           families 1 and 2, and f32 query/KV — which take the selection as a launch
- *           of its own first.  Rows of requests flagged on the device are not written.
+ *           otherwise) when the selection runs as a launch of its own first: kernel
+ *           families 1 and 2, f32 query/KV, and max_pages > 1024 (the in-kernel
+ *           selection holds up to 1024 pages).  Rows of requests flagged on the device
+ *           are not written.
  * topk_cnt  device int32 [B*max_qo_len][num_kv_heads] OUT, nullable.
- * Other arguments as in verify_attention_sparse; max_pages <= 1024.
+ * Other arguments as in verify_attention_sparse; max_pages <= 4096.
  */
 int32_t verify_attention_sparse_select(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                        const int32_t* kv_len, int32_t B, int32_t max_qo_len,

@@ -585,9 +585,6 @@ static int32_t sparse_attention(const void* q, int32_t q_dt, const int32_t* qo_i
     return fail(SDV_ERR_SHAPE, "top_k %d x max_qo_len %d outside [1, 512]", top_k, max_qo_len);
   if (max_pages < 1 || max_pages > 16384 || bt_stride < max_pages)
     return fail(SDV_ERR_SHAPE, "max_pages %d (<= 16384), bt_stride %d", max_pages, bt_stride);
-  if (scores && max_pages > sdv::kFusedTopkMaxPages)
-    return fail(SDV_ERR_SHAPE, "max_pages %d > %d for the in-kernel selection", max_pages,
-                sdv::kFusedTopkMaxPages);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
     return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
@@ -606,10 +603,14 @@ static int32_t sparse_attention(const void* q, int32_t q_dt, const int32_t* qo_i
   a.head_dim = kv->head_dim; a.kv_dt = kv->kv_dtype; a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale; a.softmax_scale = softmax_scale; a.num_splits = num_splits;
   a.out = out; a.out_dt = out_dt; a.dev_err = dev_err;
-  const bool select_in_kernel = scores && fam != 1 && fam != 2 && sdv::mfma_supported(a);
+  const bool select_in_kernel = scores && fam != 1 && fam != 2 && sdv::mfma_supported(a) &&
+                                max_pages <= sdv::kFusedTopkMaxPages;
   if (scores && !select_in_kernel && B > 0 && !topk_out)
-    return fail(SDV_ERR_NULL_POINTER, "the vector-ALU and register-prefetch kernels need "
-                "topk_idx to hold the selection");
+    return fail(SDV_ERR_NULL_POINTER, "topk_idx must hold the selection: the vector-ALU and "
+                "register-prefetch kernels, and tables over %d pages, select in a launch of its own",
+                sdv::kFusedTopkMaxPages);
+  if (scores && !select_in_kernel && max_pages > 4096)
+    return fail(SDV_ERR_SHAPE, "max_pages %d > 4096 for the page selection", max_pages);
   if (B == 0) return ok();
   hipError_t e;
   if (scores && !select_in_kernel) {

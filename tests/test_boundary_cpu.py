@@ -208,6 +208,29 @@ def test_sparse_rejections():
     assert _sparse(_kv(), B=0) == L.SDV_OK
 
 
+def _select(kv, **kw):
+    a = dict(q=FAKE, q_dt=L.SDV_BF16, B=2, max_qo=4, Hq=16, max_pages=8, bt=8, scores=FAKE, k=2,
+             idx=FAKE, splits=1, out=FAKE, out_dt=L.SDV_BF16)
+    a.update(kw)
+    return L.load().verify_attention_sparse_select(
+        a["q"], a["q_dt"], FAKE, FAKE, a["B"], a["max_qo"], a["Hq"], C.byref(kv), FAKE,
+        a["max_pages"], a["bt"], a["scores"], a["k"], a["idx"], None, 0.088, a["splits"], None, 0,
+        a["out"], a["out_dt"], None, None)
+
+
+def test_select_rejections():
+    # (every case fails on the host before a launch)
+    assert _select(_kv(), scores=None) == L.SDV_ERR_NULL_POINTER
+    assert _select(_kv(), q_dt=L.SDV_F32) == L.SDV_ERR_DTYPE
+    assert _select(_kv(), k=200) == L.SDV_ERR_SHAPE                # 4 x 200 > 512
+    # over 1024 pages the selection runs in a launch of its own into topk_idx ...
+    assert _select(_kv(), max_pages=2000, bt=2000, idx=None) == L.SDV_ERR_NULL_POINTER
+    # ... which takes up to 4096 pages
+    assert _select(_kv(), max_pages=5000, bt=5000) == L.SDV_ERR_SHAPE
+    assert _select(_kv(), splits=2) == L.SDV_ERR_WORKSPACE
+    assert _select(_kv(), B=0) == L.SDV_OK
+
+
 def _paged(kv, **kw):
     a = dict(q=FAKE, q_dt=L.SDV_BF16, B=2, max_qo=4, Hq=16, max_pages=8, bt=8, splits=1,
              out=FAKE, out_dt=L.SDV_BF16)

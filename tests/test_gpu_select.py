@@ -102,6 +102,29 @@ def test_select_widest_table():
     assert ok, worst
 
 
+def test_select_over_1024_pages_selects_in_its_own_launch():
+    # 1100-page table: the selection runs as the standalone top-k into topk_idx, then the
+    # sparse attention over it; without topk_idx the call is refused on the host
+    w = W.LONG_FP8.scaled(name="pages_1100", batch=1, kv=("list", (140000,)), kv_capacity=140800,
+                          top_k=8, num_q_heads=4, num_kv_heads=1)
+    c = W.make_sparse_case(w)
+    run = SparseRun(c)
+    assert run.bt.shape[1] == 1100
+    scores = run.scores()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, idx, cnt = _select(run, scores, 2, dev_err=err)
+    torch.cuda.synchronize()
+    ref = sparse_oracle(c)
+    n = run.n
+    assert np.array_equal(idx[:n].cpu().numpy(), ref["topk"][:n].astype(np.int32))
+    assert np.array_equal(cnt[:n].cpu().numpy(), ref["count"][:n].astype(np.int32))
+    ok, worst = tol_ok(out_numpy(out[:n]), ref["out"], "bf16")
+    assert int(err.item()) == 0
+    assert ok, worst
+    with pytest.raises(sdv.SdvError):
+        _select(run, scores, 1, write=False)
+
+
 def test_select_top_k_beyond_valid_pages():
     # kv = 4, 128, 200 tokens: one or two valid pages, top_k = 8 -> -1 padding and
     # counts below top_k
@@ -141,10 +164,11 @@ def test_select_host_errors():
     with pytest.raises(sdv.SdvError):
         _select(run, scores, 1, write=False)
     sdv.set_kernel_family(0)
-    # more pages than the in-kernel selection takes
-    wide = torch.zeros(scores.shape[0], scores.shape[1], 1025, dtype=torch.float32, device=DEV)
-    bt = torch.zeros(run.bt.shape[0], 1025, dtype=torch.int32, device=DEV)
+    # more pages than any selection takes
+    wide = torch.zeros(scores.shape[0], scores.shape[1], 4097, dtype=torch.float32, device=DEV)
+    bt = torch.zeros(run.bt.shape[0], 4097, dtype=torch.int32, device=DEV)
+    idx = torch.zeros(scores.shape[0], scores.shape[1], 4, dtype=torch.int32, device=DEV)
     with pytest.raises(sdv.SdvError):
         sdv.verify_attention_sparse_select(run.q, run.qo_indptr, run.kv_len, run.kv, bt, wide,
                                            max_qo_len=run.max_qo, top_k=4,
-                                           softmax_scale=c.softmax_scale)
+                                           softmax_scale=c.softmax_scale, topk_idx=idx)
