@@ -726,10 +726,13 @@ def main():
                     torch.empty(wa.batch, dtype=torch.int32, device=dev),
                     torch.empty((wa.batch, wa.max_qo()), dtype=torch.int32, device=dev),
                     torch.empty(wa.batch, dtype=torch.int32, device=dev))
+        acc_ws = torch.empty(sdv.greedy_accept_workspace_bytes(wa.batch, wa.max_qo(), ACCEPT_VOCAB,
+                                                               torch.bfloat16),
+                             dtype=torch.uint8, device=dev)
 
         def k_accept():
             sdv.greedy_accept(ac.logits, ac.tokens, ac.qo_indptr, ac.kv_len, max_qo_len=wa.max_qo(),
-                              outs=acc_outs)
+                              outs=acc_outs, workspace=acc_ws)
 
         msa, pera, _ = time_steps([("greedy_accept", k_accept)], args.steps, args.warmup, torch,
                                   flush)

@@ -406,21 +406,36 @@ int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_d
  * acceptance under greedy decoding, rate and mean length; PR #3 MSA verify commit —
  * the verify batch of qo_len = 1 + draft_len tokens.)
  *
- * logits       device [B*max_qo_len rows capacity][vocab], F32 or BF16, 16-byte
- *              aligned; vocab a multiple of 4 (F32) or 8 (BF16).
+ * logits       device [rows][vocab] (rows = qo_indptr[B] <= B*max_qo_len), F32 or BF16,
+ *              16-byte aligned; vocab a multiple of 4 (F32) or 8 (BF16).
  * tokens       device int32 [rows]: the verify input tokens.
- * targets_out  device int32 [B*max_qo_len]: argmax per row (rows past qo_indptr[B]
+ * workspace    device, >= sdv_greedy_accept_workspace_bytes(B, max_qo_len, vocab,
+ *              logits_dt) bytes, 4-byte aligned: each row's logits are reduced in
+ *              parts of 4096 (F32) or 8192 (BF16) values whose maxima and indices it
+ *              holds between the two launches.  Owned by the caller; contents on entry
+ *              ignored; calls that share it on different streams race.
+ * targets_out  device int32 [B*max_qo_len]: argmax per row, for the rows of every
+ *              request whose rows lie inside [0, qo_indptr[B]) (rows past qo_indptr[B]
  *              untouched).
  * accept_out   device int32 [B]: accepted drafts a (-1 for a request with unusable
- *              lengths, flagged SDV_DEVERR_QO_LEN).
+ *              lengths, flagged SDV_DEVERR_QO_LEN; rows reaching past qo_indptr[B] are
+ *              unusable too).
  * emitted_out  device int32 [B][max_qo_len]: the a + 1 emitted tokens, -1 padded.
  * new_kv_len_out device int32 [B]: kv_len - qo_len + 1 + a (kv_len when flagged).
+ * Errors: SDV_ERR_DTYPE (logits not F32/BF16), SDV_ERR_SHAPE (vocab, B, max_qo_len,
+ * alignment, or B*max_qo_len*parts beyond 2^31 - 1 workgroups), SDV_ERR_NULL_POINTER,
+ * SDV_ERR_WORKSPACE (workspace smaller than the size above).
  */
 int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
                       const int32_t* tokens, const int32_t* qo_indptr, const int32_t* kv_len,
-                      int32_t B, int32_t max_qo_len, int32_t* targets_out,
-                      int32_t* accept_out, int32_t* emitted_out, int32_t* new_kv_len_out,
-                      int32_t* dev_err, hipStream_t stream);
+                      int32_t B, int32_t max_qo_len, void* workspace, size_t workspace_bytes,
+                      int32_t* targets_out, int32_t* accept_out, int32_t* emitted_out,
+                      int32_t* new_kv_len_out, int32_t* dev_err, hipStream_t stream);
+
+/* Workspace bytes greedy_accept needs: B * max_qo_len * ceil(vocab / (1024 * values per
+ * 16 bytes)) * 8 (host only; 0 for arguments greedy_accept rejects). */
+size_t sdv_greedy_accept_workspace_bytes(int32_t B, int32_t max_qo_len, int32_t vocab,
+                                         int32_t logits_dt);
 
 /* One byte-range copy: dst_base[dst_offset ..) = src_base[src_offset ..), `bytes` long. */
 typedef struct sdv_copy_desc {

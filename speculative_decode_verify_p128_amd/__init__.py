@@ -2,7 +2,7 @@
 C ABI, see include/sdv.h).  The PyTorch binding passes tensors' device pointers and
 the current stream; nothing here computes on the host."""
 from .api import (PagedKV, SubpageView, alloc_workspace, copy_descriptors, dtype_code, fill_u32,
-                  greedy_accept, hnd_head_slice_descriptors,
+                  greedy_accept, greedy_accept_workspace_bytes, hnd_head_slice_descriptors,
                   kv_subpage_view_init, ladder_topk_pages, lse_combine, proxy_page_scores,
                   read_probe, set_kernel_family, stage_verify_kv_paged, stage_verify_kv_view,
                   verify_attention_dense, verify_attention_dense_view, verify_attention_paged,
@@ -12,7 +12,7 @@ from ._lib import LIB_PATH, SdvError, load
 
 __all__ = [
     "PagedKV", "SubpageView", "alloc_workspace", "copy_descriptors", "dtype_code", "fill_u32",
-    "greedy_accept", "hnd_head_slice_descriptors",
+    "greedy_accept", "greedy_accept_workspace_bytes", "hnd_head_slice_descriptors",
     "kv_subpage_view_init", "ladder_topk_pages", "lse_combine", "proxy_page_scores", "read_probe",
     "set_kernel_family", "stage_verify_kv_paged", "stage_verify_kv_view",
     "verify_attention_dense", "verify_attention_dense_view", "verify_attention_paged",

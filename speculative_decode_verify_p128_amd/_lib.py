@@ -86,7 +86,8 @@ SIGNATURES = {
     "hnd_head_slice_descriptors": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I,
                                         _P]),
     "copy_descriptors": (_I, [_P, _S, _P, _S, _P, _I, _P, _P]),
-    "greedy_accept": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "greedy_accept": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _S, _P, _P, _P, _P, _P, _P]),
+    "sdv_greedy_accept_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "lse_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "sdv_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "sdv_status_string": (C.c_char_p, [_I]),

@@ -360,26 +360,36 @@ def copy_descriptors(src: torch.Tensor, dst: torch.Tensor, descs: torch.Tensor, 
         _ptr(descs), descs.shape[0], _ptr(dev_err), _stream(dst.device)))
 
 
+def greedy_accept_workspace_bytes(B: int, max_qo_len: int, vocab: int, dtype) -> int:
+    return int(L.load().sdv_greedy_accept_workspace_bytes(B, max_qo_len, vocab, dtype_code(dtype)))
+
+
 def greedy_accept(logits: torch.Tensor, tokens: torch.Tensor, qo_indptr: torch.Tensor,
                   kv_len: torch.Tensor, *, max_qo_len: int,
-                  dev_err: Optional[torch.Tensor] = None, outs=None):
+                  dev_err: Optional[torch.Tensor] = None, outs=None,
+                  workspace: Optional[torch.Tensor] = None):
     """Returns (targets [B*max_qo_len], accept [B], emitted [B, max_qo_len], new_kv_len [B]);
-    `outs` may pass those four int32 tensors preallocated.  Target rows past
-    qo_indptr[B] are left as they were."""
+    `outs` may pass those four int32 tensors preallocated, `workspace` a byte tensor of
+    greedy_accept_workspace_bytes(...) or more.  Target rows past qo_indptr[B] are left
+    as they were."""
     _need(logits, "logits")
     _need(tokens, "tokens", torch.int32)
     B = kv_len.numel()
     dev = logits.device
+    vocab = logits.shape[-1]
     if outs is None:
         outs = (torch.empty(B * max_qo_len, dtype=torch.int32, device=dev),
                 torch.empty(B, dtype=torch.int32, device=dev),
                 torch.empty((B, max_qo_len), dtype=torch.int32, device=dev),
                 torch.empty(B, dtype=torch.int32, device=dev))
+    if workspace is None:
+        need = greedy_accept_workspace_bytes(B, max_qo_len, vocab, logits.dtype)
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
     targets, accept, emitted, new_kv = outs
     L.check(L.load().greedy_accept(
-        _ptr(logits), dtype_code(logits.dtype), logits.shape[-1], _ptr(tokens), _ptr(qo_indptr),
-        _ptr(kv_len), B, max_qo_len, _ptr(targets), _ptr(accept), _ptr(emitted), _ptr(new_kv),
-        _ptr(dev_err), _stream(dev)))
+        _ptr(logits), dtype_code(logits.dtype), vocab, _ptr(tokens), _ptr(qo_indptr),
+        _ptr(kv_len), B, max_qo_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(targets), _ptr(accept), _ptr(emitted), _ptr(new_kv), _ptr(dev_err), _stream(dev)))
     return targets, accept, emitted, new_kv
 
 

@@ -190,11 +190,15 @@ hipError_t launch_copy_descriptors(const void* src, size_t src_bytes, void* dst,
                                   const sdv_copy_desc* descs, int32_t n, int32_t* dev_err,
                                   hipStream_t s);
 
+// Parts of 1024 16-byte vectors per logits row; the workspace holds a float and an int32
+// per (row, part) of B * max_qo_len rows.
+int32_t greedy_accept_parts(int32_t vocab, int32_t logits_dt);
 hipError_t launch_greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
                                 const int32_t* tokens, const int32_t* qo_indptr,
                                 const int32_t* kv_len, int32_t B, int32_t max_qo_len,
-                                int32_t* targets, int32_t* accept, int32_t* emitted,
-                                int32_t* new_kv_len, int32_t* dev_err, hipStream_t s);
+                                void* workspace, int32_t* targets, int32_t* accept,
+                                int32_t* emitted, int32_t* new_kv_len, int32_t* dev_err,
+                                hipStream_t s);
 
 hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,

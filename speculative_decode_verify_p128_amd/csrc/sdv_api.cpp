@@ -470,11 +470,19 @@ int32_t copy_descriptors(const void* src_base, size_t src_bytes, void* dst_base,
                     "copy_descriptors launch");
 }
 
+size_t sdv_greedy_accept_workspace_bytes(int32_t B, int32_t max_qo_len, int32_t vocab,
+                                     int32_t logits_dt) {
+  if (B < 0 || max_qo_len < 1 || vocab < 1 || (logits_dt != SDV_F32 && logits_dt != SDV_BF16))
+    return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(max_qo_len) *
+         static_cast<size_t>(sdv::greedy_accept_parts(vocab, logits_dt)) * 8u;
+}
+
 int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
                       const int32_t* tokens, const int32_t* qo_indptr, const int32_t* kv_len,
-                      int32_t B, int32_t max_qo_len, int32_t* targets_out, int32_t* accept_out,
-                      int32_t* emitted_out, int32_t* new_kv_len_out, int32_t* dev_err,
-                      hipStream_t stream) {
+                      int32_t B, int32_t max_qo_len, void* workspace, size_t workspace_bytes,
+                      int32_t* targets_out, int32_t* accept_out, int32_t* emitted_out,
+                      int32_t* new_kv_len_out, int32_t* dev_err, hipStream_t stream) {
   if (logits_dt != SDV_F32 && logits_dt != SDV_BF16)
     return fail(SDV_ERR_DTYPE, "logits dtype %d (supported: F32, BF16)", logits_dt);
   const int per = logits_dt == SDV_F32 ? 4 : 8;
@@ -482,15 +490,25 @@ int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
     return fail(SDV_ERR_SHAPE, "vocab %d must be a positive multiple of %d", vocab, per);
   if (B < 0 || max_qo_len < 1 || static_cast<int64_t>(B) * max_qo_len > INT32_MAX)
     return fail(SDV_ERR_SHAPE, "B %d, max_qo_len %d", B, max_qo_len);
+  const int64_t wgs = static_cast<int64_t>(B) * max_qo_len * sdv::greedy_accept_parts(vocab, logits_dt);
+  if (wgs > INT32_MAX)
+    return fail(SDV_ERR_SHAPE, "B * max_qo_len * ceil(vocab / %d) = %lld exceeds the grid limit",
+                per * 1024, static_cast<long long>(wgs));
   if (B == 0) return ok();
-  if (!logits || !tokens || !qo_indptr || !kv_len || !targets_out || !accept_out ||
+  if (!logits || !tokens || !qo_indptr || !kv_len || !workspace || !targets_out || !accept_out ||
       !emitted_out || !new_kv_len_out)
     return fail(SDV_ERR_NULL_POINTER, "every array argument but dev_err must be non-null");
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
     return fail(SDV_ERR_SHAPE, "logits must be 16-byte aligned");
+  const size_t need = sdv_greedy_accept_workspace_bytes(B, max_qo_len, vocab, logits_dt);
+  if (workspace_bytes < need)
+    return fail(SDV_ERR_WORKSPACE, "workspace holds %zu bytes, the call needs %zu",
+                workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+    return fail(SDV_ERR_SHAPE, "workspace must be 4-byte aligned");
   return hip_status(sdv::launch_greedy_accept(logits, logits_dt, vocab, tokens, qo_indptr, kv_len,
-                                              B, max_qo_len, targets_out, accept_out, emitted_out,
-                                              new_kv_len_out, dev_err, stream),
+                                              B, max_qo_len, workspace, targets_out, accept_out,
+                                              emitted_out, new_kv_len_out, dev_err, stream),
                     "greedy_accept launch");
 }
 

@@ -252,15 +252,32 @@ def test_paged_rejections():
     assert _paged(_kv(), B=0) == L.SDV_OK
 
 
+def test_greedy_accept_workspace_bytes():
+    lib = L.load()
+    ws = lib.sdv_greedy_accept_workspace_bytes
+    # one part per 1024 16-byte vectors: 8192 bf16 or 4096 f32 logits; 8 bytes per (row, part)
+    assert ws(64, 4, 131072, L.SDV_BF16) == 64 * 4 * 16 * 8
+    assert ws(64, 4, 131072, L.SDV_F32) == 64 * 4 * 32 * 8
+    assert ws(3, 2, 8200, L.SDV_BF16) == 3 * 2 * 2 * 8
+    assert ws(3, 2, 8, L.SDV_BF16) == 3 * 2 * 1 * 8
+    assert ws(0, 4, 1024, L.SDV_BF16) == 0
+    assert ws(2, 4, 1024, L.SDV_FP8_E4M3) == 0
+
+
 def test_greedy_accept_rejections():
     lib = L.load()
-    args = lambda dt, vocab, logits=FAKE, tokens=FAKE: (  # noqa: E731
-        logits, dt, vocab, tokens, FAKE, FAKE, 2, 4, FAKE, FAKE, FAKE, FAKE, None, None)
+    big = 1 << 20
+    args = lambda dt, vocab, logits=FAKE, tokens=FAKE, ws=FAKE, wsb=big: (  # noqa: E731
+        logits, dt, vocab, tokens, FAKE, FAKE, 2, 4, ws, wsb, FAKE, FAKE, FAKE, FAKE, None, None)
     assert lib.greedy_accept(*args(L.SDV_FP8_E4M3, 1024)) == L.SDV_ERR_DTYPE
     assert lib.greedy_accept(*args(L.SDV_BF16, 1020)) == L.SDV_ERR_SHAPE     # not a multiple of 8
     assert lib.greedy_accept(*args(L.SDV_F32, 0)) == L.SDV_ERR_SHAPE
     assert lib.greedy_accept(*args(L.SDV_BF16, 1024, tokens=None)) == L.SDV_ERR_NULL_POINTER
+    assert lib.greedy_accept(*args(L.SDV_BF16, 1024, ws=None)) == L.SDV_ERR_NULL_POINTER
     assert lib.greedy_accept(*args(L.SDV_BF16, 1024, logits=C.c_void_p(0x10008))) == L.SDV_ERR_SHAPE
+    # 2 requests x 4 rows x 2 parts x 8 bytes = 128
+    assert lib.greedy_accept(*args(L.SDV_BF16, 16384, wsb=127)) == L.SDV_ERR_WORKSPACE
+    assert lib.greedy_accept(*args(L.SDV_BF16, 16384, ws=C.c_void_p(0x10002))) == L.SDV_ERR_SHAPE
 
 
 def test_combine_and_helpers():

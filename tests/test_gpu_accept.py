@@ -1,6 +1,8 @@
 """GPU parity of greedy acceptance against the oracle, bit for bit (integer outputs):
 bf16 and f32 logits, rows with two equal maxima and with NaN, ragged qo_len including
-decode rows, the full benchmark vocabulary on sampled requests, and the length flag."""
+decode rows, vocabularies that span several row parts (ragged last part, equal maxima in
+different parts, NaN-only parts), the full benchmark vocabulary on sampled requests, a
+reused workspace, and the length flag."""
 import numpy as np
 import pytest
 import torch
@@ -45,6 +47,76 @@ def test_accept_bit_exact(w, dt):
     assert np.array_equal(em[:, :ref["emitted"].shape[1]], ref["emitted"])
     assert np.all(em[:, ref["emitted"].shape[1]:] == -1)
     assert np.array_equal(new_kv.cpu().numpy(), ref["new_kv"])
+
+
+def _check(c, out):
+    targets, accept, emitted, new_kv = out
+    ref = oracle.greedy_accept_case(c.logits.float().numpy(), c.tokens.numpy(),
+                                    c.qo_indptr.numpy(), c.lengths.kv)
+    n = c.lengths.total_q
+    assert np.array_equal(targets[:n].cpu().numpy(), ref["targets"])
+    assert np.array_equal(accept.cpu().numpy(), ref["accept"])
+    em = emitted.cpu().numpy()
+    assert np.array_equal(em[:, :ref["emitted"].shape[1]], ref["emitted"])
+    assert np.all(em[:, ref["emitted"].shape[1]:] == -1)
+    assert np.array_equal(new_kv.cpu().numpy(), ref["new_kv"])
+    return ref
+
+
+@pytest.mark.parametrize("dt,vocab", [(torch.bfloat16, 3 * 8192 + 8), (torch.float32, 2 * 4096 + 4),
+                                      (torch.bfloat16, 8192), (torch.float32, 3 * 4096 - 4)],
+                         ids=["bf16_ragged_part", "f32_ragged_part", "bf16_one_part", "f32_3parts"])
+def test_accept_several_parts(dt, vocab):
+    w = W.RAGGED_MIXED.scaled(name="accept_parts", batch=24)
+    c = W.make_accept_case(w, vocab, dtype=dt, tie_rows=0.3, nan_rows=0.2)
+    x = c.logits
+    per_part = 8192 if dt == torch.bfloat16 else 4096
+    parts = -(-vocab // per_part)
+    # hand-made rows: equal maxima in the last and the first part (the first wins), in two
+    # later parts, an all-NaN row, an all -inf row, NaN everywhere but the last part, a
+    # maximum in the one-vector tail
+    big = 50.0
+    x[0, :] = 0.0
+    x[0, vocab - 3] = big
+    x[0, 5] = big
+    if parts > 2:
+        x[1, :] = -1.0
+        x[1, 2 * per_part + 1] = big
+        x[1, per_part + 7] = big
+    x[2, :] = float("nan")
+    x[3, :] = float("-inf")
+    x[4, :] = float("nan")
+    x[4, (parts - 1) * per_part:] = -2.0
+    x[4, vocab - 1] = -1.5
+    x[5, :] = -3.0
+    x[5, vocab - 1] = 4.0
+    out = _run(c, w.max_qo())
+    torch.cuda.synchronize()
+    ref = _check(c, out)
+    assert ref["targets"][0] == 5 and ref["targets"][2] == -1 and ref["targets"][3] == 0
+    assert ref["targets"][4] == vocab - 1 and ref["targets"][5] == vocab - 1
+    if parts > 2:
+        assert ref["targets"][1] == per_part + 7
+
+
+def test_accept_reused_workspace_smaller_second_call():
+    """One workspace and output set serve two calls in a row, the second with fewer
+    requests and a smaller vocabulary: stale part results of the first call must not
+    leak into the second."""
+    w1 = W.RAGGED_MIXED.scaled(name="accept_ws1", batch=32)
+    c1 = W.make_accept_case(w1, 4 * 8192, tie_rows=0.2, nan_rows=0.1)
+    need = sdv.greedy_accept_workspace_bytes(w1.batch, w1.max_qo(), 4 * 8192, torch.bfloat16)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    out1 = sdv.greedy_accept(c1.logits.to(DEV), c1.tokens.to(DEV), c1.qo_indptr.to(DEV),
+                             c1.kv_len.to(DEV), max_qo_len=w1.max_qo(), workspace=ws)
+    torch.cuda.synchronize()
+    _check(c1, out1)
+    w2 = W.RAGGED_MIXED.scaled(name="accept_ws2", batch=5)
+    c2 = W.make_accept_case(w2, 8192 + 64, tie_rows=0.2, nan_rows=0.1)
+    out2 = sdv.greedy_accept(c2.logits.to(DEV), c2.tokens.to(DEV), c2.qo_indptr.to(DEV),
+                             c2.kv_len.to(DEV), max_qo_len=w2.max_qo(), workspace=ws)
+    torch.cuda.synchronize()
+    _check(c2, out2)
 
 
 def test_accept_full_vocab_sampled():
