@@ -405,6 +405,27 @@ def attainable_read_gbs(torch, sdv, dev, gib=4):
     return best
 
 
+def units_read_gbs(torch, sdv, dev, base, units, unit_bytes, flush, reps=5):
+    """Best cold rate of the unit-list probe over a kernel's own gather list."""
+    best = 0.0
+    nbytes = units.numel() * unit_bytes
+    for blocks in (1024, 2048, 4096):
+        sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+        tot = 0.0
+        for it in range(reps + 1):
+            if flush:
+                flush()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            sdv.read_units_probe(base, units, unit_bytes, sink, blocks)
+            e.record()
+            torch.cuda.synchronize()
+            if it:
+                tot += s.elapsed_time(e)
+        best = max(best, nbytes / (tot / reps * 1e-3) / 1e9)
+    return best
+
+
 def calibrate_copy(torch, mib=1024, reps=3):
     """A plain device copy of known size, for scaling the memory counters."""
     src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
@@ -615,6 +636,27 @@ def main():
                          "traffic": load_traffic("verify_attention_dense_view", wd.name,
                                                  source_hash(*KERNEL_SOURCES["verify_attention_dense_view"]))},
         }
+        if not args.no_probe:
+            # what the call's own access pattern attains: the K and V runs (8 KiB each) of
+            # every block it reads, streamed once by the unit-list probe, cold
+            k_view()
+            torch.cuda.synchronize()
+            o_ = offs.cpu().numpy()
+            unit = wd.head_dim * 2 * 32
+            root = d.pool[wd.root_page]
+            shift = root.data_ptr() - d.pool.data_ptr()
+            assert shift % unit == 0
+            lst = []
+            for r_ in range(wd.batch):
+                nb_ = (int(d.lengths.kv[r_]) + 31) // 32
+                for h_ in range(wd.num_kv_heads):
+                    lst.append(o_[r_, 0, :nb_].astype(np.int64) * wd.num_kv_heads + h_)
+                    lst.append(o_[r_, 1, :nb_].astype(np.int64) * wd.num_kv_heads + h_)
+            units_d = torch.from_numpy(np.concatenate(lst) + shift // unit).to(dev)
+            result["dense"]["attainable_read_GB_s"] = units_read_gbs(
+                torch, sdv, dev, d.pool, units_d, unit, flush)
+            result["dense"]["frac_of_attainable"] = gbs / result["dense"]["attainable_read_GB_s"]
+            del units_d
         if args.dense_two_call:
             ms2, per2, _ = time_steps([("kv_subpage_view_init", k_view),
                                        ("verify_attention_dense", k_dense)],

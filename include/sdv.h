@@ -537,6 +537,16 @@ int32_t sdv_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t stre
 int32_t sdv_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
                        hipStream_t stream);
 
+/* Measurement helper: read a list of equal units once — unit u is the unit_bytes (4096,
+ * 8192 or 16384) bytes at base + u * unit_bytes; units (device int64 [n_units]) outside
+ * the base_bytes of memory at base are skipped — with `blocks` workgroups of 256
+ * threads, four units in flight per workgroup; sink (device, >= blocks words) gets an
+ * XOR fold.  Given a kernel's own gather list (say the K and V runs of every block a
+ * dense call reads), its rate is the attainable bandwidth of that access pattern. */
+int32_t sdv_read_units_probe(const void* base, size_t base_bytes, const int64_t* units,
+                             int64_t n_units, int32_t unit_bytes, uint32_t* sink, int32_t blocks,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,7 @@ SIGNATURES = {
     "sdv_set_kernel_family": (_I, [_I]),
     "sdv_fill_u32": (_I, [_P, _S, C.c_uint32, _P]),
     "sdv_read_probe": (_I, [_P, _S, _P, _I, _P]),
+    "sdv_read_units_probe": (_I, [_P, _S, _P, C.c_int64, _I, _P, _I, _P]),
 }
 
 _lib = None

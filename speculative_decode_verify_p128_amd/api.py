@@ -421,6 +421,15 @@ def fill_u32(dst: torch.Tensor, pattern: int = 0) -> None:
                                   _stream(dst.device)))
 
 
+def read_units_probe(base: torch.Tensor, units: torch.Tensor, unit_bytes: int, sink: torch.Tensor,
+                     blocks: int) -> None:
+    """Streaming read of the listed unit_bytes units of base (measurement helper); units:
+    int64 device tensor of unit indices; sink: int32 [>= blocks]."""
+    L.check(L.load().sdv_read_units_probe(_ptr(base), base.numel() * base.element_size(), _ptr(units),
+                                          units.numel(), unit_bytes, _ptr(sink), blocks,
+                                          _stream(base.device)))
+
+
 def read_probe(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
     """Streaming read of all of src (measurement helper); sink: int32 [>= blocks]."""
     L.check(L.load().sdv_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),

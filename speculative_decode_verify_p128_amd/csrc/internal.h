@@ -201,6 +201,9 @@ hipError_t launch_greedy_accept(const void* logits, int32_t logits_dt, int32_t v
                                 hipStream_t s);
 
 hipError_t launch_fill_u32(void* dst, size_t bytes, uint32_t pattern, hipStream_t s);
+hipError_t launch_read_units_probe(const void* base, const int64_t* units, int64_t n_units,
+                                   int64_t max_units, int32_t unit_bytes, uint32_t* sink,
+                                   int32_t blocks, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
                              hipStream_t s);
 

@@ -175,6 +175,47 @@ __global__ void __launch_bounds__(256) sdv_read_probe_kernel(const uint4* __rest
   if ((threadIdx.x & (kWave - 1)) == 0) atomicXor(sink + blockIdx.x, acc);
 }
 
+// Streaming read of a list of equal units (4, 8 or 16 KiB, unit u at base + u * bytes):
+// workgroup g takes units g, g + grid, ...; a unit is 256 threads x 1-4 16-byte loads,
+// four units in flight per workgroup.  Units outside [0, max_units) are skipped.
+__global__ void __launch_bounds__(256) sdv_read_units_probe_kernel(
+    const char* __restrict__ base, const int64_t* __restrict__ units, int64_t n_units,
+    int64_t max_units, int32_t unit_bytes, uint32_t* __restrict__ sink) {
+  constexpr int kInFlight = 4;
+  const int per = unit_bytes / (256 * 16);
+  uint32_t acc = 0;
+  const int64_t grid = gridDim.x;
+  for (int64_t u0 = blockIdx.x; u0 < n_units; u0 += kInFlight * grid) {
+    uint4 v[kInFlight][4];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      const int64_t i = u0 + k * grid;
+      const int64_t u = i < n_units ? units[i] : -1;
+      const bool ok = u >= 0 && u < max_units;
+      const char* p = base + (ok ? u : 0) * unit_bytes;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[k][j] = ok && j < per ? probe_load(reinterpret_cast<const uint4*>(p) + j * 256 + threadIdx.x)
+                                : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc ^= v[k][j].x ^ v[k][j].y ^ v[k][j].z ^ v[k][j].w;
+  }
+  for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicXor(sink + blockIdx.x, acc);
+}
+
+hipError_t launch_read_units_probe(const void* base, const int64_t* units, int64_t n_units,
+                                   int64_t max_units, int32_t unit_bytes, uint32_t* sink,
+                                   int32_t blocks, hipStream_t s) {
+  if (n_units == 0) return hipSuccess;
+  hipLaunchKernelGGL(sdv_read_units_probe_kernel, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const char*>(base), units, n_units, max_units, unit_bytes, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
                              hipStream_t s) {
   const int64_t n16 = static_cast<int64_t>(bytes / 16);

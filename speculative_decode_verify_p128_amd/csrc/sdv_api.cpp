@@ -724,4 +724,20 @@ int32_t sdv_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t bl
                     "sdv_read_probe launch");
 }
 
+int32_t sdv_read_units_probe(const void* base, size_t base_bytes, const int64_t* units,
+                             int64_t n_units, int32_t unit_bytes, uint32_t* sink, int32_t blocks,
+                             hipStream_t stream) {
+  if (n_units == 0) return ok();
+  if (!base || !units || !sink) return fail(SDV_ERR_NULL_POINTER, "base, units and sink must be non-null");
+  if (unit_bytes != 4096 && unit_bytes != 8192 && unit_bytes != 16384)
+    return fail(SDV_ERR_SHAPE, "unit_bytes %d (4096, 8192 or 16384)", unit_bytes);
+  if (n_units < 0 || reinterpret_cast<uintptr_t>(base) % 16 != 0)
+    return fail(SDV_ERR_SHAPE, "n_units %lld, base alignment", static_cast<long long>(n_units));
+  if (blocks < 1 || blocks > (1 << 20)) return fail(SDV_ERR_SHAPE, "blocks %d", blocks);
+  return hip_status(sdv::launch_read_units_probe(base, units, n_units,
+                                                 static_cast<int64_t>(base_bytes / unit_bytes),
+                                                 unit_bytes, sink, blocks, stream),
+                    "sdv_read_units_probe launch");
+}
+
 }  // extern "C"

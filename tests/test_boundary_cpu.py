@@ -280,6 +280,16 @@ def test_greedy_accept_rejections():
     assert lib.greedy_accept(*args(L.SDV_BF16, 16384, ws=C.c_void_p(0x10002))) == L.SDV_ERR_SHAPE
 
 
+def test_read_units_probe_rejections():
+    lib = L.load()
+    f = lib.sdv_read_units_probe
+    assert f(FAKE, 1 << 20, FAKE, 0, 8192, FAKE, 64, None) == L.SDV_OK          # nothing to read
+    assert f(None, 1 << 20, FAKE, 4, 8192, FAKE, 64, None) == L.SDV_ERR_NULL_POINTER
+    assert f(FAKE, 1 << 20, FAKE, 4, 1000, FAKE, 64, None) == L.SDV_ERR_SHAPE
+    assert f(FAKE, 1 << 20, FAKE, 4, 8192, FAKE, 0, None) == L.SDV_ERR_SHAPE
+    assert f(C.c_void_p(0x10008), 1 << 20, FAKE, 4, 8192, FAKE, 64, None) == L.SDV_ERR_SHAPE
+
+
 def test_combine_and_helpers():
     lib = L.load()
     assert lib.lse_combine(FAKE, FAKE, 0, 4, 4, 128, FAKE, 0, None, None) == L.SDV_ERR_SHAPE
