@@ -405,10 +405,11 @@ def attainable_read_gbs(torch, sdv, dev, gib=4):
     return best
 
 
-def units_read_gbs(torch, sdv, dev, base, units, unit_bytes, flush, reps=5):
-    """Best cold rate of the unit-list probe over a kernel's own gather list."""
+def units_read_gbs(torch, sdv, dev, lists, flush, reps=5):
+    """Best cold rate of the unit-list probe over a kernel's own gather list, given as
+    (base tensor, int64 unit indices, unit bytes) per buffer, read back to back."""
     best = 0.0
-    nbytes = units.numel() * unit_bytes
+    nbytes = sum(u.numel() * ub for _, u, ub in lists)
     for blocks in (1024, 2048, 4096):
         sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
         tot = 0.0
@@ -417,13 +418,38 @@ def units_read_gbs(torch, sdv, dev, base, units, unit_bytes, flush, reps=5):
                 flush()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
-            sdv.read_units_probe(base, units, unit_bytes, sink, blocks)
+            for base, units, unit_bytes in lists:
+                sdv.read_units_probe(base, units, unit_bytes, sink, blocks)
             e.record()
             torch.cuda.synchronize()
             if it:
                 tot += s.elapsed_time(e)
         best = max(best, nbytes / (tot / reps * 1e-3) / 1e9)
     return best
+
+
+def sparse_gather_units(case, idx_np, torch, dev):
+    """The proxy's gather list (K of every valid page of every (request, KV head)) and the
+    sparse attention's (K and V of the pages any token of the pair chose), as 16 KiB
+    units of the head-major P128 pools (a page's head is two units)."""
+    w = case.w
+    Hkv = w.num_kv_heads
+    bt = case.block_table.cpu().numpy()
+    ind = case.qo_indptr.cpu().numpy()
+    assert w.head_dim * 2 * 128 == 2 * 16384 and case.k_pool.is_contiguous()
+    proxy, sel = [], []
+    for r in range(w.batch):
+        n = (int(case.lengths.kv[r]) + 127) // 128
+        phys = bt[r, :n].astype(np.int64)
+        for h in range(Hkv):
+            for half in (0, 1):
+                proxy.append((phys * Hkv + h) * 2 + half)
+            chosen = np.unique(idx_np[ind[r]:ind[r + 1], h, :])
+            chosen = chosen[chosen >= 0]
+            for half in (0, 1):
+                sel.append((bt[r, chosen].astype(np.int64) * Hkv + h) * 2 + half)
+    t = lambda a: torch.from_numpy(np.concatenate(a)).to(dev)  # noqa: E731
+    return t(proxy), t(sel)
 
 
 def calibrate_copy(torch, mib=1024, reps=3):
@@ -579,6 +605,17 @@ def main():
         "cache": ("warm: consecutive steps, no eviction" if args.warm else
                   "cold: a 1 GiB fill before every step (untimed) evicts L2 and the Infinity Cache"),
     }
+    if not args.no_probe:
+        # what the two kernels' own access patterns attain: their gather lists streamed
+        # once by the unit-list probe, cold
+        pu, su = sparse_gather_units(c, idx_np, torch, dev)
+        att = {"proxy_page_scores": units_read_gbs(torch, sdv, dev, [(c.k_pool, pu, 16384)], flush),
+               "verify_attention_sparse_select": units_read_gbs(
+                   torch, sdv, dev, [(c.k_pool, su, 16384), (c.v_pool, su, 16384)], flush)}
+        for name, gbs_att in att.items():
+            kern[name]["attainable_read_GB_s"] = gbs_att
+            kern[name]["frac_of_attainable"] = kern[name]["GB_s"] / gbs_att
+        del pu, su
     del scores, ws
 
     # ---- dense draft-layer path ----
@@ -654,7 +691,7 @@ def main():
                     lst.append(o_[r_, 1, :nb_].astype(np.int64) * wd.num_kv_heads + h_)
             units_d = torch.from_numpy(np.concatenate(lst) + shift // unit).to(dev)
             result["dense"]["attainable_read_GB_s"] = units_read_gbs(
-                torch, sdv, dev, d.pool, units_d, unit, flush)
+                torch, sdv, dev, [(d.pool, units_d, unit)], flush)
             result["dense"]["frac_of_attainable"] = gbs / result["dense"]["attainable_read_GB_s"]
             del units_d
         if args.dense_two_call:
