@@ -76,3 +76,35 @@ def test_sparse_full_size_sampled(w):
     rows = rows_of(c, req)
     ok, worst = tol_ok(o_np[rows], ref["out"][rows], "bf16")
     assert ok, worst
+
+
+@pytest.mark.parametrize("w", [W.SPARSE_BF16, W.LONG_FP8, W.RAGGED_MIXED], ids=lambda w: w.name)
+def test_select_full_size_sampled(w):
+    """The benchmark's sparse step (proxy scores, then selection + attention in one
+    launch) at full size and the workload's split count: its selection (written out) is
+    the oracle's on sampled requests and its output within tolerance."""
+    print(f"\n[gpu] fused select full {w.name}", flush=True)
+    c = W.make_sparse_case(w, device=DEV)
+    run = SparseRun(c)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    scores = run.scores(dev_err=err)
+    rows_cap = w.batch * w.max_qo()
+    idx = torch.full((rows_cap, w.num_kv_heads, w.top_k), -7, dtype=torch.int32, device=DEV)
+    out = sdv.verify_attention_sparse_select(run.q, run.qo_indptr, run.kv_len, run.kv, run.bt,
+                                             scores, max_qo_len=run.max_qo, top_k=w.top_k,
+                                             softmax_scale=c.softmax_scale,
+                                             num_splits=w.num_splits, topk_idx=idx, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    i_np, o_np = idx.cpu().numpy(), out_numpy(out[:run.n])
+    del run, scores, idx, out
+    c = _to_cpu(c)
+    req = _sample(c.lengths.kv, 2, 7)
+    ref = sparse_oracle(c, requests=req)
+    ind = c.qo_indptr.numpy()
+    for r in req:
+        a, b = ind[r], ind[r + 1]
+        assert np.array_equal(i_np[a:b], ref["topk"][a:b].astype(np.int32)), f"topk r={r}"
+    rows = rows_of(c, req)
+    ok, worst = tol_ok(o_np[rows], ref["out"][rows], "bf16")
+    assert ok, worst
