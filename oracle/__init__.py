@@ -41,15 +41,15 @@ from .attention import attend, dense_verify_request, sparse_verify_request, lse_
 from .proxy import proxy_scores_request, canonical_dot_f32
 from .topk import ladder_topk_request
 from .accept import greedy_accept_case, greedy_accept_request, greedy_argmax
-from .pipeline import (dense_verify_case, sparse_verify_case, paged_verify_case, dense_rows,
-                       sparse_rows, request_kv_dense, request_kv_sparse)
+from .pipeline import (dense_verify_case, sparse_verify_case, paged_verify_case,
+                       request_kv_dense, request_kv_sparse)
 
 __all__ = [
     "ladder_bounds", "n_valid_pages", "decode_e4m3fn", "decode_bf16", "decode_store",
     "subpage_offsets", "gather_subpage_view", "gather_hnd", "head_slice_contiguous",
     "head_slice_grouped", "head_slice_descriptors", "attend", "dense_verify_request", "sparse_verify_request",
     "lse_combine", "proxy_scores_request", "canonical_dot_f32", "ladder_topk_request",
-    "dense_verify_case", "sparse_verify_case", "paged_verify_case", "dense_rows", "sparse_rows",
+    "dense_verify_case", "sparse_verify_case", "paged_verify_case",
     "request_kv_dense", "request_kv_sparse", "greedy_argmax", "greedy_accept_request",
     "greedy_accept_case",
 ]

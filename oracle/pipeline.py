@@ -14,12 +14,10 @@ import numpy as np
 
 from .attention import dense_verify_request, sparse_verify_request
 from .fp8 import decode_store
-from .ladder import ladder_bounds, n_valid_pages
 from .proxy import proxy_scores_request
 from .topk import ladder_topk_request
 from .view import gather_hnd, gather_subpage_view, subpage_offsets
 
-PAGE = 128
 
 
 def _q_values(q_raw, q_dtype):
@@ -57,11 +55,6 @@ def dense_verify_case(q_raw, q_dtype, qo_indptr, kv_len, pool_flat_raw, kv_dtype
                                         v.astype(np.float64) * v_scale, int(kv_len[r]),
                                         softmax_scale)
     return out
-
-
-def dense_rows(*args, **kwargs):
-    """Alias of dense_verify_case for sampled requests (kept for call-site clarity)."""
-    return dense_verify_case(*args, **kwargs)
 
 
 def paged_verify_case(q_raw, q_dtype, qo_indptr, kv_len, k_pool_raw, v_pool_raw, kv_dtype,
@@ -111,19 +104,3 @@ def sparse_verify_case(q_raw, q_dtype, qo_indptr, kv_len, k_pool_raw, v_pool_raw
         out[a:b] = sparse_verify_request(q[a:b].astype(np.float64), k.astype(np.float64) * k_scale,
                                          v.astype(np.float64) * v_scale, kvr, idx, softmax_scale)
     return {"scores": scores, "topk": topk, "count": count, "out": out}
-
-
-def sparse_rows(*args, **kwargs):
-    """Alias of sparse_verify_case for sampled requests."""
-    return sparse_verify_case(*args, **kwargs)
-
-
-def ladder_table(qo_indptr, kv_len, page=PAGE):
-    """(bound, n_valid) per query row, for checks of device-side ladder metadata."""
-    bounds, nv = [], []
-    for r in range(len(kv_len)):
-        qo = int(qo_indptr[r + 1] - qo_indptr[r])
-        bd = ladder_bounds(int(kv_len[r]), qo)
-        bounds.append(bd)
-        nv.append(n_valid_pages(bd, page))
-    return np.concatenate(bounds), np.concatenate(nv)
