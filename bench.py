@@ -42,8 +42,9 @@ def parse():
     p.add_argument("--splits", type=int, default=None, help="override sparse num_splits")
     p.add_argument("--dense-splits", type=int, default=None)
     p.add_argument("--family", type=int, default=0,
-                   help="attention kernels: 0 auto, 1 vector-ALU, 2 register-streaming MFMA, "
-                        "3 per-wave LDS stream, 4 workgroup LDS ring")
+                   help="attention kernels (through the cross-check library when nonzero): "
+                        "0 default, 1 vector-ALU, 3 per-wave LDS stream, 4 workgroup LDS ring, "
+                        "5 persistent per-wave, 6 persistent ring")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-paged", action="store_true")
     p.add_argument("--paged-splits", type=int, default=None)
@@ -59,6 +60,11 @@ def parse():
     p.add_argument("--dense-two-call", action="store_true",
                    help="also time the draft-layer step as two calls (view offsets, then "
                         "attention over them), reported under dense.two_call")
+    p.add_argument("--no-extra-configs", action="store_true",
+                   help="skip the long-context fp8 and ragged-batch lines")
+    p.add_argument("--only", default=None,
+                   help="comma list of sections to run (sparse, dense, paged, long_fp8, ragged, "
+                        "staging, transfer, accept); the headline sparse line always runs")
     p.add_argument("--no-unfused", action="store_true",
                    help="skip timing the three-launch step (proxy, standalone top-k, sparse "
                         "attention over its indices) reported under 'unfused'")
@@ -452,6 +458,98 @@ def sparse_gather_units(case, idx_np, torch, dev):
     return t(proxy), t(sel)
 
 
+def sparse_config_line(torch, sdv, W, w, dev, args, flush, fam):
+    """The sparse target-layer step (proxy scores, then top-k + sparse attention in one
+    launch, + the split-KV combine) on workload w: tokens/s, per-kernel times and
+    algorithmic GB/s."""
+    c = W.make_sparse_case(w, device=dev)
+    kv = sdv.PagedKV(c.k_pool, c.v_pool, c.k_scale, c.v_scale)
+    mq = w.max_qo()
+    rows_cap = w.batch * mq
+    q = torch.zeros((rows_cap, w.num_q_heads, w.head_dim), dtype=c.q.dtype, device=dev)
+    q[:c.q.shape[0]] = c.q
+    scores = torch.empty((rows_cap, w.num_kv_heads, w.max_pages()), dtype=torch.float32, device=dev)
+    idx = torch.empty((rows_cap, w.num_kv_heads, w.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((rows_cap, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, w.num_splits, dev, op="sparse")
+
+    def k_proxy():
+        sdv.proxy_page_scores(q, c.qo_indptr, c.kv_len, kv, c.block_table, max_qo_len=mq,
+                              scores=scores)
+
+    def k_select():
+        sdv.verify_attention_sparse_select(q, c.qo_indptr, c.kv_len, kv, c.block_table, scores,
+                                           max_qo_len=mq, top_k=w.top_k,
+                                           softmax_scale=c.softmax_scale,
+                                           num_splits=w.num_splits, workspace=ws, out=out,
+                                           family=fam)
+
+    fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
+    ms, per, _ = time_steps(fns, args.steps, args.warmup, torch, flush)
+    # the selection, written out once after timing, sizes the algorithmic bytes
+    sdv.ladder_topk_pages(scores, c.qo_indptr, c.kv_len, max_qo_len=mq, top_k=w.top_k,
+                          topk_idx=idx)
+    torch.cuda.synchronize()
+    ab = sparse_algorithmic_bytes(c, idx.cpu().numpy())
+    kern = {}
+    for name, key in (("proxy_page_scores", "proxy"), ("verify_attention_sparse_select", "select")):
+        gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
+        kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
+                      "frac_of_peak": gbs / HBM_PEAK_GBS,
+                      "traffic": load_traffic(name, w.name, source_hash(*KERNEL_SOURCES[name]))}
+    path = ab["proxy"] + ab["select"]
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    tokens = c.lengths.total_q
+    res = {"value": tokens / (ms * 1e-3), "unit": "verify tokens/s", "ms_per_step": ms,
+           "verify_tokens": tokens, "kv_tokens": int(c.lengths.kv.sum()),
+           "num_splits": w.num_splits, "path_algorithmic_bytes": path,
+           "gb_per_s": path / (ms * 1e-3) / 1e9,
+           "frac_of_peak": path / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_s"],
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
+                        "traffic": kern[dom]["traffic"]},
+           "kernels": kern}
+    del c, kv, q, scores, idx, out, ws
+    return res
+
+
+def dense_config_line(torch, sdv, W, w, dev, args, flush, fam, splits=None):
+    """The dense draft-layer step through the P32 view (page indices computed in the
+    attention launch, + the split-KV combine) on workload w."""
+    splits = splits or w.num_splits
+    d = W.make_dense_case(w, device=dev)
+    mq = w.max_qo()
+    rows_cap = w.batch * mq
+    q = torch.zeros((rows_cap, w.num_q_heads, w.head_dim), dtype=d.q.dtype, device=dev)
+    q[:d.q.shape[0]] = d.q
+    out = torch.empty((rows_cap, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, splits, dev)
+    view, _ = sdv.kv_subpage_view_init(
+        d.pool[w.root_page], d.block_table, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+        slot_stride=w.slot_stride, num_slots=d.num_slots, k_scale=d.k_scale, v_scale=d.v_scale,
+        pool_index_scale=w.pool_index_scale, stage_offsets=False)
+
+    def k_dview():
+        sdv.verify_attention_dense_view(q, d.qo_indptr, d.kv_len, view, d.block_table,
+                                        max_qo_len=mq, softmax_scale=d.softmax_scale,
+                                        num_splits=splits, workspace=ws, out=out, family=fam)
+
+    name = "verify_attention_dense_view"
+    ms, per, _ = time_steps([(name, k_dview)], args.steps, args.warmup, torch, flush)
+    db = dense_algorithmic_bytes(d)
+    gbs = db / (per[name]["avg_us"] * 1e-6) / 1e9
+    tokens = d.lengths.total_q
+    res = {"value": tokens / (ms * 1e-3), "unit": "verify tokens/s", "ms_per_step": ms,
+           "verify_tokens": tokens, "kv_tokens": int(d.lengths.kv.sum()), "num_splits": splits,
+           "algorithmic_bytes": db, "kernels": per,
+           "roofline": {"bound": "hbm", "kernel": name, "achieved": gbs, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": load_traffic(name, w.name, source_hash(*KERNEL_SOURCES[name]))}}
+    del d, q, out, ws, view
+    return res
+
+
 def calibrate_copy(torch, mib=1024, reps=3):
     """A plain device copy of known size, for scaling the memory counters."""
     src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
@@ -482,7 +580,12 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch)
         return
-    sdv.set_kernel_family(args.family)
+    fam = args.family
+    only = set(args.only.split(",")) if args.only else None
+
+    def want(section, disabled=False):
+        return (section in only) if only is not None else not disabled
+
     flush = None
     if not args.warm:
         flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -499,7 +602,7 @@ def main():
     scores = torch.empty((rows_cap, w.num_kv_heads, w.max_pages()), dtype=torch.float32, device=dev)
     idx = torch.empty((rows_cap, w.num_kv_heads, w.top_k), dtype=torch.int32, device=dev)
     out = torch.empty((rows_cap, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, splits, dev)
+    ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, splits, dev, op="sparse")
     mq = w.max_qo()
 
     def k_proxy():
@@ -513,13 +616,13 @@ def main():
     def k_sparse():
         sdv.verify_attention_sparse(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, idx,
                                     max_qo_len=mq, softmax_scale=c.softmax_scale,
-                                    num_splits=splits, workspace=ws, out=out)
+                                    num_splits=splits, workspace=ws, out=out, family=fam)
 
     def k_select():
         sdv.verify_attention_sparse_select(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, scores,
                                            max_qo_len=mq, top_k=w.top_k,
                                            softmax_scale=c.softmax_scale, num_splits=splits,
-                                           workspace=ws, out=out)
+                                           workspace=ws, out=out, family=fam)
 
     fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
     launch_stats = {}
@@ -553,7 +656,7 @@ def main():
         kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
                       "frac_of_peak": gbs / HBM_PEAK_GBS}
     unfused = None
-    if not args.no_unfused:
+    if want("unfused", args.no_unfused):
         ufns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
                 ("verify_attention_sparse", k_sparse)]
         u_ms, u_per, _ = time_steps(ufns, args.steps, args.warmup, torch, flush)
@@ -619,7 +722,7 @@ def main():
     del scores, ws
 
     # ---- dense draft-layer path ----
-    if not args.no_dense:
+    if want("dense", args.no_dense):
         wd = W.DENSE_BF16
         dsplits = args.dense_splits or wd.num_splits
         d = W.make_dense_case(wd, device=dev)
@@ -636,7 +739,8 @@ def main():
         def k_dview():
             sdv.verify_attention_dense_view(d.q, d.qo_indptr, d.kv_len, view_only, d.block_table,
                                             max_qo_len=wd.max_qo(), softmax_scale=d.softmax_scale,
-                                            num_splits=dsplits, workspace=wsd, out=outd)
+                                            num_splits=dsplits, workspace=wsd, out=outd,
+                                            family=fam)
 
         def k_view():
             holder["view"], _ = sdv.kv_subpage_view_init(
@@ -647,7 +751,7 @@ def main():
         def k_dense():
             sdv.verify_attention_dense(d.q, d.qo_indptr, d.kv_len, holder["view"], offs,
                                        max_qo_len=wd.max_qo(), softmax_scale=d.softmax_scale,
-                                       num_splits=dsplits, workspace=wsd, out=outd)
+                                       num_splits=dsplits, workspace=wsd, out=outd, family=fam)
 
         # the step: the view's page indices computed inside the attention launch
         msd, perd, _ = time_steps([("verify_attention_dense_view", k_dview)],
@@ -702,20 +806,38 @@ def main():
                                            "algorithmic_bytes": dense_algorithmic_bytes(d, True)}
         del d, outd, wsd
 
+    # ---- long-context sparse verify with fp8 K/V, 16-way split-KV ----
+    if want("long_fp8", args.no_extra_configs):
+        result["long_fp8"] = {
+            "workload": "long_fp8: sparse verify, batch 8, qo_len 4, 16 q / 4 kv heads, head_dim "
+                        "128, kv_len 131072, fp8 e4m3 K/V with per-tensor scales, bf16 Q, top-k "
+                        "64, 16 splits",
+            **sparse_config_line(torch, sdv, W, W.LONG_FP8, dev, args, flush, fam)}
+
+    # ---- ragged mixed batch through both paths ----
+    if want("ragged", args.no_extra_configs):
+        wr = W.RAGGED_MIXED
+        result["ragged_mixed"] = {
+            "workload": "ragged_mixed: batch 256, qo_len 1..8, kv_len log-normal (median 2048, "
+                        "clipped [64, 65536]) with page-crossing rows, 16 q / 4 kv heads, "
+                        "head_dim 128, bf16, top-k 16 clamped",
+            "sparse": sparse_config_line(torch, sdv, W, wr, dev, args, flush, fam),
+            "dense": dense_config_line(torch, sdv, W, wr, dev, args, flush, fam)}
+
     # ---- target dense layers: ladder attention over ordinary head-major P128 pages ----
-    if not args.no_paged:
+    if want("paged", args.no_paged):
         wp = W.PAGED_BF16
         psplits = args.paged_splits or wp.num_splits
         pc = W.make_sparse_case(wp, device=dev)
         pkv = sdv.PagedKV(pc.k_pool, pc.v_pool, pc.k_scale, pc.v_scale)
         rows_p = wp.batch * wp.max_qo()
         outp = torch.empty((rows_p, wp.num_q_heads, wp.head_dim), dtype=torch.bfloat16, device=dev)
-        wsp = sdv.alloc_workspace(rows_p, wp.num_q_heads, wp.head_dim, psplits, dev)
+        wsp = sdv.alloc_workspace(rows_p, wp.num_q_heads, wp.head_dim, psplits, dev, op="paged")
 
         def k_paged():
             sdv.verify_attention_paged(pc.q, pc.qo_indptr, pc.kv_len, pkv, pc.block_table,
                                        max_qo_len=wp.max_qo(), softmax_scale=pc.softmax_scale,
-                                       num_splits=psplits, workspace=wsp, out=outp)
+                                       num_splits=psplits, workspace=wsp, out=outp, family=fam)
 
         msp, perp, _ = time_steps([("verify_attention_paged", k_paged)], args.steps, args.warmup,
                                   torch, flush)
@@ -735,7 +857,7 @@ def main():
         del pc, pkv, outp, wsp
 
     # ---- ladder KV slot staging of the verify tokens (the step before the path) ----
-    if not args.no_paged:
+    if want("staging", args.no_paged):
         ws_ = W.PAGED_BF16
         sc = W.make_sparse_case(ws_, device=dev)
         rows_s = sc.lengths.total_q
@@ -762,7 +884,7 @@ def main():
         del sc, skv, kn, vn
 
     # ---- grouped head-major head-slice transfer of the draft layer (two TP ranks -> one) ----
-    if not args.no_dense:
+    if want("transfer", args.no_dense):
         wt = W.DENSE_BF16
         dc = W.make_dense_case(wt, device=dev)
         H, per = wt.num_kv_heads, wt.num_kv_heads // 2
@@ -798,7 +920,7 @@ def main():
         del dc, senders, recv, descs
 
     # ---- greedy acceptance after the verify step (target argmax vs draft tokens) ----
-    if not args.no_paged:
+    if want("accept", args.no_paged):
         wa = W.SPARSE_BF16
         ac = W.make_accept_case(wa, ACCEPT_VOCAB, device=dev)
         acc_outs = (torch.empty(wa.batch * wa.max_qo(), dtype=torch.int32, device=dev),

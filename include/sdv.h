@@ -172,11 +172,12 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
  *              sub-pages over all (request, KV head) pairs divided by the workgroups
  *              the GPU holds at once (so long and short requests balance), at least
  *              ceil(longest request's sub-pages / num_splits) and at most 1024; the
- *              other kernels take C = ceil(max_sub_pages / num_splits).
+ *              vector-ALU kernels take C = ceil(max_sub_pages / num_splits).
  *              Trailing splits of short requests are empty.  num_splits = 1 needs no
- *              workspace.
- * workspace    device, >= sdv_workspace_bytes(B*max_qo_len, num_q_heads, head_dim,
- *              num_splits) bytes (nullable when that is 0).
+ *              workspace.  A split holds at most 1024 sub-pages, so
+ *              ceil(max_sub_pages / num_splits) > 1024 is SDV_ERR_SHAPE.
+ * workspace    device, >= sdv_workspace_bytes(SDV_OP_VERIFY_DENSE, B*max_qo_len,
+ *              num_q_heads, head_dim, num_splits) bytes (nullable when that is 0).
  * out          device [rows][num_q_heads][head_dim], out_dt (F32 or BF16); 16-byte
  *              aligned.
  * Supported: q_dt F32 with F32 K/V; q_dt BF16 with BF16 or FP8 K/V; head_dim 64 or
@@ -498,33 +499,26 @@ int32_t lse_combine(const float* partial_out, const float* partial_lse, int32_t 
                     int32_t num_rows, int32_t num_heads, int32_t head_dim, void* out,
                     int32_t out_dt, float* lse_out, hipStream_t stream);
 
-/* Workspace (bytes) a split-KV attention call needs for q_rows_cap = B * max_qo_len
- * query rows; 0 when num_splits == 1. */
-size_t sdv_workspace_bytes(int32_t q_rows_cap, int32_t num_q_heads, int32_t head_dim,
-                           int32_t num_splits);
+/* Operations that take a split-KV workspace (sdv_workspace_bytes' op argument). */
+typedef enum sdv_op {
+  SDV_OP_VERIFY_DENSE = 1,    /* verify_attention_dense, verify_attention_dense_view   */
+  SDV_OP_VERIFY_SPARSE = 2,   /* verify_attention_sparse, verify_attention_sparse_select */
+  SDV_OP_VERIFY_PAGED = 3,    /* verify_attention_paged                                 */
+} sdv_op;
+
+/* Workspace (bytes) the attention call `op` needs for q_rows_cap = B * max_qo_len query
+ * rows and num_splits splits: the fp32 partial outputs [num_splits][q_rows_cap]
+ * [num_q_heads][head_dim] and their log-sum-exps [num_splits][q_rows_cap][num_q_heads],
+ * each padded to 256 bytes.  0 when num_splits == 1, for non-positive sizes, and for an
+ * op not listed in sdv_op (the call itself then rejects a missing workspace). */
+size_t sdv_workspace_bytes(int32_t op, int32_t q_rows_cap, int32_t num_q_heads,
+                           int32_t head_dim, int32_t num_splits);
 
 /* Static text for a status code. */
 const char* sdv_status_string(int32_t status);
 
 /* Message of the calling thread's most recent failed call ("" if none). */
 const char* sdv_last_error(void);
-
-/* Kernel family selection, for cross-checking: 0 = automatic (matrix-core kernels:
- * one LDS block stream per wave for sparse attention, the workgroup-shared LDS block
- * ring for dense attention; vector-ALU kernels for fp32), 1 = the vector-ALU kernels,
- * 2 = the matrix-core kernels that stream K/V through registers, 3 = the per-wave
- * LDS-stream kernels for both, 4 = the workgroup-shared LDS-ring kernels for both,
- * 5 = for dense attention with num_splits >= 2, the persistent per-wave kernel that
- * gives every workgroup an equal range of 32-token blocks over all (request, KV head)
- * pairs (split slots are then consecutive pieces of a pair; needs B <= 2048 and
- * ceil(block capacity / (num_splits - 1)) <= 1024, else as 0).  Automatic selection
- * uses it for verify_attention_paged when it applies, the per-wave kernel otherwise.
- * 6 = the same persistent partition over one workgroup-shared LDS ring per workgroup
- * that runs through the boundaries between (request, KV head) pieces (each piece's
- * query rows staged through LDS by the same asynchronous copies), for dense and paged
- * attention under the same conditions.
- * Process-wide; returns the previous value. */
-int32_t sdv_set_kernel_family(int32_t family);
 
 /* Measurement helper: fill `bytes` (multiple of 16) of device memory with a 32-bit
  * pattern — used to evict caches between timed runs. */

@@ -1,6 +1,8 @@
-"""ctypes declarations of libsdv.so (the C ABI in include/sdv.h).
+"""ctypes declarations of libsdv.so (the C ABI in include/sdv.h) and of the cross-check
+build libsdv_xcheck.so (the same library plus sdv_xcheck_* entry points that take the
+kernel family as an argument; the tests use it to run every kernel implementation).
 
-Loading fails loudly when the library has not been built: there is no fallback path.
+Loading fails loudly when a library has not been built: there is no fallback path.
 """
 from __future__ import annotations
 
@@ -9,6 +11,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdv.so")
+XCHECK_LIB_PATH = os.path.join(_HERE, "libsdv_xcheck.so")
 
 SDV_OK = 0
 SDV_ERR_NULL_POINTER = 1
@@ -21,6 +24,17 @@ SDV_ERR_HIP = 6
 SDV_F32 = 0
 SDV_BF16 = 1
 SDV_FP8_E4M3 = 2
+
+SDV_OP_VERIFY_DENSE = 1
+SDV_OP_VERIFY_SPARSE = 2
+SDV_OP_VERIFY_PAGED = 3
+
+# Kernel families of the cross-check entry points: 0 = the default kernel for the
+# arguments; 1 = vector-ALU kernels; 3 = one LDS block stream per wave; 4 = the
+# workgroup-shared LDS block ring; 5 = the persistent equal-range partition with the
+# per-wave body (dense and paged, num_splits >= 2); 6 = the same partition over one ring
+# per workgroup.  A family that does not serve a call runs the default kernel.
+FAMILY_AUTO, FAMILY_VALU, FAMILY_WAVES, FAMILY_RING, FAMILY_PERSIST, FAMILY_FLAT = 0, 1, 3, 4, 5, 6
 
 DEVERR_QO_LEN = 1
 DEVERR_KV_CAPACITY = 2
@@ -89,32 +103,52 @@ SIGNATURES = {
     "greedy_accept": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _S, _P, _P, _P, _P, _P, _P]),
     "sdv_greedy_accept_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "lse_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
-    "sdv_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "sdv_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "sdv_status_string": (C.c_char_p, [_I]),
     "sdv_last_error": (C.c_char_p, []),
-    "sdv_set_kernel_family": (_I, [_I]),
     "sdv_fill_u32": (_I, [_P, _S, C.c_uint32, _P]),
     "sdv_read_probe": (_I, [_P, _S, _P, _I, _P]),
     "sdv_read_units_probe": (_I, [_P, _S, _P, C.c_int64, _I, _P, _I, _P]),
 }
 
+# The cross-check build's extra entry points: the attention calls with a leading family.
+XCHECK_SIGNATURES = {
+    f"sdv_xcheck_{name}": (SIGNATURES[name][0], [_I, *SIGNATURES[name][1]])
+    for name in ("verify_attention_dense", "verify_attention_dense_view",
+                 "verify_attention_sparse", "verify_attention_sparse_select",
+                 "verify_attention_paged")
+}
+
 _lib = None
+_xlib = None
+
+
+def _open(path: str, signatures) -> C.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc, gfx950); there is no fallback implementation")
+    lib = C.CDLL(path)
+    for name, (res, args) in signatures.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
 
 
 def load() -> C.CDLL:
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "(hipcc, gfx950); there is no fallback implementation")
-        lib = C.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = _open(LIB_PATH, SIGNATURES)
     return _lib
+
+
+def load_xcheck() -> C.CDLL:
+    """The cross-check build (raises if it has not been built)."""
+    global _xlib
+    if _xlib is None:
+        _xlib = _open(XCHECK_LIB_PATH, {**SIGNATURES, **XCHECK_SIGNATURES})
+    return _xlib
 
 
 class SdvError(RuntimeError):
@@ -124,7 +158,7 @@ class SdvError(RuntimeError):
         self.message = message
 
 
-def check(status: int) -> None:
+def check(status: int, lib: C.CDLL = None) -> None:
     if status != SDV_OK:
-        lib = load()
+        lib = lib or load()
         raise SdvError(status, lib.sdv_last_error().decode() or lib.sdv_status_string(status).decode())

@@ -1,6 +1,11 @@
-"""Builds libsdv.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Builds libsdv.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and the
+cross-check library libsdv_xcheck.so that the GPU tests load beside it.
 
-Each source compiles to its own object under _build/ (in parallel), then one link.
+Each source compiles to its own object under _build/ (in parallel).  The C-ABI source
+compiles twice: as is for libsdv.so, and with SDV_XCHECK for libsdv_xcheck.so, whose
+extra sdv_xcheck_* entry points take the kernel family as an argument so that the tests
+can run every kernel implementation on the same inputs.  Both libraries link the same
+kernel objects.
 """
 from __future__ import annotations
 
@@ -15,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsdv.so")
+XCHECK_LIB = os.path.join(PKG, "libsdv_xcheck.so")
+API_SOURCE = "sdv_api.cpp"
 ARCH = "gfx950"
 
 COMMON = [
@@ -46,10 +53,11 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src,
-           "-o", obj]
+def _compile(job, verbose: bool) -> str:
+    src, defines, suffix = job
+    obj = os.path.join(BUILD, os.path.basename(src) + suffix + ".o")
+    cmd = [hipcc(), *COMMON, *defines, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c",
+           src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
@@ -60,17 +68,29 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build_library(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False, jobs: int = 8) -> str:
+    """Builds both libraries; returns the product library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs_list = [(s, [], "") for s in srcs]
+    api = [s for s in srcs if os.path.basename(s) == API_SOURCE]
+    jobs_list += [(s, ["-DSDV_XCHECK"], ".xcheck") for s in api]
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(jobs_list))) as ex:
+        objs = list(ex.map(lambda j: _compile(j, verbose), jobs_list))
+    plain = objs[:len(srcs)]
+    xobj = objs[len(srcs):]
+    kernels = [o for s, o in zip(srcs, plain) if os.path.basename(s) != API_SOURCE]
+    _link(plain, LIB)
+    _link(kernels + xobj, XCHECK_LIB)
     return LIB
 
 

@@ -134,14 +134,22 @@ hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int3
 hipError_t launch_attn_dense_valu(const AttnArgs& a, const DenseSource& src, hipStream_t s);
 hipError_t launch_attn_sparse_valu(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 
-// Matrix-core attention kernels (bf16 Q; bf16 or fp8 K/V; head_dim 64/128).
-bool mfma_supported(const AttnArgs& a);
-hipError_t launch_attn_dense_mfma(const AttnArgs& a, const DenseSource& src, hipStream_t s);
-hipError_t launch_attn_sparse_mfma(const AttnArgs& a, const SparseSource& src, hipStream_t s);
+// Whether the matrix-core attention kernels serve a call: bf16 Q with bf16 or fp8 K/V,
+// head_dim 64 or 128, at most 64 query rows (G x max_qo_len) per (request, KV head),
+// 16-byte aligned q and out.
+inline bool mfma_supported(const AttnArgs& a) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.q) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(a.out) % 16 == 0);
+  return a.q_dt == SDV_BF16 && (a.kv_dt == SDV_BF16 || a.kv_dt == SDV_FP8_E4M3) &&
+         (a.head_dim == 64 || a.head_dim == 128) &&
+         a.max_qo_len * (a.num_q_heads / a.num_kv_heads) <= 64 && aligned;
+}
 
-// Matrix-core attention with an LDS block ring fed by asynchronous global->LDS copies
-// (same support as the kernels above; dense needs at most 1024 blocks per split).
-constexpr int kStreamMaxDenseBlocks = 1024;
+// 32-token blocks one split of a dense call may hold (the block list a workgroup stages);
+// the host rejects calls whose capacity over num_splits exceeds it.
+constexpr int kMaxSplitBlocks = 1024;
+
+// Matrix-core attention with an LDS block ring fed by asynchronous global->LDS copies.
 hipError_t launch_attn_dense_stream(const AttnArgs& a, const DenseSource& src, hipStream_t s);
 hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s);
 

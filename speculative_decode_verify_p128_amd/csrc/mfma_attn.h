@@ -248,7 +248,7 @@ struct BlockCopier {
   }
 };
 
-constexpr int kMaxDenseBlocks = 1024;   // 32-token blocks per dense split
+constexpr int kMaxDenseBlocks = kMaxSplitBlocks;   // 32-token blocks per dense split
 
 // f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
 template <int N, int I = 0, typename F>

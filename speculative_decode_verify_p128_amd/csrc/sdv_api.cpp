@@ -1,8 +1,12 @@
 // C ABI of the verify-attention library: argument validation (host only, before any
-// HIP call), workspace layout, kernel-family dispatch and status reporting.
+// HIP call), workspace layout, kernel dispatch and status reporting.
+//
+// The library keeps no state between calls (the last-error text is per thread and only
+// reports).  Each attention entry point runs the default kernel for its arguments; the
+// cross-check build (compiled with SDV_XCHECK, a separate test library) adds
+// sdv_xcheck_* entry points that take the kernel family as an argument of the call.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -13,7 +17,20 @@
 namespace {
 
 thread_local std::string g_last_error;
-std::atomic<int32_t> g_family{0};
+
+// Kernel families (cross-check build only; the product entry points always pass
+// kFamilyAuto).
+constexpr int32_t kFamilyAuto = 0;      // the default kernel for the arguments
+constexpr int32_t kFamilyValu = 1;      // vector-ALU kernels
+constexpr int32_t kFamilyWaves = 3;     // one LDS block stream per wave
+constexpr int32_t kFamilyRing = 4;      // workgroup-shared LDS block ring
+constexpr int32_t kFamilyPersist = 5;   // persistent equal-range partition, per-wave body
+constexpr int32_t kFamilyFlat = 6;      // persistent equal-range partition, one ring
+
+[[maybe_unused]] bool valid_family(int32_t f) {
+  return f == kFamilyAuto || f == kFamilyValu || f == kFamilyWaves || f == kFamilyRing ||
+         f == kFamilyPersist || f == kFamilyFlat;
+}
 
 int32_t fail(int32_t status, const char* fmt, ...) {
   char buf[512];
@@ -69,12 +86,12 @@ int32_t check_query_side(const void* q, const int32_t* qo_indptr, const int32_t*
   return SDV_OK;
 }
 
-int32_t check_workspace(void* workspace, size_t workspace_bytes, int64_t rows_cap,
+int32_t check_workspace(int32_t op, void* workspace, size_t workspace_bytes, int64_t rows_cap,
                         int32_t num_q_heads, int32_t head_dim, int32_t num_splits) {
   if (num_splits < 1 || num_splits > 4096)
     return fail(SDV_ERR_SHAPE, "num_splits %d outside [1, 4096]", num_splits);
-  const size_t need = sdv_workspace_bytes(static_cast<int32_t>(rows_cap), num_q_heads, head_dim,
-                                          num_splits);
+  const size_t need = sdv_workspace_bytes(op, static_cast<int32_t>(rows_cap), num_q_heads,
+                                          head_dim, num_splits);
   if (need > 0) {
     if (!workspace) return fail(SDV_ERR_WORKSPACE, "workspace of %zu bytes required, got null", need);
     if (workspace_bytes < need)
@@ -102,8 +119,10 @@ void split_workspace(void* workspace, int64_t rows_cap, int32_t num_q_heads, int
 
 extern "C" {
 
-size_t sdv_workspace_bytes(int32_t q_rows_cap, int32_t num_q_heads, int32_t head_dim,
-                           int32_t num_splits) {
+size_t sdv_workspace_bytes(int32_t op, int32_t q_rows_cap, int32_t num_q_heads,
+                           int32_t head_dim, int32_t num_splits) {
+  if (op != SDV_OP_VERIFY_DENSE && op != SDV_OP_VERIFY_SPARSE && op != SDV_OP_VERIFY_PAGED)
+    return 0;
   if (num_splits <= 1 || q_rows_cap <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   const size_t units = static_cast<size_t>(num_splits) * q_rows_cap * num_q_heads;
   return align256(units * head_dim * sizeof(float)) + align256(units * sizeof(float));
@@ -123,10 +142,6 @@ const char* sdv_status_string(int32_t status) {
 }
 
 const char* sdv_last_error(void) { return g_last_error.c_str(); }
-
-int32_t sdv_set_kernel_family(int32_t family) {
-  return g_family.exchange(family >= 0 && family <= 6 ? family : 0);
-}
 
 int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_table,
                              int32_t B, int32_t max_blocks, int32_t bt_stride,
@@ -203,7 +218,8 @@ static int32_t dense_attention(const void* q, int32_t q_dt, const int32_t* qo_in
                                const int32_t* block_table, int32_t bt_stride,
                                float softmax_scale, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, void* out, int32_t out_dt,
-                               int32_t* dev_err, hipStream_t stream, const char* name) {
+                               int32_t* dev_err, hipStream_t stream, const char* name,
+                               int32_t fam) {
   if (!view) return fail(SDV_ERR_NULL_POINTER, "view must be non-null");
   const sdv_subpage_view& v = *view;
   int32_t st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, v.num_kv_heads);
@@ -216,13 +232,19 @@ static int32_t dense_attention(const void* q, int32_t q_dt, const int32_t* qo_in
   if (static_cast<int64_t>(G) * max_qo_len > 64)
     return fail(SDV_ERR_SHAPE, "group %d x max_qo_len %d exceeds 64 query rows", G, max_qo_len);
   if (max_sub_pages < 1) return fail(SDV_ERR_SHAPE, "max_sub_pages %d < 1", max_sub_pages);
+  if (num_splits >= 1 &&
+      (static_cast<int64_t>(max_sub_pages) + num_splits - 1) / num_splits > sdv::kMaxSplitBlocks)
+    return fail(SDV_ERR_SHAPE, "num_splits %d too small: each split may hold at most %d "
+                "32-token blocks of the %d-sub-page capacity", num_splits, sdv::kMaxSplitBlocks,
+                max_sub_pages);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
     return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (!valid_scale(v.k_scale) || !valid_scale(v.v_scale) || !v.k_root || v.num_sub_pages < 8)
     return fail(SDV_ERR_GEOMETRY, "native P128 draft view unavailable: view not initialised");
   const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
   if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
-  st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, v.head_dim, num_splits);
+  st = check_workspace(SDV_OP_VERIFY_DENSE, workspace, workspace_bytes, rows_cap, num_q_heads,
+                       v.head_dim, num_splits);
   if (st) return st;
   if (B > 0 && ((!sub_offsets && !block_table) || !out))
     return fail(SDV_ERR_NULL_POINTER, "%s and out must be non-null",
@@ -240,18 +262,15 @@ static int32_t dense_attention(const void* q, int32_t q_dt, const int32_t* qo_in
   split_workspace(workspace, rows_cap, num_q_heads, v.head_dim, num_splits, &a.part_o, &a.part_lse);
   sdv::DenseSource src{v.k_root, sub_offsets, max_sub_pages, v.num_sub_pages,
                        sub_offsets ? nullptr : block_table, bt_stride, v.index_scale, v.num_slots};
-  const int32_t fam = g_family.load();
-  const bool stream_ok =
-      (max_sub_pages + num_splits - 1) / num_splits <= sdv::kStreamMaxDenseBlocks;
   hipError_t e;
-  if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_dense_valu(a, src, stream);
-  else if (fam == 2 || !stream_ok) e = sdv::launch_attn_dense_mfma(a, src, stream);
-  else if (fam == 3) e = sdv::launch_attn_dense_waves(a, src, stream);
-  else if (fam == 5 && sdv::persist_supported(a, max_sub_pages))
+  if (fam == kFamilyValu || !sdv::mfma_supported(a)) e = sdv::launch_attn_dense_valu(a, src, stream);
+  else if (fam == kFamilyWaves) e = sdv::launch_attn_dense_waves(a, src, stream);
+  else if (fam == kFamilyPersist && sdv::persist_supported(a, max_sub_pages))
     e = sdv::launch_attn_dense_persist(a, src, stream);
-  else if (fam == 6 && sdv::persist_supported(a, max_sub_pages))
+  else if (fam == kFamilyFlat && sdv::persist_supported(a, max_sub_pages))
     e = sdv::launch_attn_dense_flat(a, src, stream);
-  else e = sdv::launch_attn_dense_stream(a, src, stream);   // 0 (automatic), 4, 5 and 6
+  else e = sdv::launch_attn_dense_stream(a, src, stream);   // automatic, ring, and the
+                                                            // persistent ones that do not apply
   if (e != hipSuccess) return hip_status(e, name);
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
@@ -264,6 +283,43 @@ static int32_t dense_attention(const void* q, int32_t q_dt, const int32_t* qo_in
 
 extern "C" {
 
+}  // extern "C"
+
+static int32_t dense_offsets_call(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                                  const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                                  int32_t num_q_heads, const sdv_subpage_view* view,
+                                  const int32_t* sub_offsets, int32_t max_sub_pages,
+                                  float softmax_scale, int32_t num_splits, void* workspace,
+                                  size_t workspace_bytes, void* out, int32_t out_dt,
+                                  int32_t* dev_err, hipStream_t stream, int32_t fam) {
+  if (B > 0 && !sub_offsets) return fail(SDV_ERR_NULL_POINTER, "sub_offsets must be non-null");
+  return dense_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                         sub_offsets, max_sub_pages, nullptr, 0, softmax_scale, num_splits,
+                         workspace, workspace_bytes, out, out_dt, dev_err, stream,
+                         "verify_attention_dense launch", fam);
+}
+
+static int32_t dense_view_call(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_subpage_view* view,
+                               const int32_t* block_table, int32_t max_blocks,
+                               int32_t bt_stride, float softmax_scale, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* out,
+                               int32_t out_dt, int32_t* dev_err, hipStream_t stream,
+                               int32_t fam) {
+  if (max_blocks < 1 || bt_stride < max_blocks)
+    return fail(SDV_ERR_SHAPE, "max_blocks %d, bt_stride %d", max_blocks, bt_stride);
+  if (static_cast<int64_t>(max_blocks) * 4 > INT32_MAX / 32)
+    return fail(SDV_ERR_SHAPE, "max_blocks %d too large", max_blocks);
+  if (B > 0 && !block_table) return fail(SDV_ERR_NULL_POINTER, "block_table must be non-null");
+  return dense_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view, nullptr,
+                         4 * max_blocks, block_table, bt_stride, softmax_scale, num_splits,
+                         workspace, workspace_bytes, out, out_dt, dev_err, stream,
+                         "verify_attention_dense_view launch", fam);
+}
+
+extern "C" {
+
 int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                int32_t num_q_heads, const sdv_subpage_view* view,
@@ -271,11 +327,9 @@ int32_t verify_attention_dense(const void* q, int32_t q_dt, const int32_t* qo_in
                                float softmax_scale, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, void* out, int32_t out_dt,
                                int32_t* dev_err, hipStream_t stream) {
-  if (B > 0 && !sub_offsets) return fail(SDV_ERR_NULL_POINTER, "sub_offsets must be non-null");
-  return dense_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
-                         sub_offsets, max_sub_pages, nullptr, 0, softmax_scale, num_splits,
-                         workspace, workspace_bytes, out, out_dt, dev_err, stream,
-                         "verify_attention_dense launch");
+  return dense_offsets_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                            sub_offsets, max_sub_pages, softmax_scale, num_splits, workspace,
+                            workspace_bytes, out, out_dt, dev_err, stream, kFamilyAuto);
 }
 
 int32_t verify_attention_dense_view(const void* q, int32_t q_dt, const int32_t* qo_indptr,
@@ -285,15 +339,9 @@ int32_t verify_attention_dense_view(const void* q, int32_t q_dt, const int32_t* 
                                     int32_t bt_stride, float softmax_scale, int32_t num_splits,
                                     void* workspace, size_t workspace_bytes, void* out,
                                     int32_t out_dt, int32_t* dev_err, hipStream_t stream) {
-  if (max_blocks < 1 || bt_stride < max_blocks)
-    return fail(SDV_ERR_SHAPE, "max_blocks %d, bt_stride %d", max_blocks, bt_stride);
-  if (static_cast<int64_t>(max_blocks) * 4 > INT32_MAX / 32)
-    return fail(SDV_ERR_SHAPE, "max_blocks %d too large", max_blocks);
-  if (B > 0 && !block_table) return fail(SDV_ERR_NULL_POINTER, "block_table must be non-null");
-  return dense_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view, nullptr,
-                         4 * max_blocks, block_table, bt_stride, softmax_scale, num_splits,
-                         workspace, workspace_bytes, out, out_dt, dev_err, stream,
-                         "verify_attention_dense_view launch");
+  return dense_view_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                         block_table, max_blocks, bt_stride, softmax_scale, num_splits,
+                         workspace, workspace_bytes, out, out_dt, dev_err, stream, kFamilyAuto);
 }
 
 static int32_t check_paged_kv(const sdv_paged_kv* kv) {
@@ -512,13 +560,15 @@ int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
                     "greedy_accept launch");
 }
 
-int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
-                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
-                               int32_t num_q_heads, const sdv_paged_kv* kv,
-                               const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
-                               float softmax_scale, int32_t num_splits, void* workspace,
-                               size_t workspace_bytes, void* out, int32_t out_dt,
-                               int32_t* dev_err, hipStream_t stream) {
+}  // extern "C"
+
+static int32_t paged_call(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                          const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                          int32_t num_q_heads, const sdv_paged_kv* kv,
+                          const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                          float softmax_scale, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* out, int32_t out_dt, int32_t* dev_err,
+                          hipStream_t stream, int32_t fam) {
   int32_t st = check_paged_kv(kv);
   if (st) return st;
   st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv->num_kv_heads);
@@ -533,15 +583,16 @@ int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_in
   if (max_qo_len > 32) return fail(SDV_ERR_SHAPE, "max_qo_len %d > 32", max_qo_len);
   if (max_pages < 1 || max_pages > (1 << 20) || bt_stride < max_pages)
     return fail(SDV_ERR_SHAPE, "max_pages %d (<= 2^20), bt_stride %d", max_pages, bt_stride);
-  if (num_splits < 1 || (4ll * max_pages + num_splits - 1) / num_splits > sdv::kStreamMaxDenseBlocks)
+  if (num_splits < 1 || (4ll * max_pages + num_splits - 1) / num_splits > sdv::kMaxSplitBlocks)
     return fail(SDV_ERR_SHAPE, "num_splits %d too small: each split may hold at most %d "
                 "32-token blocks of the %d-page capacity", num_splits,
-                sdv::kStreamMaxDenseBlocks, max_pages);
+                sdv::kMaxSplitBlocks, max_pages);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
     return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
   if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
-  st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, kv->head_dim, num_splits);
+  st = check_workspace(SDV_OP_VERIFY_PAGED, workspace, workspace_bytes, rows_cap, num_q_heads,
+                       kv->head_dim, num_splits);
   if (st) return st;
   if (B > 0 && (!block_table || !out))
     return fail(SDV_ERR_NULL_POINTER, "block_table and out must be non-null");
@@ -558,13 +609,12 @@ int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_in
   split_workspace(workspace, rows_cap, num_q_heads, kv->head_dim, num_splits, &a.part_o, &a.part_lse);
   sdv::SparseSource src{kv->k, kv->v, kv->page_stride, kv->num_pages, block_table, bt_stride,
                         max_pages, nullptr, 0};
-  const int32_t fam = g_family.load();
   hipError_t e;
-  if (fam == 4) e = sdv::launch_attn_paged_stream(a, src, stream);
-  else if (fam == 3 || !sdv::persist_supported(a, 4ll * max_pages))
+  if (fam == kFamilyRing) e = sdv::launch_attn_paged_stream(a, src, stream);
+  else if (fam == kFamilyWaves || !sdv::persist_supported(a, 4ll * max_pages))
     e = sdv::launch_attn_paged_waves(a, src, stream);
-  else if (fam == 6) e = sdv::launch_attn_paged_flat(a, src, stream);
-  else e = sdv::launch_attn_paged_persist(a, src, stream);   // 0 (automatic) and 5
+  else if (fam == kFamilyFlat) e = sdv::launch_attn_paged_flat(a, src, stream);
+  else e = sdv::launch_attn_paged_persist(a, src, stream);   // automatic and persistent
   if (e != hipSuccess) return hip_status(e, "verify_attention_paged launch");
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
@@ -573,6 +623,20 @@ int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_in
     if (e != hipSuccess) return hip_status(e, "verify_attention_paged combine launch");
   }
   return ok();
+}
+
+extern "C" {
+
+int32_t verify_attention_paged(const void* q, int32_t q_dt, const int32_t* qo_indptr,
+                               const int32_t* kv_len, int32_t B, int32_t max_qo_len,
+                               int32_t num_q_heads, const sdv_paged_kv* kv,
+                               const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+                               float softmax_scale, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, void* out, int32_t out_dt,
+                               int32_t* dev_err, hipStream_t stream) {
+  return paged_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
+                    max_pages, bt_stride, softmax_scale, num_splits, workspace, workspace_bytes,
+                    out, out_dt, dev_err, stream, kFamilyAuto);
 }
 
 }  // extern "C"
@@ -587,7 +651,7 @@ static int32_t sparse_attention(const void* q, int32_t q_dt, const int32_t* qo_i
                                 int32_t* cnt_out, int32_t top_k, float softmax_scale,
                                 int32_t num_splits, void* workspace, size_t workspace_bytes,
                                 void* out, int32_t out_dt, int32_t* dev_err, hipStream_t stream,
-                                const char* name) {
+                                const char* name, int32_t fam) {
   int32_t st = check_paged_kv(kv);
   if (st) return st;
   st = check_query_side(q, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv->num_kv_heads);
@@ -607,25 +671,25 @@ static int32_t sparse_attention(const void* q, int32_t q_dt, const int32_t* qo_i
     return fail(SDV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
   if (rows_cap > (1ll << 30)) return fail(SDV_ERR_SHAPE, "too many query rows");
-  st = check_workspace(workspace, workspace_bytes, rows_cap, num_q_heads, kv->head_dim, num_splits);
+  st = check_workspace(SDV_OP_VERIFY_SPARSE, workspace, workspace_bytes, rows_cap, num_q_heads,
+                       kv->head_dim, num_splits);
   if (st) return st;
   if (B > 0 && (!block_table || !out || (!scores && !topk_idx)))
     return fail(SDV_ERR_NULL_POINTER, "block_table, %s and out must be non-null",
                 scores ? "scores" : "topk_idx");
   if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return fail(SDV_ERR_SHAPE, "out must be 16-byte aligned");
-  const int32_t fam = g_family.load();
   sdv::AttnArgs a{};
   a.q = q; a.q_dt = q_dt; a.qo_indptr = qo_indptr; a.kv_len = kv_len; a.B = B;
   a.max_qo_len = max_qo_len; a.num_q_heads = num_q_heads; a.num_kv_heads = kv->num_kv_heads;
   a.head_dim = kv->head_dim; a.kv_dt = kv->kv_dtype; a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale; a.softmax_scale = softmax_scale; a.num_splits = num_splits;
   a.out = out; a.out_dt = out_dt; a.dev_err = dev_err;
-  const bool select_in_kernel = scores && fam != 1 && fam != 2 && sdv::mfma_supported(a) &&
+  const bool select_in_kernel = scores && fam != kFamilyValu && sdv::mfma_supported(a) &&
                                 max_pages <= sdv::kFusedTopkMaxPages;
   if (scores && !select_in_kernel && B > 0 && !topk_out)
-    return fail(SDV_ERR_NULL_POINTER, "topk_idx must hold the selection: the vector-ALU and "
-                "register-prefetch kernels, and tables over %d pages, select in a launch of its own",
+    return fail(SDV_ERR_NULL_POINTER, "topk_idx must hold the selection: the vector-ALU "
+                "kernels, and tables over %d pages, select in a launch of its own",
                 sdv::kFusedTopkMaxPages);
   if (scores && !select_in_kernel && max_pages > 4096)
     return fail(SDV_ERR_SHAPE, "max_pages %d > 4096 for the page selection", max_pages);
@@ -642,9 +706,8 @@ static int32_t sparse_attention(const void* q, int32_t q_dt, const int32_t* qo_i
   sdv::SparseSource src{kv->k, kv->v, kv->page_stride, kv->num_pages, block_table, bt_stride,
                         max_pages, select_in_kernel ? nullptr : topk_idx, top_k,
                         select_in_kernel ? scores : nullptr, topk_out, cnt_out};
-  if (fam == 1 || !sdv::mfma_supported(a)) e = sdv::launch_attn_sparse_valu(a, src, stream);
-  else if (fam == 2) e = sdv::launch_attn_sparse_mfma(a, src, stream);
-  else if (fam == 4) e = sdv::launch_attn_sparse_stream(a, src, stream);
+  if (fam == kFamilyValu || !sdv::mfma_supported(a)) e = sdv::launch_attn_sparse_valu(a, src, stream);
+  else if (fam == kFamilyRing) e = sdv::launch_attn_sparse_stream(a, src, stream);
   else e = sdv::launch_attn_sparse_waves(a, src, stream);
   if (e != hipSuccess) return hip_status(e, name);
   if (num_splits > 1) {
@@ -669,7 +732,7 @@ int32_t verify_attention_sparse(const void* q, int32_t q_dt, const int32_t* qo_i
   return sparse_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
                           max_pages, bt_stride, topk_idx, nullptr, nullptr, nullptr, top_k,
                           softmax_scale, num_splits, workspace, workspace_bytes, out, out_dt,
-                          dev_err, stream, "verify_attention_sparse launch");
+                          dev_err, stream, "verify_attention_sparse launch", kFamilyAuto);
 }
 
 int32_t verify_attention_sparse_select(const void* q, int32_t q_dt, const int32_t* qo_indptr,
@@ -685,7 +748,7 @@ int32_t verify_attention_sparse_select(const void* q, int32_t q_dt, const int32_
   return sparse_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
                           max_pages, bt_stride, nullptr, scores, topk_idx, topk_cnt, top_k,
                           softmax_scale, num_splits, workspace, workspace_bytes, out, out_dt,
-                          dev_err, stream, "verify_attention_sparse_select launch");
+                          dev_err, stream, "verify_attention_sparse_select launch", kFamilyAuto);
 }
 
 int32_t lse_combine(const float* partial_out, const float* partial_lse, int32_t num_splits,
@@ -741,3 +804,83 @@ int32_t sdv_read_units_probe(const void* base, size_t base_bytes, const int64_t*
 }
 
 }  // extern "C"
+
+#ifdef SDV_XCHECK
+// Cross-check build: the attention entry points with the kernel family as an argument of
+// the call (declared in tests' ctypes binding only; the product library does not export
+// them).  An unknown family is SDV_ERR_SHAPE; a family that does not serve the arguments
+// falls back to the default kernel, as documented per family in the test binding.
+extern "C" {
+
+#define SDV_XCHECK_FAMILY()                                                            \
+  if (!valid_family(family)) return fail(SDV_ERR_SHAPE, "kernel family %d", family);
+
+int32_t sdv_xcheck_verify_attention_dense(
+    int32_t family, const void* q, int32_t q_dt, const int32_t* qo_indptr,
+    const int32_t* kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+    const sdv_subpage_view* view, const int32_t* sub_offsets, int32_t max_sub_pages,
+    float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* out,
+    int32_t out_dt, int32_t* dev_err, hipStream_t stream) {
+  SDV_XCHECK_FAMILY()
+  return dense_offsets_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                            sub_offsets, max_sub_pages, softmax_scale, num_splits, workspace,
+                            workspace_bytes, out, out_dt, dev_err, stream, family);
+}
+
+int32_t sdv_xcheck_verify_attention_dense_view(
+    int32_t family, const void* q, int32_t q_dt, const int32_t* qo_indptr,
+    const int32_t* kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+    const sdv_subpage_view* view, const int32_t* block_table, int32_t max_blocks,
+    int32_t bt_stride, float softmax_scale, int32_t num_splits, void* workspace,
+    size_t workspace_bytes, void* out, int32_t out_dt, int32_t* dev_err, hipStream_t stream) {
+  SDV_XCHECK_FAMILY()
+  return dense_view_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                         block_table, max_blocks, bt_stride, softmax_scale, num_splits,
+                         workspace, workspace_bytes, out, out_dt, dev_err, stream, family);
+}
+
+int32_t sdv_xcheck_verify_attention_sparse(
+    int32_t family, const void* q, int32_t q_dt, const int32_t* qo_indptr,
+    const int32_t* kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+    const sdv_paged_kv* kv, const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+    const int32_t* topk_idx, int32_t top_k, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes, void* out, int32_t out_dt, int32_t* dev_err,
+    hipStream_t stream) {
+  SDV_XCHECK_FAMILY()
+  return sparse_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
+                          max_pages, bt_stride, topk_idx, nullptr, nullptr, nullptr, top_k,
+                          softmax_scale, num_splits, workspace, workspace_bytes, out, out_dt,
+                          dev_err, stream, "verify_attention_sparse launch", family);
+}
+
+int32_t sdv_xcheck_verify_attention_sparse_select(
+    int32_t family, const void* q, int32_t q_dt, const int32_t* qo_indptr,
+    const int32_t* kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+    const sdv_paged_kv* kv, const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+    const float* scores, int32_t top_k, int32_t* topk_idx, int32_t* topk_cnt,
+    float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* out,
+    int32_t out_dt, int32_t* dev_err, hipStream_t stream) {
+  SDV_XCHECK_FAMILY()
+  if (B > 0 && !scores) return fail(SDV_ERR_NULL_POINTER, "scores must be non-null");
+  return sparse_attention(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
+                          max_pages, bt_stride, nullptr, scores, topk_idx, topk_cnt, top_k,
+                          softmax_scale, num_splits, workspace, workspace_bytes, out, out_dt,
+                          dev_err, stream, "verify_attention_sparse_select launch", family);
+}
+
+int32_t sdv_xcheck_verify_attention_paged(
+    int32_t family, const void* q, int32_t q_dt, const int32_t* qo_indptr,
+    const int32_t* kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+    const sdv_paged_kv* kv, const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
+    float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* out,
+    int32_t out_dt, int32_t* dev_err, hipStream_t stream) {
+  SDV_XCHECK_FAMILY()
+  return paged_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, block_table,
+                    max_pages, bt_stride, softmax_scale, num_splits, workspace, workspace_bytes,
+                    out, out_dt, dev_err, stream, family);
+}
+
+#undef SDV_XCHECK_FAMILY
+
+}  // extern "C"
+#endif  // SDV_XCHECK

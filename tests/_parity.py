@@ -13,6 +13,14 @@ from workloads import raw_numpy
 DEV = torch.device("cuda:0")
 
 
+def q_capacity(q: torch.Tensor, rows: int) -> torch.Tensor:
+    """q on the GPU with at least `rows` rows (the B * max_qo_len capacity the library
+    addresses); rows past the batch's tokens are zero and never read."""
+    out = torch.zeros((max(rows, q.shape[0]),) + tuple(q.shape[1:]), dtype=q.dtype, device=DEV)
+    out[:q.shape[0]] = q.to(DEV)
+    return out
+
+
 def tol_ok(got: np.ndarray, ref: np.ndarray, dtype: str):
     """fp32: |gpu - ref| <= 1e-4 |ref| + 1e-5 elementwise; bf16/fp8: max-abs <= 2e-2."""
     got = np.asarray(got, dtype=np.float64)
@@ -29,7 +37,7 @@ class SparseRun:
         self.c = c
         w = c.w
         self.kv = sdv.PagedKV(c.k_pool.to(DEV), c.v_pool.to(DEV), c.k_scale, c.v_scale)
-        self.q = c.q.to(DEV)
+        self.q = q_capacity(c.q, w.batch * w.max_qo())
         self.qo_indptr = c.qo_indptr.to(DEV)
         self.kv_len = c.kv_len.to(DEV)
         self.bt = c.block_table.to(DEV)
@@ -45,19 +53,19 @@ class SparseRun:
                                      top_k=top_k or self.c.w.top_k, want_count=True,
                                      dev_err=dev_err)
 
-    def attend(self, idx, num_splits=1, dev_err=None):
+    def attend(self, idx, num_splits=1, dev_err=None, family=0):
         return sdv.verify_attention_sparse(self.q, self.qo_indptr, self.kv_len, self.kv, self.bt,
                                            idx, max_qo_len=self.max_qo,
                                            softmax_scale=self.c.softmax_scale,
-                                           num_splits=num_splits, dev_err=dev_err)
+                                           num_splits=num_splits, dev_err=dev_err, family=family)
 
 
 class PagedRun(SparseRun):
-    def attend_paged(self, num_splits=1, dev_err=None):
+    def attend_paged(self, num_splits=1, dev_err=None, family=0):
         return sdv.verify_attention_paged(self.q, self.qo_indptr, self.kv_len, self.kv, self.bt,
                                           max_qo_len=self.max_qo,
                                           softmax_scale=self.c.softmax_scale,
-                                          num_splits=num_splits, dev_err=dev_err)
+                                          num_splits=num_splits, dev_err=dev_err, family=family)
 
 
 def paged_oracle(c: W.SparseCase, requests=None):
@@ -81,7 +89,7 @@ class DenseRun:
         self.c = c
         w = c.w
         self.pool = c.pool.to(DEV)
-        self.q = c.q.to(DEV)
+        self.q = q_capacity(c.q, w.batch * w.max_qo())
         self.qo_indptr = c.qo_indptr.to(DEV)
         self.kv_len = c.kv_len.to(DEV)
         self.bt = c.block_table.to(DEV)
@@ -96,11 +104,11 @@ class DenseRun:
                                         k_scale=self.c.k_scale, v_scale=self.c.v_scale,
                                         pool_index_scale=w.pool_index_scale, dev_err=dev_err)
 
-    def attend(self, view, offs, num_splits=1, dev_err=None):
+    def attend(self, view, offs, num_splits=1, dev_err=None, family=0):
         return sdv.verify_attention_dense(self.q, self.qo_indptr, self.kv_len, view, offs,
                                           max_qo_len=self.max_qo,
                                           softmax_scale=self.c.softmax_scale,
-                                          num_splits=num_splits, dev_err=dev_err)
+                                          num_splits=num_splits, dev_err=dev_err, family=family)
 
 
 def dense_oracle(c: W.DenseCase, requests=None):

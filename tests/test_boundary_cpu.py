@@ -104,13 +104,16 @@ def test_dense_rejections():
     assert _dense(v, splits=0) == L.SDV_ERR_SHAPE
     assert _dense(v, q=None) == L.SDV_ERR_NULL_POINTER
     assert _dense(v, splits=4) == L.SDV_ERR_WORKSPACE             # no workspace given
-    need = L.load().sdv_workspace_bytes(8, 64, 128, 4)
+    need = L.load().sdv_workspace_bytes(L.SDV_OP_VERIFY_DENSE, 8, 64, 128, 4)
     assert need >= 4 * 8 * 64 * 129 * 4
     assert _dense(v, splits=4, ws=FAKE, ws_bytes=need - 1) == L.SDV_ERR_WORKSPACE
     assert _dense(v, q=C.c_void_p(0x10008)) == L.SDV_ERR_SHAPE    # q not 16-byte aligned
     assert _dense(v, out=C.c_void_p(0x10004)) == L.SDV_ERR_SHAPE  # out not 16-byte aligned
     assert _dense(v, B=0) == L.SDV_OK                             # nothing to do
     assert _dense(v, offs=None) == L.SDV_ERR_NULL_POINTER
+    # a split holds at most 1024 sub-pages: 2048 need two splits
+    assert _dense(v, msp=2048) == L.SDV_ERR_SHAPE
+    assert _dense(v, msp=2048, splits=2) == L.SDV_ERR_WORKSPACE   # accepted, needs a workspace
     empty = L.SubpageView()
     assert _dense(empty) != L.SDV_OK
 
@@ -297,8 +300,44 @@ def test_combine_and_helpers():
     assert lib.lse_combine(FAKE, FAKE, 2, 4, 4, 128, FAKE, 2, None, None) == L.SDV_ERR_DTYPE
     assert lib.lse_combine(None, FAKE, 2, 4, 4, 128, FAKE, 0, None, None) == L.SDV_ERR_NULL_POINTER
     assert lib.lse_combine(FAKE, FAKE, 2, 0, 4, 128, FAKE, 0, None, None) == L.SDV_OK
-    assert lib.sdv_workspace_bytes(8, 16, 128, 1) == 0
     assert lib.sdv_status_string(3).decode().startswith("unsupported geometry")
     assert lib.sdv_fill_u32(FAKE, 17, 0, None) == L.SDV_ERR_SHAPE
-    prev = lib.sdv_set_kernel_family(1)
-    assert lib.sdv_set_kernel_family(prev) == 1
+
+
+def test_workspace_bytes_per_op():
+    lib = L.load()
+    f = lib.sdv_workspace_bytes
+    units = 4 * 8 * 64                              # splits x rows x heads
+    pad = lambda x: (x + 255) // 256 * 256          # noqa: E731
+    for op in (L.SDV_OP_VERIFY_DENSE, L.SDV_OP_VERIFY_SPARSE, L.SDV_OP_VERIFY_PAGED):
+        assert f(op, 8, 64, 128, 4) == pad(units * 128 * 4) + pad(units * 4)
+        assert f(op, 8, 64, 128, 1) == 0            # one split: no partials
+        assert f(op, 0, 64, 128, 4) == 0
+    assert f(0, 8, 64, 128, 4) == 0                 # not an attention op
+    assert f(99, 8, 64, 128, 4) == 0
+
+
+def test_product_library_holds_no_kernel_selection_state():
+    """The product library exports no setter that changes what later calls compute and no
+    cross-check entry point; the cross-check build exports per-call family variants."""
+    lib = C.CDLL(L.LIB_PATH)
+    assert not hasattr(lib, "sdv_set_kernel_family")
+    for name in L.XCHECK_SIGNATURES:
+        assert not hasattr(lib, name), name
+    x = L.load_xcheck()
+    for name in L.XCHECK_SIGNATURES:
+        assert hasattr(x, name), name
+    assert not hasattr(x, "sdv_set_kernel_family")
+
+
+def test_xcheck_rejects_unknown_family_before_any_launch():
+    x = L.load_xcheck()
+    v = _good_view()
+    args = (FAKE, L.SDV_BF16, FAKE, FAKE, 2, 4, 64, C.byref(v), FAKE, 16, 16, 0.088, 1, None, 0,
+            FAKE, L.SDV_BF16, None, None)
+    for fam in (2, 7, -1):
+        assert x.sdv_xcheck_verify_attention_dense_view(fam, *args) == L.SDV_ERR_SHAPE
+        assert "kernel family" in x.sdv_last_error().decode()
+    # a valid family still validates the arguments on the host (null q)
+    bad = (None,) + args[1:]
+    assert x.sdv_xcheck_verify_attention_dense_view(L.FAMILY_VALU, *bad) == L.SDV_ERR_NULL_POINTER

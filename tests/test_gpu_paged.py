@@ -30,18 +30,16 @@ CASES = [PAGED_S, PAGED_FP8, PAGED_RAGGED, PAGED_D64, PAGED_G16]
 def _announce(request):
     print(f"\n[gpu] {request.node.name}", flush=True)
     yield
-    sdv.set_kernel_family(0)
 
 
 @pytest.mark.parametrize("family", [0, 3, 4, 5, 6])
 @pytest.mark.parametrize("splits", [1, 2, 16])
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_paged_parity(w, splits, family):
-    sdv.set_kernel_family(family)
     c = W.make_sparse_case(w)
     run = PagedRun(c)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = run.attend_paged(num_splits=splits, dev_err=err)
+    out = run.attend_paged(num_splits=splits, dev_err=err, family=family)
     torch.cuda.synchronize()
     ref = paged_oracle(c)
     ok, worst = tol_ok(out_numpy(out[:run.n]), ref, "bf16")
@@ -53,7 +51,6 @@ def test_paged_parity(w, splits, family):
 def test_paged_poison_never_read(family):
     """NaN beyond every request's kv_len in its last page and in every page it does not
     own: no output may see them."""
-    sdv.set_kernel_family(family)
     c = W.make_sparse_case(PAGED_S, poison=True)
     for pool in (c.k_pool, c.v_pool):
         for r, kv in enumerate(c.lengths.kv):
@@ -61,7 +58,7 @@ def test_paged_poison_never_read(family):
             if kv % 128:
                 pool[int(c.block_table[r, kv // 128]), :, kv % 128:, :] = float("nan")
     run = PagedRun(c)
-    out = run.attend_paged(num_splits=2)
+    out = run.attend_paged(num_splits=2, family=family)
     torch.cuda.synchronize()
     ok, worst = tol_ok(out_numpy(out[:run.n]), paged_oracle(c), "bf16")
     assert ok, worst

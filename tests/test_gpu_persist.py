@@ -50,19 +50,17 @@ def _paged(w):
 def _announce(request):
     print(f"\n[gpu] {request.node.name}", flush=True)
     yield
-    sdv.set_kernel_family(0)
 
 
 @pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("splits", [2, 3, 16])
 @pytest.mark.parametrize("w", [MANY_SHORT_VIEW, FEW_LONG_VIEW], ids=lambda w: w.name)
 def test_persist_view_parity(w, splits, family):
-    sdv.set_kernel_family(family)
     c, ref = _dense(w)
     run = DenseRun(c)
     view, offs = run.view()
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = run.attend(view, offs, num_splits=splits, dev_err=err)
+    out = run.attend(view, offs, num_splits=splits, dev_err=err, family=family)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     ok, worst = tol_ok(out_numpy(out[:run.n]), ref, "bf16")
@@ -74,11 +72,10 @@ def test_persist_view_parity(w, splits, family):
 @pytest.mark.parametrize("w", [MANY_SHORT_PAGED, FEW_LONG_PAGED, RAGGED_PAGED_FP8],
                          ids=lambda w: w.name)
 def test_persist_paged_parity(w, splits, family):
-    sdv.set_kernel_family(family)
     c, ref = _paged(w)
     run = PagedRun(c)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = run.attend_paged(num_splits=splits, dev_err=err)
+    out = run.attend_paged(num_splits=splits, dev_err=err, family=family)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     ok, worst = tol_ok(out_numpy(out[:run.n]), ref, "bf16")
@@ -91,7 +88,6 @@ def test_persist_inconsistent_requests_flagged_others_exact(family):
     both are flagged and count as empty; every other request matches the oracle."""
     w = W.PAGED_BF16.scaled(name="persist_flags", batch=8, kv=("uniform", 200, 2000),
                             kv_capacity=2048)
-    sdv.set_kernel_family(family)
     c = W.make_sparse_case(w)
     run = PagedRun(c)
     kv_bad = c.kv_len.clone()
@@ -99,7 +95,7 @@ def test_persist_inconsistent_requests_flagged_others_exact(family):
     kv_bad[5] = w.max_pages() * 128 + 1
     run.kv_len = kv_bad.to(DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = run.attend_paged(num_splits=4, dev_err=err)
+    out = run.attend_paged(num_splits=4, dev_err=err, family=family)
     torch.cuda.synchronize()
     e = int(err.item())
     assert e & sdv._lib.DEVERR_QO_LEN and e & sdv._lib.DEVERR_KV_CAPACITY
@@ -113,15 +109,13 @@ def test_persist_inconsistent_requests_flagged_others_exact(family):
 def test_persist_matches_per_split_kernel_at_benchmark_size(family):
     """The dense benchmark configuration: the persistent kernel and the per-split kernel
     agree to the bf16 tolerance on every row, and sampled requests match the oracle."""
-    sdv.set_kernel_family(family)
     w = W.DENSE_BF16
     c = W.make_dense_case(w, device=DEV)
     run = DenseRun(c)
     view, offs = run.view()
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    got = run.attend(view, offs, num_splits=8, dev_err=err)
-    sdv.set_kernel_family(3)
-    ref_gpu = run.attend(view, offs, num_splits=8)
+    got = run.attend(view, offs, num_splits=8, dev_err=err, family=family)
+    ref_gpu = run.attend(view, offs, num_splits=8, family=sdv.FAMILY_WAVES)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     ok, worst = tol_ok(out_numpy(got[:run.n]), out_numpy(ref_gpu[:run.n]), "bf16")

@@ -34,10 +34,9 @@ CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64]
 def _announce(request):
     print(f"\n[gpu] {request.node.name}", flush=True)
     yield
-    sdv.set_kernel_family(0)
 
 
-def _select(run, scores, num_splits, write=True, dev_err=None, top_k=None):
+def _select(run, scores, num_splits, write=True, dev_err=None, top_k=None, family=0):
     w = run.c.w
     k = top_k or w.top_k
     rows_cap = w.batch * w.max_qo()
@@ -48,22 +47,21 @@ def _select(run, scores, num_splits, write=True, dev_err=None, top_k=None):
     out = sdv.verify_attention_sparse_select(
         run.q, run.qo_indptr, run.kv_len, run.kv, run.bt, scores, max_qo_len=run.max_qo,
         top_k=k, softmax_scale=run.c.softmax_scale, num_splits=num_splits, topk_idx=idx,
-        topk_cnt=cnt, dev_err=dev_err)
+        topk_cnt=cnt, dev_err=dev_err, family=family)
     return out, idx, cnt
 
 
-@pytest.mark.parametrize("family", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("family", [0, 1, 3, 4])
 @pytest.mark.parametrize("splits", [1, 2, 16])
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_select_parity(w, splits, family):
-    sdv.set_kernel_family(family)
     c = W.make_sparse_case(w)
     run = SparseRun(c)
     scores = run.scores()
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out, idx, cnt = _select(run, scores, splits, dev_err=err)
+    out, idx, cnt = _select(run, scores, splits, dev_err=err, family=family)
     idx2, _ = run.topk(scores)
-    out2 = run.attend(idx2, num_splits=splits)
+    out2 = run.attend(idx2, num_splits=splits, family=family)
     torch.cuda.synchronize()
     ref = sparse_oracle(c)
     n = run.n
@@ -77,10 +75,9 @@ def test_select_parity(w, splits, family):
 
 @pytest.mark.parametrize("family", [0, 3, 4])
 def test_select_without_writing_the_selection(family):
-    sdv.set_kernel_family(family)
     c = W.make_sparse_case(SPARSE_S)
     run = SparseRun(c)
-    out, _, _ = _select(run, run.scores(), 2, write=False)
+    out, _, _ = _select(run, run.scores(), 2, write=False, family=family)
     torch.cuda.synchronize()
     ok, worst = tol_ok(out_numpy(out[:run.n]), sparse_oracle(c)["out"], "bf16")
     assert ok, worst
@@ -160,10 +157,8 @@ def test_select_host_errors():
     run = SparseRun(c)
     scores = run.scores()
     # the vector-ALU family needs an index buffer to hold the selection
-    sdv.set_kernel_family(1)
     with pytest.raises(sdv.SdvError):
-        _select(run, scores, 1, write=False)
-    sdv.set_kernel_family(0)
+        _select(run, scores, 1, write=False, family=sdv.FAMILY_VALU)
     # more pages than any selection takes
     wide = torch.zeros(scores.shape[0], scores.shape[1], 4097, dtype=torch.float32, device=DEV)
     bt = torch.zeros(run.bt.shape[0], 4097, dtype=torch.int32, device=DEV)

@@ -52,7 +52,7 @@ def _raw(t):
 @pytest.mark.parametrize("w", STAGE_HND, ids=lambda w: w.name)
 def test_stage_paged_bit_exact(w):
     c = W.make_sparse_case(w)
-    rows = c.lengths.total_q
+    rows = w.batch * w.max_qo()
     kn, vn = _new_rows(rows, w.num_kv_heads, w.head_dim, c.k_pool.dtype, 11)
     ref_k, ref_v = stage_paged(_raw(c.k_pool), _raw(c.v_pool), _raw(kn), _raw(vn),
                                c.qo_indptr.numpy(), c.lengths.kv, c.block_table.numpy())
@@ -69,7 +69,7 @@ def test_stage_paged_bit_exact(w):
 @pytest.mark.parametrize("w", STAGE_VIEW, ids=lambda w: w.name)
 def test_stage_view_bit_exact(w):
     c = W.make_dense_case(w)
-    rows = c.lengths.total_q
+    rows = w.batch * w.max_qo()
     kn, vn = _new_rows(rows, w.num_kv_heads, w.head_dim, c.pool.dtype, 12)
     page_elems = 4 * w.num_kv_heads * 32 * w.head_dim
     ref = stage_view(_raw(c.pool).reshape(-1), w.root_page * page_elems, _raw(kn), _raw(vn),
@@ -126,7 +126,7 @@ def test_overlap_correction_restage_then_attention():
 def test_stage_flags():
     w = STAGE_HND[0]
     c = W.make_sparse_case(w)
-    kn, vn = _new_rows(c.lengths.total_q, w.num_kv_heads, w.head_dim, torch.bfloat16, 13)
+    kn, vn = _new_rows(w.batch * w.max_qo(), w.num_kv_heads, w.head_dim, torch.bfloat16, 13)
     kv = sdv.PagedKV(c.k_pool.to(DEV), c.v_pool.to(DEV))
     bt = c.block_table.clone()
     bt[0, :] = c.k_pool.shape[0] + 3                   # request 0: pages out of range
@@ -145,7 +145,7 @@ def test_stage_full_size_properties():
     staged elements changed."""
     w = W.PAGED_BF16
     c = W.make_sparse_case(w, device=DEV)
-    rows = c.lengths.total_q
+    rows = w.batch * w.max_qo()
     g = torch.Generator(device=DEV).manual_seed(31)
     kn = torch.randn((rows, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(torch.bfloat16)
     vn = torch.randn((rows, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(torch.bfloat16)
