@@ -217,6 +217,31 @@ int32_t verify_attention_dense_view(const void* q, int32_t q_dt, const int32_t* 
                                     void* workspace, size_t workspace_bytes, void* out,
                                     int32_t out_dt, int32_t* dev_err, hipStream_t stream);
 
+/*
+ * verify_attention_dense_view_noalloc — verify_attention_dense_view for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Arguments, results and errors
+ * as verify_attention_dense_view without workspace / workspace_bytes: the split-KV
+ * partials (sdv_workspace_bytes(SDV_OP_VERIFY_DENSE, B * max_qo_len, num_q_heads,
+ * head_dim, num_splits) bytes) go to a device scratch array of
+ * SDV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends.  A call that needs more is SDV_ERR_WORKSPACE (use fewer splits or rows,
+ * or the workspace entry point).  The call allocates nothing; the first call on a device
+ * looks up that device's scratch address.  Every call on one GPU shares that GPU's
+ * scratch, so calls that overlap in time on one GPU (concurrent streams, or host threads
+ * enqueueing on different streams) race and give unspecified results; calls ordered on
+ * one stream do not.  Nothing in the scratch needs to start at zero.
+ */
+#define SDV_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int32_t verify_attention_dense_view_noalloc(const void* q, int32_t q_dt,
+                                            const int32_t* qo_indptr, const int32_t* kv_len,
+                                            int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+                                            const sdv_subpage_view* view,
+                                            const int32_t* block_table, int32_t max_blocks,
+                                            int32_t bt_stride, float softmax_scale,
+                                            int32_t num_splits, void* out, int32_t out_dt,
+                                            int32_t* dev_err, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------
  * Sparse target layer over ordinary head-major 128-token pages: page p of K holds
  * [num_kv_heads][128][head_dim] contiguous elements at k + p * page_stride (V alike).

@@ -25,6 +25,8 @@ SDV_F32 = 0
 SDV_BF16 = 1
 SDV_FP8_E4M3 = 2
 
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # SDV_NOALLOC_SCRATCH_BYTES
+
 SDV_OP_VERIFY_DENSE = 1
 SDV_OP_VERIFY_SPARSE = 2
 SDV_OP_VERIFY_PAGED = 3
@@ -83,6 +85,9 @@ SIGNATURES = {
                                     _F, _I, _P, _S, _P, _I, _P, _P]),
     "verify_attention_dense_view": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(SubpageView), _P,
                                          _I, _I, _F, _I, _P, _S, _P, _I, _P, _P]),
+    "verify_attention_dense_view_noalloc": (_I, [_P, _I, _P, _P, _I, _I, _I,
+                                                 C.POINTER(SubpageView), _P, _I, _I, _F, _I, _P,
+                                                 _I, _P, _P]),
     "proxy_page_scores": (_I, [_P, _I, _P, _P, _I, _I, _I, C.POINTER(PagedKV), _P, _I, _I, _P,
                                _P, _P]),
     "ladder_topk_pages": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),

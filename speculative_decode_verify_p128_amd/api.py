@@ -264,6 +264,33 @@ def verify_attention_dense_view(q: torch.Tensor, qo_indptr: torch.Tensor, kv_len
     return out
 
 
+def verify_attention_dense_view_noalloc(q: torch.Tensor, qo_indptr: torch.Tensor,
+                                        kv_len: torch.Tensor, view: SubpageView,
+                                        block_table: torch.Tensor, *, max_qo_len: int,
+                                        softmax_scale: float, num_splits: int = 1,
+                                        max_blocks: Optional[int] = None,
+                                        out: torch.Tensor, dev_err: Optional[torch.Tensor] = None
+                                        ) -> torch.Tensor:
+    """verify_attention_dense_view with the split-KV partials in the library's device
+    scratch (no workspace; `out` must be passed: nothing is allocated)."""
+    B = _lengths(qo_indptr, kv_len)
+    rows_cap = B * max_qo_len
+    _query(q, rows_cap, view.num_kv_heads, view.head_dim)
+    _block_table(block_table, B)
+    mb = block_table.shape[1] if max_blocks is None else max_blocks
+    if mb > block_table.shape[1]:
+        raise ValueError(f"max_blocks {mb} exceeds the block table's width {block_table.shape[1]}")
+    out = _out(out, q, rows_cap, None)
+    _dev_err(dev_err)
+    _same_device(q.device, qo_indptr=qo_indptr, kv_len=kv_len, block_table=block_table, out=out,
+                 dev_err=dev_err, pool=view.pool)
+    L.check(L.load().verify_attention_dense_view_noalloc(
+        _ptr(q), dtype_code(q.dtype), _ptr(qo_indptr), _ptr(kv_len), B, max_qo_len, q.shape[1],
+        C.byref(view.c), _ptr(block_table), mb, block_table.stride(0), softmax_scale,
+        num_splits, _ptr(out), dtype_code(out.dtype), _ptr(dev_err), _stream(q.device)))
+    return out
+
+
 @dataclass
 class PagedKV:
     """Head-major P128 page arrays k/v [num_pages, Hkv, 128, d] (non-owning view)."""

@@ -7,9 +7,11 @@
 // sdv_xcheck_* entry points that take the kernel family as an argument of the call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -113,6 +115,45 @@ void split_workspace(void* workspace, int64_t rows_cap, int32_t num_q_heads, int
                                   head_dim * sizeof(float));
   *part_o = reinterpret_cast<float*>(workspace);
   *part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+}
+
+}  // namespace
+
+// Device scratch of the allocation-free entry point: the split-KV partial outputs and
+// log-sum-exps of verify_attention_dense_view_noalloc live here instead of in a caller
+// workspace.  Each GPU holds its own copy for the life of the process.  Host code never
+// uses this name as an address: the address of a device's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SDV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the device's first call), or null
+// with the failure recorded.
+void* device_scratch(int32_t* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = fail(SDV_ERR_HIP, "no usable current device for the scratch buffer (%d): %s", dev,
+                   hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *status = fail(SDV_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *status = SDV_OK;
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -342,6 +383,39 @@ int32_t verify_attention_dense_view(const void* q, int32_t q_dt, const int32_t* 
   return dense_view_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
                          block_table, max_blocks, bt_stride, softmax_scale, num_splits,
                          workspace, workspace_bytes, out, out_dt, dev_err, stream, kFamilyAuto);
+}
+
+int32_t verify_attention_dense_view_noalloc(const void* q, int32_t q_dt,
+                                            const int32_t* qo_indptr, const int32_t* kv_len,
+                                            int32_t B, int32_t max_qo_len, int32_t num_q_heads,
+                                            const sdv_subpage_view* view,
+                                            const int32_t* block_table, int32_t max_blocks,
+                                            int32_t bt_stride, float softmax_scale,
+                                            int32_t num_splits, void* out, int32_t out_dt,
+                                            int32_t* dev_err, hipStream_t stream) {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (B > 0 && num_splits > 1 && view && view->num_kv_heads >= 1 &&
+      num_q_heads % view->num_kv_heads == 0) {
+    const size_t need = sdv_workspace_bytes(SDV_OP_VERIFY_DENSE,
+                                            static_cast<int32_t>(std::min<int64_t>(
+                                                static_cast<int64_t>(B) * max_qo_len, INT32_MAX)),
+                                            num_q_heads, view->head_dim, num_splits);
+    if (need > SDV_NOALLOC_SCRATCH_BYTES)
+      return fail(SDV_ERR_WORKSPACE, "the call needs %zu bytes of split-KV scratch, the "
+                  "allocation-free entry point holds %zu: use fewer splits or rows, or "
+                  "verify_attention_dense_view with a workspace", need,
+                  static_cast<size_t>(SDV_NOALLOC_SCRATCH_BYTES));
+    if (need > 0) {
+      int32_t st = SDV_OK;
+      ws = device_scratch(&st);
+      if (!ws) return st;
+      ws_bytes = SDV_NOALLOC_SCRATCH_BYTES;
+    }
+  }
+  return dense_view_call(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, view,
+                         block_table, max_blocks, bt_stride, softmax_scale, num_splits, ws,
+                         ws_bytes, out, out_dt, dev_err, stream, kFamilyAuto);
 }
 
 static int32_t check_paged_kv(const sdv_paged_kv* kv) {

@@ -341,3 +341,17 @@ def test_xcheck_rejects_unknown_family_before_any_launch():
     # a valid family still validates the arguments on the host (null q)
     bad = (None,) + args[1:]
     assert x.sdv_xcheck_verify_attention_dense_view(L.FAMILY_VALU, *bad) == L.SDV_ERR_NULL_POINTER
+
+
+def test_dense_view_noalloc_host_checks():
+    lib = L.load()
+    v = _good_view()
+    f = lambda B, splits, Hq=64: lib.verify_attention_dense_view_noalloc(  # noqa: E731
+        FAKE, L.SDV_BF16, FAKE, FAKE, B, 4, Hq, C.byref(v), FAKE, 16, 16, 0.088, splits, FAKE,
+        L.SDV_BF16, None, None)
+    # partials of 4096 splits x 8 rows x 64 heads x 128 channels exceed the scratch: refused
+    # before any HIP call
+    assert f(2, 4096) == L.SDV_ERR_WORKSPACE
+    assert "scratch" in lib.sdv_last_error().decode()
+    assert f(0, 4) == L.SDV_OK                          # nothing to do
+    assert f(2, 1, Hq=66) == L.SDV_ERR_SHAPE            # argument checks as the workspace entry
