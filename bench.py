@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--dense-two-call", action="store_true",
                    help="also time the draft-layer step as two calls (view offsets, then "
                         "attention over them), reported under dense.two_call")
+    p.add_argument("--long-splits", type=int, default=None)
+    p.add_argument("--ragged-splits", type=int, default=None, help="ragged sparse num_splits")
+    p.add_argument("--ragged-dense-splits", type=int, default=None)
     p.add_argument("--no-extra-configs", action="store_true",
                    help="skip the long-context fp8 and ragged-batch lines")
     p.add_argument("--only", default=None,
@@ -458,10 +461,14 @@ def sparse_gather_units(case, idx_np, torch, dev):
     return t(proxy), t(sel)
 
 
-def sparse_config_line(torch, sdv, W, w, dev, args, flush, fam):
-    """The sparse target-layer step (proxy scores, then top-k + sparse attention in one
-    launch, + the split-KV combine) on workload w: tokens/s, per-kernel times and
-    algorithmic GB/s."""
+def sparse_config_line(torch, sdv, W, w, dev, args, flush, fam, splits=None):
+    """The sparse target-layer step on workload w: proxy scores, then the ladder top-k
+    and sparse attention (+ the split-KV combine) either in one launch (selection inside
+    the attention workgroups) or as a standalone top-k launch and the attention over its
+    indices; both are timed and the faster is the line's step.  Tokens/s, per-kernel
+    times and algorithmic GB/s."""
+    if splits:
+        w = w.scaled(num_splits=splits)
     c = W.make_sparse_case(w, device=dev)
     kv = sdv.PagedKV(c.k_pool, c.v_pool, c.k_scale, c.v_scale)
     mq = w.max_qo()
@@ -484,32 +491,52 @@ def sparse_config_line(torch, sdv, W, w, dev, args, flush, fam):
                                            num_splits=w.num_splits, workspace=ws, out=out,
                                            family=fam)
 
-    fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
-    ms, per, _ = time_steps(fns, args.steps, args.warmup, torch, flush)
+    def k_topk():
+        sdv.ladder_topk_pages(scores, c.qo_indptr, c.kv_len, max_qo_len=mq, top_k=w.top_k,
+                              topk_idx=idx)
+
+    def k_sparse():
+        sdv.verify_attention_sparse(q, c.qo_indptr, c.kv_len, kv, c.block_table, idx,
+                                    max_qo_len=mq, softmax_scale=c.softmax_scale,
+                                    num_splits=w.num_splits, workspace=ws, out=out, family=fam)
+
+    paths = {
+        "fused": [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)],
+        "three_launch": [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
+                         ("verify_attention_sparse", k_sparse)]}
+    timed = {p: time_steps(f, args.steps, args.warmup, torch, flush) for p, f in paths.items()}
     # the selection, written out once after timing, sizes the algorithmic bytes
-    sdv.ladder_topk_pages(scores, c.qo_indptr, c.kv_len, max_qo_len=mq, top_k=w.top_k,
-                          topk_idx=idx)
+    k_topk()
     torch.cuda.synchronize()
     ab = sparse_algorithmic_bytes(c, idx.cpu().numpy())
-    kern = {}
-    for name, key in (("proxy_page_scores", "proxy"), ("verify_attention_sparse_select", "select")):
-        gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
-        kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
-                      "frac_of_peak": gbs / HBM_PEAK_GBS,
-                      "traffic": load_traffic(name, w.name, source_hash(*KERNEL_SOURCES[name]))}
-    path = ab["proxy"] + ab["select"]
-    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    keys = {"proxy_page_scores": "proxy", "verify_attention_sparse_select": "select",
+            "ladder_topk_pages": "topk", "verify_attention_sparse": "sparse"}
     tokens = c.lengths.total_q
-    res = {"value": tokens / (ms * 1e-3), "unit": "verify tokens/s", "ms_per_step": ms,
+    lines = {}
+    for p, (ms, per, _) in timed.items():
+        kern = {}
+        for name in per:
+            key = keys[name]
+            gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
+            kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
+                          "frac_of_peak": gbs / HBM_PEAK_GBS,
+                          "traffic": load_traffic(name, w.name, source_hash(*KERNEL_SOURCES[name]))}
+        path = sum(ab[keys[name]] for name in per)
+        dom = max(kern, key=lambda k: kern[k]["avg_us"])
+        lines[p] = {"value": tokens / (ms * 1e-3), "ms_per_step": ms,
+                    "path_algorithmic_bytes": path, "gb_per_s": path / (ms * 1e-3) / 1e9,
+                    "frac_of_peak": path / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_s"],
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
+                                 "traffic": kern[dom]["traffic"]},
+                    "kernels": kern}
+    best = min(lines, key=lambda p: lines[p]["ms_per_step"])
+    res = {"step": best, **{k: v for k, v in lines[best].items()}, "unit": "verify tokens/s",
            "verify_tokens": tokens, "kv_tokens": int(c.lengths.kv.sum()),
-           "num_splits": w.num_splits, "path_algorithmic_bytes": path,
-           "gb_per_s": path / (ms * 1e-3) / 1e9,
-           "frac_of_peak": path / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-           "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_s"],
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
-                        "traffic": kern[dom]["traffic"]},
-           "kernels": kern}
+           "num_splits": w.num_splits, "paths": {p: {"ms_per_step": v["ms_per_step"],
+                                                     "kernels": v["kernels"]}
+                                                 for p, v in lines.items()}}
     del c, kv, q, scores, idx, out, ws
     return res
 
@@ -812,7 +839,8 @@ def main():
             "workload": "long_fp8: sparse verify, batch 8, qo_len 4, 16 q / 4 kv heads, head_dim "
                         "128, kv_len 131072, fp8 e4m3 K/V with per-tensor scales, bf16 Q, top-k "
                         "64, 16 splits",
-            **sparse_config_line(torch, sdv, W, W.LONG_FP8, dev, args, flush, fam)}
+            **sparse_config_line(torch, sdv, W, W.LONG_FP8, dev, args, flush, fam,
+                                 args.long_splits)}
 
     # ---- ragged mixed batch through both paths ----
     if want("ragged", args.no_extra_configs):
@@ -821,8 +849,10 @@ def main():
             "workload": "ragged_mixed: batch 256, qo_len 1..8, kv_len log-normal (median 2048, "
                         "clipped [64, 65536]) with page-crossing rows, 16 q / 4 kv heads, "
                         "head_dim 128, bf16, top-k 16 clamped",
-            "sparse": sparse_config_line(torch, sdv, W, wr, dev, args, flush, fam),
-            "dense": dense_config_line(torch, sdv, W, wr, dev, args, flush, fam)}
+            "sparse": sparse_config_line(torch, sdv, W, wr, dev, args, flush, fam,
+                                         args.ragged_splits),
+            "dense": dense_config_line(torch, sdv, W, wr, dev, args, flush, fam,
+                                       args.ragged_dense_splits)}
 
     # ---- target dense layers: ladder attention over ordinary head-major P128 pages ----
     if want("paged", args.no_paged):

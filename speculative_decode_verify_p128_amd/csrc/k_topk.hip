@@ -14,6 +14,13 @@
 // only when a ballot shows a tie, and the owning lane retires the key and refreshes its
 // cache (wave_ladder_topk, shared with the selection inside the sparse attention
 // kernels).
+//
+// Tables over 256 pages take one 256-thread workgroup per (token row, KV head) instead,
+// whose cost does not grow with top_k: with the same 64-bit keys (unique, because the
+// page is part of the key), the k_eff-th largest key T is found bit by bit from the top
+// (the largest T that at least k_eff keys reach; the page word's high bits are the same
+// in every key and are set at once), the keys >= T -- exactly the selection -- are
+// gathered into LDS, and a bitonic network sorts them into rank order.
 #include "device.h"
 #include "internal.h"
 
@@ -54,11 +61,172 @@ __global__ void __launch_bounds__(64) sdv_topk_kernel(
   if (topk_cnt && lane == 0) topk_cnt[row * Hkv + h] = k_eff;
 }
 
+// Sum of v over the wave, the same in every lane: rotate-and-add inside each 16-lane row
+// (DPP row_ror), then the four row sums read into scalar registers.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  constexpr int kRowRor = 0x120;
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 1, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 2, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 4, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 8, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+}
+
+constexpr int kWideThreads = 256;
+constexpr int kWideMaxK = 1024;     // selections a workgroup sorts (top_k <= 1024)
+
+template <int ITEMS>
+__global__ void __launch_bounds__(kWideThreads) sdv_topk_wide_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ qo_indptr,
+    const int32_t* __restrict__ kv_len, int32_t B, int32_t max_qo_len, int32_t Hkv,
+    int32_t max_pages, int32_t top_k, int32_t* __restrict__ topk_idx,
+    int32_t* __restrict__ topk_cnt, int32_t* dev_err) {
+  __shared__ uint64_t sel[kWideMaxK];
+  __shared__ uint32_t part[2][kWideThreads / kWave];
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int row0 = qo_indptr[r];
+  const int qo = qo_indptr[r + 1] - row0;
+  const int kv = kv_len[r];
+  const bool bad_len = qo < 1 || qo > max_qo_len || kv < qo || row0 < 0 ||
+                       static_cast<int64_t>(row0) + qo > static_cast<int64_t>(B) * max_qo_len;
+  const bool bad_cap = !bad_len && static_cast<int64_t>(kv) > static_cast<int64_t>(max_pages) * kPage;
+  if (bad_len || bad_cap) {
+    if (tid == 0 && t == 0 && h == 0)
+      set_err(dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
+    return;
+  }
+  if (t >= qo) return;                       // uniform over the workgroup
+  const int bound = kv - qo + t + 1;
+  const int n = (bound + kPage - 1) / kPage;
+  const int64_t row = row0 + t;
+  const float* srow = scores + (row * Hkv + h) * max_pages;
+
+  // keys of pages tid + 256 i (0 past the token's valid pages; a valid key is never 0)
+  uint64_t key[ITEMS];
+  float sv[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) sv[i] = srow[min(tid + kWideThreads * i, n - 1)];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = tid + kWideThreads * i;
+    key[i] = p < n ? (static_cast<uint64_t>(ordered_key(sv[i])) << 32) |
+                         static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(p))
+                   : 0ull;
+  }
+  const int k_eff = top_k < n ? top_k : n;
+
+  // Number of keys >= c over the workgroup (one barrier; the partial sums alternate
+  // between two buffers, so a buffer is rewritten only after every thread has read it).
+  int it = 0;
+  auto count_ge = [&](uint64_t c) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) m += key[i] >= c ? 1u : 0u;
+    m = wave_sum_u32(m);
+    const int buf = it++ & 1;
+    if (lane == 0) part[buf][wave] = m;
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kWideThreads / kWave; ++w) s += part[buf][w];
+    return s;
+  };
+
+  // T: the largest value that at least k_eff keys reach, which (keys being unique) is
+  // the k_eff-th largest key.  With k_eff = n every valid key is taken (T = 1).  Every
+  // valid key's page word is 0xffffffff - p with p < 4096, so once the score word is
+  // fixed its bits 31..12 are ones and only bits 11..0 remain.
+  uint64_t T = 1;
+  if (k_eff < n) {
+    T = 0;
+    for (int bit = 63; bit >= 32; --bit) {
+      const uint64_t c = T | (1ull << bit);
+      if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
+    }
+    T |= 0xfffff000ull;
+    for (int bit = 11; bit >= 0; --bit) {
+      const uint64_t c = T | (1ull << bit);
+      if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
+    }
+  }
+
+  // the k_eff keys >= T into sel[0 .. k_eff), in any order
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  const int buf = it++ & 1;
+  if (lane == kWave - 1) part[buf][wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - mine;
+  for (int w = 0; w < wave; ++w) pos += part[buf][w];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i)
+    if (key[i] >= T) sel[pos++] = key[i];
+  // pad to a power of two with 0 keys, which sort last
+  int p2 = 1;
+  while (p2 < k_eff) p2 <<= 1;
+  for (int j = k_eff + tid; j < p2; j += kWideThreads) sel[j] = 0ull;
+  __syncthreads();
+
+  // bitonic sort of sel[0 .. p2) into descending order
+  for (int k = 2; k <= p2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < p2; i += kWideThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t a = sel[i], b = sel[l];
+          const bool swap = (i & k) == 0 ? a < b : a > b;
+          if (swap) {
+            sel[i] = b;
+            sel[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  int32_t* out = topk_idx + (row * Hkv + h) * top_k;
+  for (int k = tid; k < top_k; k += kWideThreads)
+    out[k] = k < k_eff ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(sel[k])) : -1;
+  if (topk_cnt && tid == 0) topk_cnt[row * Hkv + h] = k_eff;
+}
+
 hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int32_t* kv_len,
                        int32_t B, int32_t max_qo_len, int32_t num_kv_heads, int32_t max_pages,
                        int32_t top_k, int32_t* topk_idx, int32_t* topk_cnt, int32_t* dev_err,
                        hipStream_t s) {
   dim3 grid(max_qo_len, num_kv_heads, B);
+  if (max_pages > 256) {
+    const int witems = (max_pages + kWideThreads - 1) / kWideThreads;
+#define SDV_TOPK_WIDE_CASE(N)                                                                \
+    if (witems <= N) {                                                                       \
+      hipLaunchKernelGGL(sdv_topk_wide_kernel<N>, grid, dim3(kWideThreads), 0, s, scores,     \
+                         qo_indptr, kv_len, B, max_qo_len, num_kv_heads, max_pages, top_k,   \
+                         topk_idx, topk_cnt, dev_err);                                       \
+      return hipGetLastError();                                                              \
+    }
+    SDV_TOPK_WIDE_CASE(2)
+    SDV_TOPK_WIDE_CASE(4)
+    SDV_TOPK_WIDE_CASE(8)
+    SDV_TOPK_WIDE_CASE(16)
+#undef SDV_TOPK_WIDE_CASE
+    return hipErrorInvalidValue;
+  }
   const int items = (max_pages + kWave - 1) / kWave;
 #define SDV_TOPK_CASE(N)                                                                     \
   if (items <= N) {                                                                          \
