@@ -595,7 +595,8 @@ def main():
               "here is a single-GPU kernel library with no cross-GPU step.", file=sys.stderr)
         sys.exit(2)
     oracle_pool = None
-    if not args.no_cpu_baseline and not args.calibrate_copy:
+    headline = args.only is None or "sparse" in args.only.split(",")
+    if not args.no_cpu_baseline and not args.calibrate_copy and headline:
         oracle_pool = start_oracle_pool()
     import torch
 
@@ -621,132 +622,139 @@ def main():
             sdv.fill_u32(flush_buf, 0x5A5A5A5A)
 
     # ---- sparse target-layer path (the headline workload) ----
-    w = W.SPARSE_BF16
-    splits = args.splits or w.num_splits
-    c = W.make_sparse_case(w, device=dev)
-    kv = sdv.PagedKV(c.k_pool, c.v_pool, c.k_scale, c.v_scale)
-    rows_cap = w.batch * w.max_qo()
-    scores = torch.empty((rows_cap, w.num_kv_heads, w.max_pages()), dtype=torch.float32, device=dev)
-    idx = torch.empty((rows_cap, w.num_kv_heads, w.top_k), dtype=torch.int32, device=dev)
-    out = torch.empty((rows_cap, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, splits, dev, op="sparse")
-    mq = w.max_qo()
+    # (skipped only when --only names sections without "sparse": profiling runs of other
+    # sections, whose JSON line then carries just those sections)
+    c = None
+    if only is None or "sparse" in only:
+        w = W.SPARSE_BF16
+        splits = args.splits or w.num_splits
+        c = W.make_sparse_case(w, device=dev)
+        kv = sdv.PagedKV(c.k_pool, c.v_pool, c.k_scale, c.v_scale)
+        rows_cap = w.batch * w.max_qo()
+        scores = torch.empty((rows_cap, w.num_kv_heads, w.max_pages()), dtype=torch.float32, device=dev)
+        idx = torch.empty((rows_cap, w.num_kv_heads, w.top_k), dtype=torch.int32, device=dev)
+        out = torch.empty((rows_cap, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        ws = sdv.alloc_workspace(rows_cap, w.num_q_heads, w.head_dim, splits, dev, op="sparse")
+        mq = w.max_qo()
 
-    def k_proxy():
-        sdv.proxy_page_scores(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, max_qo_len=mq,
-                              scores=scores)
+        def k_proxy():
+            sdv.proxy_page_scores(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, max_qo_len=mq,
+                                  scores=scores)
 
-    def k_topk():
-        sdv.ladder_topk_pages(scores, c.qo_indptr, c.kv_len, max_qo_len=mq, top_k=w.top_k,
-                              topk_idx=idx)
+        def k_topk():
+            sdv.ladder_topk_pages(scores, c.qo_indptr, c.kv_len, max_qo_len=mq, top_k=w.top_k,
+                                  topk_idx=idx)
 
-    def k_sparse():
-        sdv.verify_attention_sparse(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, idx,
-                                    max_qo_len=mq, softmax_scale=c.softmax_scale,
-                                    num_splits=splits, workspace=ws, out=out, family=fam)
+        def k_sparse():
+            sdv.verify_attention_sparse(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, idx,
+                                        max_qo_len=mq, softmax_scale=c.softmax_scale,
+                                        num_splits=splits, workspace=ws, out=out, family=fam)
 
-    def k_select():
-        sdv.verify_attention_sparse_select(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, scores,
-                                           max_qo_len=mq, top_k=w.top_k,
-                                           softmax_scale=c.softmax_scale, num_splits=splits,
-                                           workspace=ws, out=out, family=fam)
+        def k_select():
+            sdv.verify_attention_sparse_select(c.q, c.qo_indptr, c.kv_len, kv, c.block_table, scores,
+                                               max_qo_len=mq, top_k=w.top_k,
+                                               softmax_scale=c.softmax_scale, num_splits=splits,
+                                               workspace=ws, out=out, family=fam)
 
-    fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
-    launch_stats = {}
-    eager_ms, per, wall = time_steps(fns, args.steps, args.warmup, torch, flush, launch_stats)
-    ms = eager_ms
-    if args.graph:
-        # the step as one HIP graph (the path is capture-safe: no allocation, no host
-        # synchronisation, lengths read on the device); its outputs must equal the eager ones
-        ref_out = out.clone()
-        ms = time_graph(fns, args.steps, args.warmup, torch, flush)
-        if not torch.equal(out.view(torch.int16), ref_out.view(torch.int16)):
-            raise RuntimeError("graph replay of the sparse path differs from its eager run")
-        del ref_out
-    # the selection the fused launch made (written out here, after timing) sizes the
-    # algorithmic bytes; the two-launch path must reach the same output
-    fused_out = out.clone()
-    k_proxy()
-    k_topk()
-    k_sparse()
-    torch.cuda.synchronize()
-    if not torch.equal(out.view(torch.int16), fused_out.view(torch.int16)):
-        raise RuntimeError("in-kernel selection and standalone top-k give different outputs")
-    del fused_out
-    tokens = c.lengths.total_q
-    idx_np = idx.cpu().numpy()
-    ab = sparse_algorithmic_bytes(c, idx_np)
-    path_bytes = ab["proxy"] + ab["select"]
-    kern = {}
-    for name, key in (("proxy_page_scores", "proxy"), ("verify_attention_sparse_select", "select")):
-        gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
-        kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
-                      "frac_of_peak": gbs / HBM_PEAK_GBS}
-    unfused = None
-    if want("unfused", args.no_unfused):
-        ufns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
-                ("verify_attention_sparse", k_sparse)]
-        u_ms, u_per, _ = time_steps(ufns, args.steps, args.warmup, torch, flush)
-        unfused = {"ms_per_step": u_ms, "kernels": {}}
-        for name, key in (("proxy_page_scores", "proxy"), ("ladder_topk_pages", "topk"),
-                          ("verify_attention_sparse", "sparse")):
-            gbs = ab[key] / (u_per[name]["avg_us"] * 1e-6) / 1e9
-            unfused["kernels"][name] = {**u_per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
-                                        "frac_of_peak": gbs / HBM_PEAK_GBS}
-    dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    traffic = load_traffic(dom, w.name, source_hash(*KERNEL_SOURCES[dom]))
-    path_gbs = path_bytes / (ms * 1e-3) / 1e9
-    result = {
-        "metric": METRIC,
-        "value": tokens / (ms * 1e-3),
-        "unit": "verify tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded, generated on the GPU)",
-        "config": {"workload": "sparse_bf16: block-sparse target-layer verify, batch 64, "
-                               "qo_len 4, 16 q / 4 kv heads, head_dim 128, kv_len U[4096, 32768], "
-                               "128-token pages, top-k 16",
-                   "batch": w.batch, "qo_len": 4, "num_q_heads": w.num_q_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "top_k": w.top_k,
-                   "num_splits": splits, "seed": W.seed_for(w), "verify_tokens": tokens,
-                   "kv_tokens": int(c.lengths.kv.sum())},
-        "gb_per_s": path_gbs,
-        "frac_of_peak": path_gbs / HBM_PEAK_GBS,
-        "path_algorithmic_bytes": path_bytes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_s"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
-                     "traffic": traffic},
-        "kernels": kern,
-        "launch": ("one HIP graph replay per step (proxy, selection + attention); the per-kernel "
-                   "times in kernels come from an eager pass with events around every launch"
-                   if args.graph else "eager: one launch per kernel"),
-        "eager_ms_per_step": eager_ms,
-        "ms_per_step_with_launch_events": launch_stats.get("ms_per_step_with_launch_events"),
-        "unfused": unfused,
-        "sparse_row_expanded_kv_bytes": ab["sparse_row_expanded_kv"],
-        "wall_s_timed": wall,
-        "cache": ("warm: consecutive steps, no eviction" if args.warm else
-                  "cold: a 1 GiB fill before every step (untimed) evicts L2 and the Infinity Cache"),
-    }
-    if not args.no_probe:
-        # what the two kernels' own access patterns attain: their gather lists streamed
-        # once by the unit-list probe, cold
-        pu, su = sparse_gather_units(c, idx_np, torch, dev)
-        att = {"proxy_page_scores": units_read_gbs(torch, sdv, dev, [(c.k_pool, pu, 16384)], flush),
-               "verify_attention_sparse_select": units_read_gbs(
-                   torch, sdv, dev, [(c.k_pool, su, 16384), (c.v_pool, su, 16384)], flush)}
-        for name, gbs_att in att.items():
-            kern[name]["attainable_read_GB_s"] = gbs_att
-            kern[name]["frac_of_attainable"] = kern[name]["GB_s"] / gbs_att
-        del pu, su
-    del scores, ws
+        fns = [("proxy_page_scores", k_proxy), ("verify_attention_sparse_select", k_select)]
+        launch_stats = {}
+        eager_ms, per, wall = time_steps(fns, args.steps, args.warmup, torch, flush, launch_stats)
+        ms = eager_ms
+        if args.graph:
+            # the step as one HIP graph (the path is capture-safe: no allocation, no host
+            # synchronisation, lengths read on the device); its outputs must equal the eager ones
+            ref_out = out.clone()
+            ms = time_graph(fns, args.steps, args.warmup, torch, flush)
+            if not torch.equal(out.view(torch.int16), ref_out.view(torch.int16)):
+                raise RuntimeError("graph replay of the sparse path differs from its eager run")
+            del ref_out
+        # the selection the fused launch made (written out here, after timing) sizes the
+        # algorithmic bytes; the two-launch path must reach the same output
+        fused_out = out.clone()
+        k_proxy()
+        k_topk()
+        k_sparse()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), fused_out.view(torch.int16)):
+            raise RuntimeError("in-kernel selection and standalone top-k give different outputs")
+        del fused_out
+        tokens = c.lengths.total_q
+        idx_np = idx.cpu().numpy()
+        ab = sparse_algorithmic_bytes(c, idx_np)
+        path_bytes = ab["proxy"] + ab["select"]
+        kern = {}
+        for name, key in (("proxy_page_scores", "proxy"), ("verify_attention_sparse_select", "select")):
+            gbs = ab[key] / (per[name]["avg_us"] * 1e-6) / 1e9
+            kern[name] = {**per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
+                          "frac_of_peak": gbs / HBM_PEAK_GBS}
+        unfused = None
+        if want("unfused", args.no_unfused):
+            ufns = [("proxy_page_scores", k_proxy), ("ladder_topk_pages", k_topk),
+                    ("verify_attention_sparse", k_sparse)]
+            u_ms, u_per, _ = time_steps(ufns, args.steps, args.warmup, torch, flush)
+            unfused = {"ms_per_step": u_ms, "kernels": {}}
+            for name, key in (("proxy_page_scores", "proxy"), ("ladder_topk_pages", "topk"),
+                              ("verify_attention_sparse", "sparse")):
+                gbs = ab[key] / (u_per[name]["avg_us"] * 1e-6) / 1e9
+                unfused["kernels"][name] = {**u_per[name], "algorithmic_bytes": ab[key], "GB_s": gbs,
+                                            "frac_of_peak": gbs / HBM_PEAK_GBS}
+        dom = max(kern, key=lambda k: kern[k]["avg_us"])
+        traffic = load_traffic(dom, w.name, source_hash(*KERNEL_SOURCES[dom]))
+        path_gbs = path_bytes / (ms * 1e-3) / 1e9
+        result = {
+            "metric": METRIC,
+            "value": tokens / (ms * 1e-3),
+            "unit": "verify tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded, generated on the GPU)",
+            "config": {"workload": "sparse_bf16: block-sparse target-layer verify, batch 64, "
+                                   "qo_len 4, 16 q / 4 kv heads, head_dim 128, kv_len U[4096, 32768], "
+                                   "128-token pages, top-k 16",
+                       "batch": w.batch, "qo_len": 4, "num_q_heads": w.num_q_heads,
+                       "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "top_k": w.top_k,
+                       "num_splits": splits, "seed": W.seed_for(w), "verify_tokens": tokens,
+                       "kv_tokens": int(c.lengths.kv.sum())},
+            "gb_per_s": path_gbs,
+            "frac_of_peak": path_gbs / HBM_PEAK_GBS,
+            "path_algorithmic_bytes": path_bytes,
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_s"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": kern[dom]["GB_s"] / HBM_PEAK_GBS,
+                         "traffic": traffic},
+            "kernels": kern,
+            "launch": ("one HIP graph replay per step (proxy, selection + attention); the per-kernel "
+                       "times in kernels come from an eager pass with events around every launch"
+                       if args.graph else "eager: one launch per kernel"),
+            "eager_ms_per_step": eager_ms,
+            "ms_per_step_with_launch_events": launch_stats.get("ms_per_step_with_launch_events"),
+            "unfused": unfused,
+            "sparse_row_expanded_kv_bytes": ab["sparse_row_expanded_kv"],
+            "wall_s_timed": wall,
+            "cache": ("warm: consecutive steps, no eviction" if args.warm else
+                      "cold: a 1 GiB fill before every step (untimed) evicts L2 and the Infinity Cache"),
+        }
+        if not args.no_probe:
+            # what the two kernels' own access patterns attain: their gather lists streamed
+            # once by the unit-list probe, cold
+            pu, su = sparse_gather_units(c, idx_np, torch, dev)
+            att = {"proxy_page_scores": units_read_gbs(torch, sdv, dev, [(c.k_pool, pu, 16384)], flush),
+                   "verify_attention_sparse_select": units_read_gbs(
+                       torch, sdv, dev, [(c.k_pool, su, 16384), (c.v_pool, su, 16384)], flush)}
+            for name, gbs_att in att.items():
+                kern[name]["attainable_read_GB_s"] = gbs_att
+                kern[name]["frac_of_attainable"] = kern[name]["GB_s"] / gbs_att
+            del pu, su
+        del scores, ws
+
+    else:
+        result = {"metric": METRIC, "sections_only": sorted(only)}
 
     # ---- dense draft-layer path ----
     if want("dense", args.no_dense):
@@ -982,7 +990,7 @@ def main():
 
     if not args.no_probe:
         result["attainable_read_GB_s"] = attainable_read_gbs(torch, sdv, dev)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and c is not None:
         c_cpu = W.SparseCase(**{**c.__dict__})
         result["cpu_baseline"] = cpu_baseline(c_cpu, args.cpu_sample)
         result["cpu_baseline"]["cpu_model"] = host_cpu_model()
@@ -995,6 +1003,9 @@ def main():
             pool.join()
     else:
         result["cpu_baseline"] = None
+        if oracle_pool is not None:
+            oracle_pool[0].close()
+            oracle_pool[0].join()
     print(json.dumps(result))
 
 

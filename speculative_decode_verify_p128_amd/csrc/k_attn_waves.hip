@@ -431,8 +431,17 @@ __device__ __forceinline__ void waves_attend(WavesLds<RT, D, KDT, MODE>& sh, con
   }
 }
 
+// Waves per SIMD an instantiation may share a CU with: 16-row tiles whose LDS leaves room
+// for a second workgroup (fp8 K/V or head_dim 64) run two workgroups per CU, so a grid of
+// up to twice the CU count (many splits) is resident at once; the others keep the whole
+// register file (up to 512 registers per lane) at one workgroup per CU.
 template <int RT, int D, int KDT, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+constexpr int waves_occupancy() {
+  return RT == 1 && sizeof(WavesLds<RT, D, KDT, MODE>) <= 80 * 1024 ? 2 : 1;
+}
+
+template <int RT, int D, int KDT, int MODE, int OCC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   __shared__ WavesLds<RT, D, KDT, MODE> sh;
   // Grid x = (request, KV head), y = split, so consecutive workgroups (dealt round-robin
@@ -480,11 +489,13 @@ sdv_attn_waves_persist_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
 template <int RT, int D, int KDT, int MODE>
 hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
                     hipStream_t s) {
-  static const int per_cu = resident_per_cu(sdv_attn_waves_kernel<RT, D, KDT, MODE>);
+  constexpr int OCC = waves_occupancy<RT, D, KDT, MODE>();
+  static const int per_cu = resident_per_cu(sdv_attn_waves_kernel<RT, D, KDT, MODE, OCC>);
   AttnArgs args = a;
   args.target_wgs = per_cu * device_cu_count();
   dim3 grid(a.num_kv_heads * a.B, a.num_splits);
-  hipLaunchKernelGGL((sdv_attn_waves_kernel<RT, D, KDT, MODE>), grid, dim3(256), 0, s, args, ds, ss);
+  hipLaunchKernelGGL((sdv_attn_waves_kernel<RT, D, KDT, MODE, OCC>), grid, dim3(256), 0, s, args,
+                     ds, ss);
   return hipGetLastError();
 }
 

@@ -15,8 +15,8 @@
 // cache (wave_ladder_topk, shared with the selection inside the sparse attention
 // kernels).
 //
-// Tables over 256 pages take one 256-thread workgroup per (token row, KV head) instead,
-// whose cost does not grow with top_k: with the same 64-bit keys (unique, because the
+// Wide tables with a large top_k take one 256-thread workgroup per (token row, KV head)
+// instead, whose cost does not grow with top_k: with the same 64-bit keys (unique, because the
 // page is part of the key), the k_eff-th largest key T is found bit by bit from the top
 // (the largest T that at least k_eff keys reach; the page word's high bits are the same
 // in every key and are set at once), the keys >= T -- exactly the selection -- are
@@ -211,7 +211,12 @@ hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int3
                        int32_t top_k, int32_t* topk_idx, int32_t* topk_cnt, int32_t* dev_err,
                        hipStream_t s) {
   dim3 grid(max_qo_len, num_kv_heads, B);
-  if (max_pages > 256) {
+  // The wave kernel's rounds cost about top_k x (items + 8) dependent instructions, the
+  // workgroup kernel's bit search about 44 x (items / 4 + 20) plus a sort: the workgroup
+  // kernel takes tables over 256 pages where the first is the larger (measured: 1024
+  // pages, top-64, 31.6 -> 17.1 us; 512 pages, top-16, the wave kernel is faster).
+  const int items = (max_pages + kWave - 1) / kWave;
+  if (max_pages > 256 && top_k * (items + 8) > 1200) {
     const int witems = (max_pages + kWideThreads - 1) / kWideThreads;
 #define SDV_TOPK_WIDE_CASE(N)                                                                \
     if (witems <= N) {                                                                       \
@@ -227,7 +232,6 @@ hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int3
 #undef SDV_TOPK_WIDE_CASE
     return hipErrorInvalidValue;
   }
-  const int items = (max_pages + kWave - 1) / kWave;
 #define SDV_TOPK_CASE(N)                                                                     \
   if (items <= N) {                                                                          \
     hipLaunchKernelGGL(sdv_topk_kernel<N>, grid, dim3(kWave), 0, s, scores, qo_indptr, kv_len, \

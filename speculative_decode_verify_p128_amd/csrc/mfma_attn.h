@@ -32,6 +32,14 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+// Two OCP E4M3FN bytes (the low half of w, or the high half) widened to two bf16 in one
+// instruction (v_cvt_scalef32_pk_bf16_fp8 with scale 1): exact, since every E4M3FN value
+// is a bf16 value.  The first byte lands in the low half.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -134,15 +142,10 @@ __device__ __forceinline__ bf16x8 k_operand(const char* kb, int tt, int s, int i
   } else {
     uint32_t r8[2];
     lds_read<8>(kb + Gm::at(row, byte), r8);
-    float f[8];
-    fp8x2_to_f32<false>(r8[0], f[0], f[1]);
-    fp8x2_to_f32<true>(r8[0], f[2], f[3]);
-    fp8x2_to_f32<false>(r8[1], f[4], f[5]);
-    fp8x2_to_f32<true>(r8[1], f[6], f[7]);
-    w[0] = pack2_bf16(f[0], f[1]);
-    w[1] = pack2_bf16(f[2], f[3]);
-    w[2] = pack2_bf16(f[4], f[5]);
-    w[3] = pack2_bf16(f[6], f[7]);
+    w[0] = fp8x2_to_bf16x2<false>(r8[0]);
+    w[1] = fp8x2_to_bf16x2<true>(r8[0]);
+    w[2] = fp8x2_to_bf16x2<false>(r8[1]);
+    w[3] = fp8x2_to_bf16x2<true>(r8[1]);
   }
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
@@ -181,19 +184,14 @@ __device__ __forceinline__ bf16x8 v_operand(const uint32_t (&raw)[8][4], int n) 
     for (int m = 0; m < 4; ++m)
       w[m] = __builtin_amdgcn_perm(raw[2 * m + 1][n >> 1], raw[2 * m][n >> 1], sel);
   } else {
+    // byte (n & 3) of wa and of wb side by side in the low half of one word, widened
+    // together (one byte permute and one conversion per output word)
+    const uint32_t sel = 0x0c0c0400u + (n & 3) * 0x0101u;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      float a0, a1, b0, b1;
       const uint32_t wa = raw[2 * m][n >> 2];
       const uint32_t wb = raw[2 * m + 1][n >> 2];
-      if ((n & 2) == 0) {
-        fp8x2_to_f32<false>(wa, a0, a1);
-        fp8x2_to_f32<false>(wb, b0, b1);
-      } else {
-        fp8x2_to_f32<true>(wa, a0, a1);
-        fp8x2_to_f32<true>(wb, b0, b1);
-      }
-      w[m] = (n & 1) ? pack2_bf16(a1, b1) : pack2_bf16(a0, b0);
+      w[m] = fp8x2_to_bf16x2<false>(__builtin_amdgcn_perm(wb, wa, sel));
     }
   }
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));

@@ -1,5 +1,6 @@
-"""GPU parity of the ladder top-k over wide page tables (more than 256 pages, where one
-workgroup per (token, KV head) finds the k-th largest key and sorts the selection):
+"""GPU parity of the ladder top-k over wide page tables (more than 256 pages: with a large
+top_k one workgroup per (token, KV head) finds the k-th largest key and sorts the
+selection, with a small one the wave kernel runs; both are exercised here):
 indices and counts bit-exact with the oracle's selection, on float scores, on integer
 scores with many exact ties and signed zeros, for top_k up to 1024 and for tokens with
 fewer valid pages than top_k."""
