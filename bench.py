@@ -137,15 +137,15 @@ def dense_algorithmic_bytes(case, staged_offsets=False):
 # other sources no longer describes the kernel.
 KERNEL_SOURCES = {
     "proxy_page_scores": ("k_proxy.hip", "device.h"),
-    "ladder_topk_pages": ("k_topk.hip", "device.h"),
+    "ladder_topk_pages": ("k_topk.hip", "device.h", "internal.h"),
     "verify_attention_sparse": ("k_attn_waves.hip", "mfma_attn.h", "sparse_union.h", "k_small.hip",
                                 "device.h", "internal.h", "sdv_api.cpp"),
     "verify_attention_sparse_select": ("k_attn_waves.hip", "mfma_attn.h", "sparse_union.h",
                                        "k_small.hip", "device.h", "internal.h", "sdv_api.cpp"),
-    "verify_attention_dense": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
-                               "internal.h", "sdv_api.cpp"),
-    "verify_attention_dense_view": ("k_attn_stream.hip", "mfma_attn.h", "k_small.hip", "device.h",
-                                    "internal.h", "sdv_api.cpp"),
+    "verify_attention_dense": ("k_attn_stream.hip", "k_attn_flat.hip", "mfma_attn.h",
+                               "k_small.hip", "device.h", "internal.h", "sdv_api.cpp"),
+    "verify_attention_dense_view": ("k_attn_stream.hip", "k_attn_flat.hip", "mfma_attn.h",
+                                    "k_small.hip", "device.h", "internal.h", "sdv_api.cpp"),
     "verify_attention_paged": ("k_attn_waves.hip", "mfma_attn.h", "k_small.hip", "device.h",
                                "internal.h", "sdv_api.cpp"),
     "greedy_accept": ("k_accept.hip", "device.h", "internal.h", "sdv_api.cpp"),
@@ -857,10 +857,11 @@ def main():
             "workload": "ragged_mixed: batch 256, qo_len 1..8, kv_len log-normal (median 2048, "
                         "clipped [64, 65536]) with page-crossing rows, 16 q / 4 kv heads, "
                         "head_dim 128, bf16, top-k 16 clamped",
+            # split counts: the fastest measured for each path (sparse 1-4, dense 2-16)
             "sparse": sparse_config_line(torch, sdv, W, wr, dev, args, flush, fam,
-                                         args.ragged_splits),
+                                         args.ragged_splits or 1),
             "dense": dense_config_line(torch, sdv, W, wr, dev, args, flush, fam,
-                                       args.ragged_dense_splits)}
+                                       args.ragged_dense_splits or 4)}
 
     # ---- target dense layers: ladder attention over ordinary head-major P128 pages ----
     if want("paged", args.no_paged):

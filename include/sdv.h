@@ -172,7 +172,12 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
  *              sub-pages over all (request, KV head) pairs divided by the workgroups
  *              the GPU holds at once (so long and short requests balance), at least
  *              ceil(longest request's sub-pages / num_splits) and at most 1024; the
- *              vector-ALU kernels take C = ceil(max_sub_pages / num_splits).
+ *              vector-ALU kernels take C = ceil(max_sub_pages / num_splits).  With at
+ *              least two (request, KV head) pairs per compute unit, num_splits >= 2,
+ *              B <= 2048 and ceil(max_sub_pages / (num_splits - 1)) <= 1024, the call
+ *              runs persistent instead: the pairs are laid end to end and every
+ *              workgroup attends an equal range of sub-pages, num_splits bounding how
+ *              many workgroups share one pair.
  *              Trailing splits of short requests are empty.  num_splits = 1 needs no
  *              workspace.  A split holds at most 1024 sub-pages, so
  *              ceil(max_sub_pages / num_splits) > 1024 is SDV_ERR_SHAPE.

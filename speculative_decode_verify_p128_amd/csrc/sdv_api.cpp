@@ -303,15 +303,22 @@ static int32_t dense_attention(const void* q, int32_t q_dt, const int32_t* qo_in
   split_workspace(workspace, rows_cap, num_q_heads, v.head_dim, num_splits, &a.part_o, &a.part_lse);
   sdv::DenseSource src{v.k_root, sub_offsets, max_sub_pages, v.num_sub_pages,
                        sub_offsets ? nullptr : block_table, bt_stride, v.index_scale, v.num_slots};
+  // Default: the per-split ring while the (request, KV head) pairs fit the GPU's resident
+  // workgroups a few times over; with more pairs than twice the compute units (the ring
+  // holds two workgroups per CU), the per-split grid queues and its imbalance compounds,
+  // so the flat persistent kernel, which gives every workgroup an equal block range, takes
+  // over (measured on the ragged 256-request batch: 378 against 432-458 us).
+  const bool many_pairs =
+      static_cast<int64_t>(B) * v.num_kv_heads >= 2ll * std::max(1, sdv::device_cu_count());
+  const bool persist_ok = sdv::persist_supported(a, max_sub_pages);
   hipError_t e;
   if (fam == kFamilyValu || !sdv::mfma_supported(a)) e = sdv::launch_attn_dense_valu(a, src, stream);
   else if (fam == kFamilyWaves) e = sdv::launch_attn_dense_waves(a, src, stream);
-  else if (fam == kFamilyPersist && sdv::persist_supported(a, max_sub_pages))
-    e = sdv::launch_attn_dense_persist(a, src, stream);
-  else if (fam == kFamilyFlat && sdv::persist_supported(a, max_sub_pages))
+  else if (fam == kFamilyPersist && persist_ok) e = sdv::launch_attn_dense_persist(a, src, stream);
+  else if ((fam == kFamilyFlat || (fam == kFamilyAuto && many_pairs)) && persist_ok)
     e = sdv::launch_attn_dense_flat(a, src, stream);
-  else e = sdv::launch_attn_dense_stream(a, src, stream);   // automatic, ring, and the
-                                                            // persistent ones that do not apply
+  else e = sdv::launch_attn_dense_stream(a, src, stream);   // the ring, and the persistent
+                                                            // kernels where they do not apply
   if (e != hipSuccess) return hip_status(e, name);
   if (num_splits > 1) {
     e = sdv::launch_combine(a.part_o, a.part_lse, num_splits, static_cast<int32_t>(rows_cap),
