@@ -441,9 +441,9 @@ int32_t stage_verify_kv_view(const void* k_new, const void* v_new, int32_t new_d
  *              16-byte aligned; vocab a multiple of 4 (F32) or 8 (BF16).
  * tokens       device int32 [rows]: the verify input tokens.
  * workspace    device, >= sdv_greedy_accept_workspace_bytes(B, max_qo_len, vocab,
- *              logits_dt) bytes, 4-byte aligned: each row's logits are reduced in
- *              parts of 4096 (F32) or 8192 (BF16) values whose maxima and indices it
- *              holds between the two launches.  Owned by the caller; contents on entry
+ *              logits_dt) bytes, 8-byte aligned: each row's logits are reduced in
+ *              parts of 4096 (F32) or 8192 (BF16) values whose maxima and indices (one
+ *              64-bit key per part) it holds between the two launches.  Owned by the caller; contents on entry
  *              ignored; calls that share it on different streams race.
  * targets_out  device int32 [B*max_qo_len]: argmax per row, for the rows of every
  *              request whose rows lie inside [0, qo_indptr[B]) (rows past qo_indptr[B]

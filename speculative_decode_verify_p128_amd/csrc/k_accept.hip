@@ -7,16 +7,20 @@
 //   1. sdv_argmax_part_kernel: each verify row's logits are cut into parts of 1024
 //      16-byte vectors (16 KiB); one 256-thread workgroup per (row, part) holds its part
 //      in registers (four non-temporal loads per thread) and writes the part's largest
-//      non-NaN value and the lowest index holding it to the workspace.  Many small
-//      workgroups keep the memory system busier than one workgroup per row (measured on
-//      256 rows x 131072 bf16 logits: 4096 part workgroups finish well ahead of 256
-//      1024-thread row workgroups).
-//   2. sdv_accept_kernel: one wave per request merges the parts of each of its rows —
-//      the largest value, ties to the earlier part, which holds the lower indices — into
-//      the target's greedy token after that row (ties to the lowest index, NaN never
-//      selected), then takes the longest prefix of drafts equal to the targets of the
-//      rows before them, emits them and the bonus target, and writes the corrected
-//      kv_len (kv_len - qo_len + 1 + accepted).
+//      non-NaN value and the lowest index holding it to the workspace, as one 64-bit key:
+//      the order-preserving bits of the value above the complemented index, so that the
+//      largest key is the largest value at the lowest index (0: a part of NaN only).
+//      Many small workgroups keep the memory system busier than one workgroup per row
+//      (measured on 256 rows x 131072 bf16 logits: 4096 part workgroups finish well
+//      ahead of 256 1024-thread row workgroups).
+//   2. sdv_accept_kernel: one wave per request takes the largest key of each of its rows
+//      — the target's greedy token after that row (ties to the lowest index, NaN never
+//      selected) — with its lanes spread over (row, part) pairs, so that every key and
+//      draft token is loaded in one round; then it takes the longest prefix of drafts
+//      equal to the targets of the rows before them, emits them and the bonus target,
+//      and writes the corrected kv_len (kv_len - qo_len + 1 + accepted).  The kernel is a
+//      chain of dependent loads (lengths, keys, outputs), so loads issued together are
+//      what its time depends on.
 #include <climits>
 
 #include "device.h"
@@ -53,8 +57,7 @@ __device__ __forceinline__ void decode16(const u32x4_acc& w, float (&x)[16 / (DT
 template <int DT>
 __global__ void __launch_bounds__(kPartThreads) sdv_argmax_part_kernel(
     const char* __restrict__ logits, int32_t vocab, int32_t parts,
-    const int32_t* __restrict__ qo_indptr, int32_t B, float* __restrict__ part_max,
-    int32_t* __restrict__ part_idx) {
+    const int32_t* __restrict__ qo_indptr, int32_t B, uint64_t* __restrict__ part_keys) {
   constexpr int EB = DT == SDV_F32 ? 4 : 2;
   constexpr int PER = 16 / EB;                 // elements per 16-byte load
   constexpr int NW = kPartThreads / kWave;
@@ -110,43 +113,30 @@ __global__ void __launch_bounds__(kPartThreads) sdv_argmax_part_kernel(
     int b = s_idx[0];
 #pragma unroll
     for (int k = 1; k < NW; ++k) b = min(b, s_idx[k]);
-    part_max[blockIdx.x] = m;
-    part_idx[blockIdx.x] = b;
+    part_keys[blockIdx.x] = b == INT_MAX ? 0ull
+                                         : (static_cast<uint64_t>(ordered_key(m)) << 32) |
+                                               static_cast<uint32_t>(~static_cast<uint32_t>(b));
   }
 }
 
-// The target after one row from its parts (parts in index order, so a strict > keeps
-// the lower index on equal values); -1 when every part held only NaN.
-__device__ __forceinline__ int merge_parts(const float* __restrict__ part_max,
-                                           const int32_t* __restrict__ part_idx, int64_t row,
-                                           int parts) {
-  const float* pm = part_max + row * parts;
-  const int32_t* pi = part_idx + row * parts;
-  float m = -INFINITY;
-  int b = INT_MAX;
-  constexpr int U = 4;
-  for (int p0 = 0; p0 < parts; p0 += U) {
-    float x[U];
-    int i[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      x[k] = p0 + k < parts ? pm[p0 + k] : -INFINITY;
-      i[k] = p0 + k < parts ? pi[p0 + k] : INT_MAX;
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k)
-      if (i[k] != INT_MAX && (b == INT_MAX || x[k] > m)) {
-        m = x[k];
-        b = i[k];
-      }
-  }
-  return b == INT_MAX ? -1 : b;
+__device__ __forceinline__ int key_target(uint64_t k) {
+  return k == 0 ? -1 : static_cast<int>(~static_cast<uint32_t>(k));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, kWave));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), off, kWave));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 constexpr int kAcceptThreads = 256;   // four requests per workgroup, one wave each
 
+// pshift: log2 of the lane segment that holds one row's parts (parts <= 64), or -1 when
+// a row has more than 64 parts (then rows are merged one after another).
 __global__ void __launch_bounds__(kAcceptThreads) sdv_accept_kernel(
-    const float* __restrict__ part_max, const int32_t* __restrict__ part_idx, int32_t parts,
+    const uint64_t* __restrict__ part_keys, int32_t parts, int32_t pshift,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ kv_len, int32_t B, int32_t max_qo_len,
     int32_t* __restrict__ targets, int32_t* __restrict__ accept, int32_t* __restrict__ emitted,
@@ -161,11 +151,58 @@ __global__ void __launch_bounds__(kAcceptThreads) sdv_accept_kernel(
   int32_t* em = emitted + static_cast<int64_t>(r) * max_qo_len;
   const bool rows_ok = row0 >= 0 && qo >= 1 && static_cast<int64_t>(row0) + qo <= rows &&
                        static_cast<int64_t>(row0) + qo <= static_cast<int64_t>(B) * max_qo_len;
-  if (!rows_ok || qo > max_qo_len || kv < qo) {
-    // the rows, when they lie inside the batch, still get their targets
-    if (rows_ok)
-      for (int t = lane; t < qo; t += kWave)
-        targets[row0 + t] = merge_parts(part_max, part_idx, row0 + t, parts);
+  const bool usable = rows_ok && qo <= max_qo_len && kv >= qo;
+  // Targets of the request's rows (also when its other lengths are unusable, as long as
+  // its rows lie inside the batch); the first row t < qo - 1 whose target differs from
+  // draft t + 1 ends the accepted prefix (a = qo - 1 when none does).
+  int a = qo - 1;
+  int tgt_a = 0;
+  bool found = !usable;
+  if (rows_ok && pshift >= 0) {
+    const int seg = 1 << pshift;           // lanes per row, >= parts
+    const int rpp = kWave >> pshift;       // rows per pass
+    const int sub = lane >> pshift;
+    const int p = lane & (seg - 1);
+    for (int t0 = 0; t0 < qo; t0 += rpp) {
+      const int t = t0 + sub;
+      uint64_t k = 0;
+      int draft = 0;
+      if (t < qo && p < parts) k = part_keys[(static_cast<int64_t>(row0) + t) * parts + p];
+      if (p == 0 && t < qo - 1) draft = tokens[row0 + t + 1];
+      for (int off = seg >> 1; off >= 1; off >>= 1) k = max_u64(k, shfl_xor_u64(k, off));
+      const int tg = key_target(k);
+      const bool lead = p == 0 && t < qo;
+      if (lead) targets[row0 + t] = tg;
+      if (!found) {
+        const uint64_t mb = __ballot(lead && t < qo - 1 && draft != tg);
+        const uint64_t last = __ballot(lead && t == qo - 1);
+        if (mb) {
+          const int l = __builtin_ctzll(mb);
+          a = t0 + (l >> pshift);
+          tgt_a = __shfl(tg, l, kWave);
+          found = true;
+        } else if (last) {
+          tgt_a = __shfl(tg, __builtin_ctzll(last), kWave);
+          found = true;
+        }
+      }
+    }
+  } else if (rows_ok) {
+    for (int t = 0; t < qo; ++t) {
+      const uint64_t* pk = part_keys + (static_cast<int64_t>(row0) + t) * parts;
+      uint64_t k = 0;
+      for (int p = lane; p < parts; p += kWave) k = max_u64(k, pk[p]);
+      for (int off = kWave >> 1; off >= 1; off >>= 1) k = max_u64(k, shfl_xor_u64(k, off));
+      const int tg = key_target(k);
+      if (lane == 0) targets[row0 + t] = tg;
+      if (!found && (t == qo - 1 || tokens[row0 + t + 1] != tg)) {
+        a = t;
+        tgt_a = tg;
+        found = true;
+      }
+    }
+  }
+  if (!usable) {
     if (lane == 0) {
       set_err(dev_err, SDV_DEVERR_QO_LEN);
       accept[r] = -1;
@@ -173,34 +210,6 @@ __global__ void __launch_bounds__(kAcceptThreads) sdv_accept_kernel(
     }
     for (int t = lane; t < max_qo_len; t += kWave) em[t] = -1;
     return;
-  }
-  // Targets of the request's rows, 64 at a time; the first row t < qo - 1 whose target
-  // differs from draft t + 1 ends the accepted prefix (a = qo - 1 when none does).
-  int a = qo - 1;
-  int tgt_a = 0;
-  bool found = false;
-  for (int t0 = 0; t0 < qo; t0 += kWave) {
-    const int t = t0 + lane;
-    int tg = 0;
-    bool miss = false;
-    if (t < qo) {
-      tg = merge_parts(part_max, part_idx, row0 + t, parts);
-      targets[row0 + t] = tg;
-      miss = t < qo - 1 && tokens[row0 + t + 1] != tg;
-    }
-    if (!found) {
-      const uint64_t mb = __ballot(miss);
-      const uint64_t last = __ballot(t == qo - 1);
-      if (mb) {
-        const int l = __builtin_ctzll(mb);
-        a = t0 + l;
-        tgt_a = __shfl(tg, l, kWave);
-        found = true;
-      } else if (last) {
-        tgt_a = __shfl(tg, __builtin_ctzll(last), kWave);
-        found = true;
-      }
-    }
   }
   for (int t = lane; t < max_qo_len; t += kWave)
     em[t] = t < a ? tokens[row0 + t + 1] : (t == a ? tgt_a : -1);
@@ -225,22 +234,26 @@ hipError_t launch_greedy_accept(const void* logits, int32_t logits_dt, int32_t v
                                 hipStream_t s) {
   const int32_t parts = greedy_accept_parts(vocab, logits_dt);
   const int64_t rows_cap = static_cast<int64_t>(B) * max_qo_len;
-  float* part_max = reinterpret_cast<float*>(workspace);
-  int32_t* part_idx = reinterpret_cast<int32_t*>(part_max + rows_cap * parts);
+  uint64_t* part_keys = reinterpret_cast<uint64_t*>(workspace);
+  int32_t pshift = -1;
+  if (parts <= kWave) {
+    pshift = 0;
+    while ((1 << pshift) < parts) ++pshift;
+  }
   const dim3 grid(static_cast<uint32_t>(rows_cap * parts));
   if (logits_dt == SDV_F32)
     hipLaunchKernelGGL(sdv_argmax_part_kernel<SDV_F32>, grid, dim3(kPartThreads), 0, s,
                        reinterpret_cast<const char*>(logits), vocab, parts, qo_indptr, B,
-                       part_max, part_idx);
+                       part_keys);
   else
     hipLaunchKernelGGL(sdv_argmax_part_kernel<SDV_BF16>, grid, dim3(kPartThreads), 0, s,
                        reinterpret_cast<const char*>(logits), vocab, parts, qo_indptr, B,
-                       part_max, part_idx);
+                       part_keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPW = kAcceptThreads / kWave;
   hipLaunchKernelGGL(sdv_accept_kernel, dim3((B + RPW - 1) / RPW), dim3(kAcceptThreads), 0, s,
-                     part_max, part_idx, parts, tokens, qo_indptr, kv_len, B, max_qo_len,
+                     part_keys, parts, pshift, tokens, qo_indptr, kv_len, B, max_qo_len,
                      targets, accept, emitted, new_kv_len, dev_err);
   return hipGetLastError();
 }

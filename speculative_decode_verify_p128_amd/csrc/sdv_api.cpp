@@ -633,8 +633,8 @@ int32_t greedy_accept(const void* logits, int32_t logits_dt, int32_t vocab,
   if (workspace_bytes < need)
     return fail(SDV_ERR_WORKSPACE, "workspace holds %zu bytes, the call needs %zu",
                 workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
-    return fail(SDV_ERR_SHAPE, "workspace must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+    return fail(SDV_ERR_SHAPE, "workspace must be 8-byte aligned");
   return hip_status(sdv::launch_greedy_accept(logits, logits_dt, vocab, tokens, qo_indptr, kv_len,
                                               B, max_qo_len, workspace, targets_out, accept_out,
                                               emitted_out, new_kv_len_out, dev_err, stream),

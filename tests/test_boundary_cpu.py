@@ -280,7 +280,7 @@ def test_greedy_accept_rejections():
     assert lib.greedy_accept(*args(L.SDV_BF16, 1024, logits=C.c_void_p(0x10008))) == L.SDV_ERR_SHAPE
     # 2 requests x 4 rows x 2 parts x 8 bytes = 128
     assert lib.greedy_accept(*args(L.SDV_BF16, 16384, wsb=127)) == L.SDV_ERR_WORKSPACE
-    assert lib.greedy_accept(*args(L.SDV_BF16, 16384, ws=C.c_void_p(0x10002))) == L.SDV_ERR_SHAPE
+    assert lib.greedy_accept(*args(L.SDV_BF16, 16384, ws=C.c_void_p(0x10004))) == L.SDV_ERR_SHAPE
 
 
 def test_read_units_probe_rejections():

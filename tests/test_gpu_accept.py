@@ -2,7 +2,8 @@
 bf16 and f32 logits, rows with two equal maxima and with NaN, ragged qo_len including
 decode rows, vocabularies that span several row parts (ragged last part, equal maxima in
 different parts, NaN-only parts), the full benchmark vocabulary on sampled requests, a
-reused workspace, and the length flag."""
+reused workspace, repeated calls, and the length flag (the flagged request's rows still
+get their targets)."""
 import numpy as np
 import pytest
 import torch
@@ -119,6 +120,26 @@ def test_accept_reused_workspace_smaller_second_call():
     _check(c2, out2)
 
 
+def test_accept_repeated_calls_same_outputs():
+    """Many calls on one workspace, with the host reading back in between: identical
+    outputs every time."""
+    w = W.SPARSE_BF16.scaled(name="accept_rep", batch=16)
+    c = W.make_accept_case(w, 2 * 8192 + 16, tie_rows=0.3, nan_rows=0.1)
+    dev_in = [t.to(DEV) for t in (c.logits, c.tokens, c.qo_indptr, c.kv_len)]
+    need = sdv.greedy_accept_workspace_bytes(w.batch, w.max_qo(), 2 * 8192 + 16, torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    first = None
+    for _ in range(20):
+        out = sdv.greedy_accept(*dev_in, max_qo_len=w.max_qo(), workspace=ws)
+        got = [t.cpu().clone() for t in out]
+        if first is None:
+            first = got
+            _check(c, out)
+        else:
+            for a, b in zip(first, got):
+                assert torch.equal(a, b)
+
+
 def test_accept_full_vocab_sampled():
     w = W.SPARSE_BF16
     c = W.make_accept_case(w, VOCAB_FULL, device=DEV)
@@ -142,10 +163,15 @@ def test_accept_flags_bad_lengths():
     kv = c.kv_len.clone()
     kv[1] = 2                                          # kv_len < qo_len
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    _, accept, emitted, new_kv = sdv.greedy_accept(c.logits.to(DEV), c.tokens.to(DEV),
-                                                   c.qo_indptr.to(DEV), kv.to(DEV),
-                                                   max_qo_len=4, dev_err=err)
+    targets, accept, emitted, new_kv = sdv.greedy_accept(c.logits.to(DEV), c.tokens.to(DEV),
+                                                         c.qo_indptr.to(DEV), kv.to(DEV),
+                                                         max_qo_len=4, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) & sdv._lib.DEVERR_QO_LEN
     assert int(accept[1]) == -1 and int(new_kv[1]) == 2 and bool((emitted[1] == -1).all())
     assert int(accept[0]) >= 0 and int(accept[2]) >= 0
+    # the flagged request's rows still get their targets
+    ind = c.qo_indptr.numpy()
+    tg, _, _, _ = oracle.greedy_accept_request(c.logits.float().numpy()[ind[1]:ind[2]],
+                                               c.tokens.numpy()[ind[1]:ind[2]], int(c.lengths.kv[1]))
+    assert list(targets[ind[1]:ind[2]].cpu().numpy()) == list(tg)
