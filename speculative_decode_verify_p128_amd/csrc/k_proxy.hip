@@ -14,9 +14,12 @@
 //
 // Design (HBM-bound; K of every valid page is read exactly once for all tokens):
 //   one workgroup = one wave per (request, KV head, run of 64/LPR pages); a group of
-//   LPR lanes owns one page, each lane a contiguous 16-byte slice of every key row (8
-//   bf16, 16 fp8 or 4 f32 channels), so each wave load instruction reads 64/LPR full
-//   page rows.  Small workgroups keep the tail of the grid short when requests differ
+//   LPR lanes owns one page, each lane a contiguous slice of every key row (16 bytes:
+//   8 bf16 or 4 f32 channels; 8 bytes: 8 fp8 channels), so each wave load instruction
+//   reads 64/LPR full page rows.  fp8 takes 8-byte slices so that a wave holds four
+//   pages rather than eight: on 8 x 131072 fp8 tokens (32 pairs of 1024 pages) the
+//   16-byte form fills the GPU with exactly one generation of waves and nothing
+//   evens out their finishing times (104.9 against 98.3 us, same scores bit for bit).  Small workgroups keep the tail of the grid short when requests differ
 //   in length.  Each lane keeps 16 rows in flight; the loads are non-temporal (the keys
 //   are read once, so they should not displace what the caches hold), which measured
 //   about 20% faster than ordinary loads on this streaming pattern.  A lane keeps its channels' running sums in registers and
@@ -42,6 +45,42 @@ __device__ __forceinline__ uint4 load_stream(const char* p) {
 }
 
 constexpr int kProxyWaves = 1;   // waves per workgroup
+
+// A lane's slice of a key row: VB bytes loaded non-temporally and decoded to N floats.
+// 16-byte slices for every format; fp8 rows may also be cut in 8-byte slices (8
+// channels a lane, sixteen lanes and so four pages a wave instead of eight), which
+// doubles the number of waves of a launch.
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+
+template <int KDT, int VB>
+struct ProxyVec {
+  static_assert(VB == 16, "16-byte slices");
+  using Raw = uint4;
+  static constexpr int N = Vec16<KDT>::N;
+  __device__ __forceinline__ static Raw load(const char* p) { return load_stream(p); }
+  __device__ __forceinline__ static void decode(const Raw& w, float* out) { Vec16<KDT>::decode(w, out); }
+};
+
+template <>
+struct ProxyVec<SDV_FP8_E4M3, 8> {
+  using Raw = uint2;
+  static constexpr int N = 8;
+  __device__ __forceinline__ static Raw load(const char* p) {
+    return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p)));
+  }
+  __device__ __forceinline__ static void decode(const Raw& w, float* out) {
+    fp8x2_to_f32<false>(w.x, out[0], out[1]);
+    fp8x2_to_f32<true>(w.x, out[2], out[3]);
+    fp8x2_to_f32<false>(w.y, out[4], out[5]);
+    fp8x2_to_f32<true>(w.y, out[6], out[7]);
+  }
+};
+
+#ifndef SDV_PROXY_FP8_VB
+#define SDV_PROXY_FP8_VB 8
+#endif
+template <int KDT>
+constexpr int proxy_vb() { return KDT == SDV_FP8_E4M3 ? SDV_PROXY_FP8_VB : 16; }
 
 // Value of lane l + OFF for lane l, valid where l % 16 + OFF < 16 (and for every lane
 // when OFF >= 16); the halving tree reads it only in lanes whose partner is OFF above.
@@ -74,8 +113,8 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     int32_t G, const void* __restrict__ kbase, int64_t page_stride, int32_t num_pages,
     const int32_t* __restrict__ block_table, int32_t bt_stride, int32_t max_pages,
     float* __restrict__ scores, int32_t* dev_err) {
-  using V16 = Vec16<KDT>;
-  constexpr int V = V16::N;          // channels per lane
+  using PV = ProxyVec<KDT, proxy_vb<KDT>()>;
+  constexpr int V = PV::N;           // channels per lane
   constexpr int LPR = D / V;         // lanes per page
   constexpr int PPW = kWave / LPR;   // pages per wave
   constexpr int PPB = PPW * kProxyWaves;   // pages per workgroup
@@ -162,7 +201,7 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   if (!active) phys = 0;
   const char* kp = reinterpret_cast<const char*>(kbase) +
                    (static_cast<int64_t>(phys) * page_stride + static_cast<int64_t>(h) * kPage * D) * EB +
-                   sub * 16;
+                   sub * proxy_vb<KDT>();
   constexpr int ROW_BYTES = D * EB;
 
   float acc[V];
@@ -181,7 +220,7 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   // rows rb .. rb + U - 1 stay in w across tokens (rb < 0: w holds no such stretch), so
   // the remainder rows of every token (the last token's bound ends up to qo - 1 rows
   // further) come from one batch of loads instead of one load after another.
-  uint4 w[U];
+  typename PV::Raw w[U];
   int rb = -1;
   for (int t = 0; t < qo; ++t) {
     const int L = rows_below(t);
@@ -190,11 +229,11 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
       rb = -1;
       const char* rows = kp + static_cast<int64_t>(j) * ROW_BYTES;
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[u] = load_stream(rows + u * ROW_BYTES);
+      for (int u = 0; u < U; ++u) w[u] = PV::load(rows + u * ROW_BYTES);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[V];
-        V16::decode(w[u], x);
+        PV::decode(w[u], x);
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
       }
@@ -207,13 +246,13 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
         const int last = (rb + U < L_last ? rb + U : L_last) - 1;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          w[u] = load_stream(kp + static_cast<int64_t>(rb + u < last ? rb + u : last) * ROW_BYTES);
+          w[u] = PV::load(kp + static_cast<int64_t>(rb + u < last ? rb + u : last) * ROW_BYTES);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (rb + u >= j && rb + u < L) {
           float x[V];
-          V16::decode(w[u], x);
+          PV::decode(w[u], x);
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[e] = acc[e] + x[e];
         }
@@ -257,7 +296,7 @@ static hipError_t launch_proxy_t(const void* q, int32_t q_dt, const int32_t* qo_
                                  int32_t num_q_heads, const sdv_paged_kv& kv,
                                  const int32_t* block_table, int32_t max_pages, int32_t bt_stride,
                                  float* scores, int32_t* dev_err, hipStream_t s) {
-  constexpr int V = Vec16<KDT>::N;
+  constexpr int V = ProxyVec<KDT, proxy_vb<KDT>()>::N;
   constexpr int PPB = (kWave / (D / V)) * kProxyWaves;
   const int G = num_q_heads / kv.num_kv_heads;
   const size_t lds = static_cast<size_t>(max_qo_len) * G * D * sizeof(float);

@@ -32,6 +32,9 @@ LONG_S = W.LONG_FP8.scaled(name="long_small", batch=2, kv=("fixed", 5000), kv_ca
 D64 = W.SPARSE_BF16.scaled(name="d64", batch=3, kv=("uniform", 130, 1000), kv_capacity=1024,
                            head_dim=64, num_q_heads=8, num_kv_heads=2, top_k=3)
 
+D64_FP8 = W.LONG_FP8.scaled(name="d64_fp8", batch=3, kv=("uniform", 130, 1500), kv_capacity=1536,
+                            head_dim=64, num_q_heads=8, num_kv_heads=2, top_k=3)
+
 DENSE_CASES = [TINY, DENSE_S, DENSE_S_FP8, RAGGED_S]
 SPARSE_CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64]
 
@@ -86,7 +89,7 @@ def test_dense_parity(w, splits, family):
     assert ok, f"max abs err {worst}"
 
 
-@pytest.mark.parametrize("w", SPARSE_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", SPARSE_CASES + [D64_FP8], ids=lambda w: w.name)
 def test_proxy_scores_bit_exact(w):
     c = W.make_sparse_case(w)
     run = SparseRun(c)
