@@ -15,12 +15,15 @@
 // cache (wave_ladder_topk, shared with the selection inside the sparse attention
 // kernels).
 //
-// Wide tables with a large top_k take one 256-thread workgroup per (token row, KV head)
-// instead, whose cost does not grow with top_k: with the same 64-bit keys (unique, because the
-// page is part of the key), the k_eff-th largest key T is found bit by bit from the top
-// (the largest T that at least k_eff keys reach; the page word's high bits are the same
-// in every key and are set at once), the keys >= T -- exactly the selection -- are
-// gathered into LDS, and a bitonic network sorts them into rank order.
+// Wide tables with a large top_k take a search whose cost does not grow with top_k
+// instead, still one wave per (token row, KV head): with the same 64-bit keys (unique,
+// because the page is part of the key), the k_eff-th largest key T is found bit by bit
+// from the top (the largest T that at least k_eff keys reach, each count a wave sum; the
+// page word's high bits are the same in every key and are set at once), the keys >= T
+// -- exactly the selection -- are gathered, and a bitonic network sorts them into rank
+// order (lane shuffles for up to 64 keys, LDS beyond).  Measured on 1024 pages, top-64,
+// 128 rows: 31.6 us for the repeated-maximum wave kernel, 18.2 us for the same search
+// by a 256-thread workgroup (a barrier per bit), 15.7 us for one wave.
 #include "device.h"
 #include "internal.h"
 
@@ -75,23 +78,30 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
 }
 
-constexpr int kWideThreads = 256;
-constexpr int kWideMaxK = 1024;     // selections a workgroup sorts (top_k <= 1024)
+constexpr int kWideMaxK = 1024;     // selections a wave sorts (top_k <= 1024)
 
+// 64-bit shuffle (two 32-bit halves).
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, kWave));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), off, kWave));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// The same selection by one wave per (token row, KV head): lane l holds the keys of pages
+// l + 64 i, the bit search counts with wave sums only (no barrier), and a selection of
+// up to 64 keys is sorted in registers by a bitonic network of lane shuffles (larger
+// selections go through LDS).
 template <int ITEMS>
-__global__ void __launch_bounds__(kWideThreads) sdv_topk_wide_kernel(
+__global__ void __launch_bounds__(kWave) sdv_topk_bits_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ kv_len, int32_t B, int32_t max_qo_len, int32_t Hkv,
     int32_t max_pages, int32_t top_k, int32_t* __restrict__ topk_idx,
     int32_t* __restrict__ topk_cnt, int32_t* dev_err) {
   __shared__ uint64_t sel[kWideMaxK];
-  __shared__ uint32_t part[2][kWideThreads / kWave];
   const int t = blockIdx.x;
   const int h = blockIdx.y;
   const int r = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int lane = threadIdx.x;
   const int row0 = qo_indptr[r];
   const int qo = qo_indptr[r + 1] - row0;
   const int kv = kv_len[r];
@@ -99,51 +109,35 @@ __global__ void __launch_bounds__(kWideThreads) sdv_topk_wide_kernel(
                        static_cast<int64_t>(row0) + qo > static_cast<int64_t>(B) * max_qo_len;
   const bool bad_cap = !bad_len && static_cast<int64_t>(kv) > static_cast<int64_t>(max_pages) * kPage;
   if (bad_len || bad_cap) {
-    if (tid == 0 && t == 0 && h == 0)
+    if (lane == 0 && t == 0 && h == 0)
       set_err(dev_err, bad_len ? SDV_DEVERR_QO_LEN : SDV_DEVERR_KV_CAPACITY);
     return;
   }
-  if (t >= qo) return;                       // uniform over the workgroup
+  if (t >= qo) return;
   const int bound = kv - qo + t + 1;
   const int n = (bound + kPage - 1) / kPage;
   const int64_t row = row0 + t;
   const float* srow = scores + (row * Hkv + h) * max_pages;
 
-  // keys of pages tid + 256 i (0 past the token's valid pages; a valid key is never 0)
   uint64_t key[ITEMS];
   float sv[ITEMS];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) sv[i] = srow[min(tid + kWideThreads * i, n - 1)];
+  for (int i = 0; i < ITEMS; ++i) sv[i] = srow[min(lane + kWave * i, n - 1)];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int p = tid + kWideThreads * i;
+    const int p = lane + kWave * i;
     key[i] = p < n ? (static_cast<uint64_t>(ordered_key(sv[i])) << 32) |
                          static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(p))
                    : 0ull;
   }
   const int k_eff = top_k < n ? top_k : n;
-
-  // Number of keys >= c over the workgroup (one barrier; the partial sums alternate
-  // between two buffers, so a buffer is rewritten only after every thread has read it).
-  int it = 0;
   auto count_ge = [&](uint64_t c) {
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) m += key[i] >= c ? 1u : 0u;
-    m = wave_sum_u32(m);
-    const int buf = it++ & 1;
-    if (lane == 0) part[buf][wave] = m;
-    __syncthreads();
-    uint32_t s = 0;
-#pragma unroll
-    for (int w = 0; w < kWideThreads / kWave; ++w) s += part[buf][w];
-    return s;
+    return wave_sum_u32(m);
   };
-
-  // T: the largest value that at least k_eff keys reach, which (keys being unique) is
-  // the k_eff-th largest key.  With k_eff = n every valid key is taken (T = 1).  Every
-  // valid key's page word is 0xffffffff - p with p < 4096, so once the score word is
-  // fixed its bits 31..12 are ones and only bits 11..0 remain.
+  // T as in the workgroup kernel: the k_eff-th largest key.
   uint64_t T = 1;
   if (k_eff < n) {
     T = 0;
@@ -158,52 +152,73 @@ __global__ void __launch_bounds__(kWideThreads) sdv_topk_wide_kernel(
     }
   }
 
-  // the k_eff keys >= T into sel[0 .. k_eff), in any order
-  uint32_t mine = 0;
+  int32_t* out = topk_idx + (row * Hkv + h) * top_k;
+  if (k_eff <= kWave) {
+    // the selection, one key a lane (0 past k_eff): lane order = page order
+    uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
-  uint32_t incl = mine;
+    for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
+    uint32_t incl = mine;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t v = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += v;
-  }
-  const int buf = it++ & 1;
-  if (lane == kWave - 1) part[buf][wave] = incl;
-  __syncthreads();
-  uint32_t pos = incl - mine;
-  for (int w = 0; w < wave; ++w) pos += part[buf][w];
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += v;
+    }
+    uint32_t pos = incl - mine;
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i)
-    if (key[i] >= T) sel[pos++] = key[i];
-  // pad to a power of two with 0 keys, which sort last
-  int p2 = 1;
-  while (p2 < k_eff) p2 <<= 1;
-  for (int j = k_eff + tid; j < p2; j += kWideThreads) sel[j] = 0ull;
-  __syncthreads();
-
-  // bitonic sort of sel[0 .. p2) into descending order
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < p2; i += kWideThreads) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint64_t a = sel[i], b = sel[l];
-          const bool swap = (i & k) == 0 ? a < b : a > b;
-          if (swap) {
-            sel[i] = b;
-            sel[l] = a;
+    for (int i = 0; i < ITEMS; ++i)
+      if (key[i] >= T) sel[pos++] = key[i];
+    __syncthreads();
+    uint64_t v = lane < k_eff ? sel[lane] : 0ull;
+    // bitonic network, descending: in a block whose lane bit k is 0 the lower lane of
+    // each pair keeps the larger key
+    for (int k = 2; k <= kWave; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const uint64_t o = shfl_xor_u64(v, j);
+        const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+        v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+      }
+    // lane k holds rank k
+    if (lane < top_k) out[lane] = lane < k_eff ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(v)) : -1;
+    for (int k = kWave + lane; k < top_k; k += kWave) out[k] = -1;
+  } else {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
+    uint32_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += v;
+    }
+    uint32_t pos = incl - mine;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (key[i] >= T) sel[pos++] = key[i];
+    int p2 = 1;
+    while (p2 < k_eff) p2 <<= 1;
+    for (int j = k_eff + lane; j < p2; j += kWave) sel[j] = 0ull;
+    __syncthreads();
+    for (int k = 2; k <= p2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = lane; i < p2; i += kWave) {
+          const int l = i ^ j;
+          if (l > i) {
+            const uint64_t a = sel[i], b = sel[l];
+            const bool swap = (i & k) == 0 ? a < b : a > b;
+            if (swap) {
+              sel[i] = b;
+              sel[l] = a;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
+    for (int k = lane; k < top_k; k += kWave)
+      out[k] = k < k_eff ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(sel[k])) : -1;
   }
-
-  int32_t* out = topk_idx + (row * Hkv + h) * top_k;
-  for (int k = tid; k < top_k; k += kWideThreads)
-    out[k] = k < k_eff ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(sel[k])) : -1;
-  if (topk_cnt && tid == 0) topk_cnt[row * Hkv + h] = k_eff;
+  if (topk_cnt && lane == 0) topk_cnt[row * Hkv + h] = k_eff;
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int32_t* kv_len,
@@ -211,25 +226,24 @@ hipError_t launch_topk(const float* scores, const int32_t* qo_indptr, const int3
                        int32_t top_k, int32_t* topk_idx, int32_t* topk_cnt, int32_t* dev_err,
                        hipStream_t s) {
   dim3 grid(max_qo_len, num_kv_heads, B);
-  // The wave kernel's rounds cost about top_k x (items + 8) dependent instructions, the
-  // workgroup kernel's bit search about 44 x (items / 4 + 20) plus a sort: the workgroup
-  // kernel takes tables over 256 pages where the first is the larger (measured: 1024
-  // pages, top-64, 31.6 -> 17.1 us; 512 pages, top-16, the wave kernel is faster).
+  // The repeated-maximum rounds cost about top_k x (items + 8) dependent instructions,
+  // the bit search 44 rounds and a sort whatever top_k is: the bit search takes tables
+  // over 256 pages where the first passes 1200 (measured: 1024 pages, top-64, 31.6 ->
+  // 15.7 us; 512 pages, top-16, the repeated maximum is faster).
   const int items = (max_pages + kWave - 1) / kWave;
   if (max_pages > 256 && top_k * (items + 8) > 1200) {
-    const int witems = (max_pages + kWideThreads - 1) / kWideThreads;
-#define SDV_TOPK_WIDE_CASE(N)                                                                \
-    if (witems <= N) {                                                                       \
-      hipLaunchKernelGGL(sdv_topk_wide_kernel<N>, grid, dim3(kWideThreads), 0, s, scores,     \
-                         qo_indptr, kv_len, B, max_qo_len, num_kv_heads, max_pages, top_k,   \
-                         topk_idx, topk_cnt, dev_err);                                       \
+#define SDV_TOPK_BITS_CASE(N)                                                                \
+    if (items <= N) {                                                                        \
+      hipLaunchKernelGGL(sdv_topk_bits_kernel<N>, grid, dim3(kWave), 0, s, scores, qo_indptr, \
+                         kv_len, B, max_qo_len, num_kv_heads, max_pages, top_k, topk_idx,    \
+                         topk_cnt, dev_err);                                                 \
       return hipGetLastError();                                                              \
     }
-    SDV_TOPK_WIDE_CASE(2)
-    SDV_TOPK_WIDE_CASE(4)
-    SDV_TOPK_WIDE_CASE(8)
-    SDV_TOPK_WIDE_CASE(16)
-#undef SDV_TOPK_WIDE_CASE
+    SDV_TOPK_BITS_CASE(8)
+    SDV_TOPK_BITS_CASE(16)
+    SDV_TOPK_BITS_CASE(32)
+    SDV_TOPK_BITS_CASE(64)
+#undef SDV_TOPK_BITS_CASE
     return hipErrorInvalidValue;
   }
 #define SDV_TOPK_CASE(N)                                                                     \
