@@ -47,9 +47,9 @@ __device__ __forceinline__ uint4 load_stream(const char* p) {
 constexpr int kProxyWaves = 1;   // waves per workgroup
 
 // A lane's slice of a key row: VB bytes loaded non-temporally and decoded to N floats.
-// 16-byte slices for every format; fp8 rows may also be cut in 8-byte slices (8
-// channels a lane, sixteen lanes and so four pages a wave instead of eight), which
-// doubles the number of waves of a launch.
+// 16-byte slices for f32 and bf16; fp8 rows are cut in 8-byte slices (8 channels a
+// lane, sixteen lanes and so four pages a wave instead of eight), which doubles the
+// number of waves of a launch.
 typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
 
 template <int KDT, int VB>
@@ -76,11 +76,8 @@ struct ProxyVec<SDV_FP8_E4M3, 8> {
   }
 };
 
-#ifndef SDV_PROXY_FP8_VB
-#define SDV_PROXY_FP8_VB 8
-#endif
 template <int KDT>
-constexpr int proxy_vb() { return KDT == SDV_FP8_E4M3 ? SDV_PROXY_FP8_VB : 16; }
+constexpr int proxy_vb() { return KDT == SDV_FP8_E4M3 ? 8 : 16; }
 
 // Value of lane l + OFF for lane l, valid where l % 16 + OFF < 16 (and for every lane
 // when OFF >= 16); the halving tree reads it only in lanes whose partner is OFF above.

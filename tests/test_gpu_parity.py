@@ -177,13 +177,17 @@ def test_sparse_with_every_page_equals_dense(w):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_combine_parity(D, out_dtype):
-    rng = np.random.default_rng(D)
-    S, R, H = 7, 19, 3
+@pytest.mark.parametrize("S", [1, 3, 4, 7, 16, 23])   # chunks of 4, 8, 16; 23: two chunks
+def test_combine_parity(D, out_dtype, S):
+    rng = np.random.default_rng(D + 100 * S)
+    R, H = 19, 3
     po = rng.standard_normal((S, R, H, D)).astype(np.float32)
     pl = (rng.standard_normal((S, R, H)) * 3).astype(np.float32)
     pl[rng.random((S, R, H)) < 0.3] = -np.inf
     pl[:, 4, 1] = -np.inf                                 # a row with no live partial
+    if S > 16:
+        pl[:16, 6, 2] = -np.inf                           # live partials only in the second chunk
+        pl[16:, 7, 0] = -np.inf                           # ... only in the first
     po[pl == -np.inf] = np.nan                            # never read
     out, lse = sdv.lse_combine(torch.from_numpy(po).to(DEV), torch.from_numpy(pl).to(DEV),
                                out_dtype=out_dtype, want_lse=True)
