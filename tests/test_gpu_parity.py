@@ -154,6 +154,35 @@ def test_sparse_parity(w, splits, family):
     assert ok, f"max abs err {worst}"
 
 
+RAGGED_MANY = W.RAGGED_MIXED.scaled(name="ragged_many", batch=48,
+                                    kv=("lognormal", 300, 1.0, 1, 1500, 0.25), kv_capacity=1536)
+RAGGED_MANY_FP8 = RAGGED_MANY.scaled(name="ragged_many_fp8", kv_dtype="fp8")
+
+
+@pytest.mark.parametrize("splits", [4, 8])
+@pytest.mark.parametrize("w", [RAGGED_MANY, RAGGED_MANY_FP8], ids=lambda w: w.name)
+def test_sparse_many_workgroups(w, splits):
+    """Ragged 32-row (request, KV head) pairs, bf16 and fp8, in launches of several
+    workgroups per CU: the standalone and the fused-selection forms against the oracle,
+    and bit-identical to each other."""
+    c = W.make_sparse_case(w)
+    run = SparseRun(c)
+    scores = run.scores()
+    idx, _ = run.topk(scores)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = run.attend(idx, num_splits=splits, dev_err=err)
+    fused = sdv.verify_attention_sparse_select(run.q, run.qo_indptr, run.kv_len, run.kv, run.bt,
+                                               scores, max_qo_len=run.max_qo, top_k=w.top_k,
+                                               softmax_scale=c.softmax_scale, num_splits=splits,
+                                               dev_err=err)
+    torch.cuda.synchronize()
+    ref = sparse_oracle(c)
+    assert int(err.item()) == 0
+    ok, worst = tol_ok(out_numpy(out[:run.n]), ref["out"], "bf16")
+    assert ok, f"max abs err {worst}"
+    assert torch.equal(out[:run.n].view(torch.int16), fused[:run.n].view(torch.int16))
+
+
 @pytest.mark.parametrize("w", [TINY, SPARSE_S], ids=lambda w: w.name)
 def test_sparse_with_every_page_equals_dense(w):
     c = W.make_sparse_case(w)
