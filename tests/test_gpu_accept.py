@@ -100,6 +100,23 @@ def test_accept_several_parts(dt, vocab):
         assert ref["targets"][1] == per_part + 7
 
 
+@pytest.mark.parametrize("dt,vocab", [(torch.bfloat16, 65 * 8192 + 8), (torch.float32, 70 * 4096 + 4)],
+                         ids=["bf16_66_parts", "f32_71_parts"])
+def test_accept_more_than_64_parts(dt, vocab):
+    """Rows of more than 64 parts, whose keys the acceptance wave merges row by row (lanes
+    over parts) instead of spreading (row, part) pairs over its lanes."""
+    w = W.SPARSE_BF16.scaled(name="accept_wide", batch=2)
+    c = W.make_accept_case(w, vocab, dtype=dt, tie_rows=0.4, nan_rows=0.2)
+    x = c.logits
+    per_part = 8192 if dt == torch.bfloat16 else 4096
+    x[0, :] = -1.0
+    x[0, 64 * per_part + 3] = 7.0                      # maximum in a part past the 64th
+    x[0, 2] = 7.0                                      # ... and the same value in part 0: wins
+    x[1, :] = -1.0
+    x[1, vocab - 1] = 9.0                              # in the last, ragged part
+    _check(c, _run(c, w.max_qo()))
+
+
 def test_accept_reused_workspace_smaller_second_call():
     """One workspace and output set serve two calls in a row, the second with fewer
     requests and a smaller vocabulary: stale part results of the first call must not
