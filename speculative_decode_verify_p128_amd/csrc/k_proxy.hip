@@ -13,24 +13,27 @@
 //   4. maximum over the G query heads; -0 becomes +0.
 //
 // Design (HBM-bound; K of every valid page is read exactly once for all tokens):
-//   one workgroup = one wave per (request, KV head, run of 64/LPR pages); a group of
-//   LPR lanes owns one page, each lane a contiguous slice of every key row (16 bytes:
-//   8 bf16 or 4 f32 channels; 8 bytes: 8 fp8 channels), so each wave load instruction
-//   reads 64/LPR full page rows.  fp8 takes 8-byte slices so that a wave holds four
-//   pages rather than eight: on 8 x 131072 fp8 tokens (32 pairs of 1024 pages) the
-//   16-byte form fills the GPU with exactly one generation of waves and nothing
-//   evens out their finishing times (104.9 against 98.3 us, same scores bit for bit).  Small workgroups keep the tail of the grid short when requests differ
-//   in length.  Each lane keeps 16 rows in flight; the loads are non-temporal (the keys
-//   are read once, so they should not displace what the caches hold), which measured
-//   about 20% faster than ordinary loads on this streaming pattern.  A lane keeps its channels' running sums in registers and
-//   scores a token as soon as the running sum reaches that token's bound; the
-//   tokens' bounds differ by one position, so every token shares one pass.
-//   The halving tree first pairs channels c and c + d/2, which live in different
-//   lanes of the group (DPP row shifts inside 16-lane rows), and ends inside the lane.
-//   Granularity matters more than per-wave start-up: four pages per wave measured
-//   faster than eight or sixteen streamed one after another by the same lanes, and
-//   keeping the next 8 rows in flight while 8 are added (up to 24 per lane) measured
-//   no faster than batches of 16.
+//   one workgroup = one wave per (request, KV head, run of 64/LPR pages); a group of LPR
+//   lanes owns one page, each lane a contiguous slice of every key row (16 bytes: 8 bf16
+//   or 4 f32 channels; 8 bytes: 8 fp8 channels), so each wave load instruction reads
+//   64/LPR full page rows.  fp8 takes 8-byte slices so that a wave holds four pages rather
+//   than eight: on 8 x 131072 fp8 tokens (32 pairs of 1024 pages) the 16-byte form fills
+//   the GPU with exactly one generation of waves and nothing evens out their finishing
+//   times (104.9 against 98.3 us, same scores bit for bit). (bf16 in 8-byte slices, two
+//   pages a wave, measured slower: 208 against 205 us on 64 x U[4096, 32768] tokens, 230
+//   against 180 us on a ragged batch.)  Small workgroups keep the tail of the grid short
+//   when requests differ in length.  Each lane keeps 256 bytes of rows in flight (16 rows
+//   of 16-byte slices, 32 of 8-byte: fp8 with 16 rows measured 2.8% slower); the loads are
+//   non-temporal (the keys are read once, so they should not displace what the caches
+//   hold), which measured about 20% faster than ordinary loads on this streaming pattern.
+//   A lane keeps its channels' running sums in registers and scores a token as soon as the
+//   running sum reaches that token's bound; the tokens' bounds differ by one position, so
+//   every token shares one pass. The halving tree first pairs channels c and c + d/2,
+//   which live in different lanes of the group (DPP row shifts inside 16-lane rows), and
+//   ends inside the lane. Granularity matters more than per-wave start-up: four pages per
+//   wave measured faster than eight or sixteen streamed one after another by the same
+//   lanes, and keeping the next 8 rows in flight while 8 are added (up to 24 per lane)
+//   measured no faster than batches of 16.
 #include "device.h"
 #include "internal.h"
 
@@ -116,7 +119,7 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   constexpr int PPW = kWave / LPR;   // pages per wave
   constexpr int PPB = PPW * kProxyWaves;   // pages per workgroup
   constexpr int EB = elem_bytes<KDT>();
-  constexpr int U = 16;              // positions per unrolled step
+  constexpr int U = 16 * 16 / (V * EB);   // positions per unrolled step: 256 bytes a lane
   extern __shared__ float q_lds[];   // [qo][G][D] float
 
   const int r = blockIdx.y;
