@@ -282,7 +282,7 @@ typedef struct sdv_paged_kv {
  *         p < ceil(kv_len[r] / 128) of each request are written, others untouched.
  * block_table device int32 [B][bt_stride], request-local page p -> physical page.
  * Supported: q F32 or BF16; K F32, BF16 or FP8; head_dim 64 or 128;
- * max_qo_len * G * head_dim <= 8192; B <= 65535; max_pages <= 262140.
+ * max_qo_len * G * head_dim <= 8192; B <= 65535; max_pages <= 131070.
  */
 int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                           const int32_t* kv_len, int32_t B, int32_t max_qo_len,
@@ -300,7 +300,7 @@ int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
  * scores    device float [B*max_qo_len][num_kv_heads][max_pages] (reads p < n_valid).
  * topk_idx  device int32 out [B*max_qo_len][num_kv_heads][top_k].
  * topk_cnt  device int32 out [B*max_qo_len][num_kv_heads], nullable.
- * Supported: page_size 128; 1 <= top_k <= 1024; max_pages <= 4096.
+ * Supported: page_size 128; 1 <= top_k <= 1024; max_pages <= 4096; B <= 65535.
  */
 int32_t ladder_topk_pages(const float* scores, const int32_t* qo_indptr,
                           const int32_t* kv_len, int32_t B, int32_t max_qo_len,

@@ -41,10 +41,12 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
   __shared__ ValuSmem<D> sm;
   constexpr int NE = kMaxRows * D / 256;   // accumulators per thread
   const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int r = blockIdx.z;
+  // grid x = (request, KV head), y = split, as the matrix-core kernels: no grid dimension
+  // bounds the batch size
   const int Hkv = a.num_kv_heads;
+  const int split = blockIdx.y;
+  const int h = blockIdx.x % Hkv;
+  const int r = blockIdx.x / Hkv;
   const int G = a.num_q_heads / Hkv;
   const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
                                 : static_cast<int64_t>(ds.max_sub_pages) * kSub;
@@ -219,7 +221,7 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
 template <bool SPARSE>
 static hipError_t launch_valu(const AttnArgs& a, const DenseSource& ds, const SparseSource& ss,
                               hipStream_t s) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.B);
+  dim3 grid(a.num_kv_heads * a.B, a.num_splits);
   if (a.head_dim == 128)
     hipLaunchKernelGGL((sdv_attn_valu_kernel<128, SPARSE>), grid, dim3(256), 0, s, a, ds, ss);
   else

@@ -462,9 +462,10 @@ int32_t proxy_page_scores(const void* q, int32_t q_dt, const int32_t* qo_indptr,
     return fail(SDV_ERR_SHAPE, "max_qo_len x group x head_dim exceeds 8192");
   if (max_pages < 1 || bt_stride < max_pages)
     return fail(SDV_ERR_SHAPE, "max_pages %d, bt_stride %d", max_pages, bt_stride);
-  // launch grid: y = request, z = run of four pages (each at most 65535)
-  if (B > 65535 || max_pages > 4 * 65535)
-    return fail(SDV_ERR_SHAPE, "batch %d (<= 65535) or max_pages %d (<= 262140)", B, max_pages);
+  // launch grid: y = request, z = run of pages (each at most 65535; a run holds at least
+  // two pages: four or eight but for f32 keys of head_dim 128)
+  if (B > 65535 || max_pages > 2 * 65535)
+    return fail(SDV_ERR_SHAPE, "batch %d (<= 65535) or max_pages %d (<= 131070)", B, max_pages);
   if (B > 0 && (!block_table || !scores))
     return fail(SDV_ERR_NULL_POINTER, "block_table and scores must be non-null");
   if (B == 0) return ok();
@@ -485,6 +486,7 @@ int32_t ladder_topk_pages(const float* scores, const int32_t* qo_indptr, const i
   if (top_k < 1 || top_k > 1024) return fail(SDV_ERR_SHAPE, "top_k %d outside [1, 1024]", top_k);
   if (max_pages < 1 || max_pages > 4096)
     return fail(SDV_ERR_SHAPE, "max_pages %d outside [1, 4096]", max_pages);
+  if (B > 65535) return fail(SDV_ERR_SHAPE, "batch %d (<= 65535: one launch-grid row each)", B);
   if (B > 0 && (!scores || !qo_indptr || !kv_len || !topk_idx))
     return fail(SDV_ERR_NULL_POINTER, "scores, qo_indptr, kv_len and topk_idx must be non-null");
   if (B == 0) return ok();

@@ -169,7 +169,7 @@ def test_proxy_rejections():
     assert _proxy(_kv(), max_qo=64) == L.SDV_ERR_SHAPE              # q staging too large
     assert _proxy(_kv(), scores=None) == L.SDV_ERR_NULL_POINTER
     assert _proxy(_kv(), B=65536) == L.SDV_ERR_SHAPE                # launch grid limits
-    assert _proxy(_kv(), max_pages=4 * 65535 + 1, bt_stride=4 * 65535 + 1) == L.SDV_ERR_SHAPE
+    assert _proxy(_kv(), max_pages=2 * 65535 + 1, bt_stride=2 * 65535 + 1) == L.SDV_ERR_SHAPE
     assert _proxy(_kv(), B=0) == L.SDV_OK
 
 
@@ -184,6 +184,7 @@ def test_topk_rejections():
     assert _topk(page=32) == L.SDV_ERR_GEOMETRY
     assert _topk(k=0) == L.SDV_ERR_SHAPE
     assert _topk(max_pages=5000) == L.SDV_ERR_SHAPE
+    assert _topk(B=65536) == L.SDV_ERR_SHAPE                        # launch grid limit
     assert _topk(idx=None) == L.SDV_ERR_NULL_POINTER
     assert _topk(B=0) == L.SDV_OK
 
