@@ -122,7 +122,14 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   constexpr int U = 16 * 16 / (V * EB);   // positions per unrolled step: 256 bytes a lane
   extern __shared__ float q_lds[];   // [qo][G][D] float
 
-  const int r = blockIdx.y;
+  // Request of this workgroup: y rotated by the page run z.  The hardware deals
+  // consecutive workgroups round-robin to the eight XCDs, so without the rotation every
+  // run of a request would land on the same XCDs (with four KV heads, even requests on
+  // XCDs 0-3 and odd ones on 4-7) and requests of unequal length would load the XCDs
+  // unevenly; rotated, a request's runs alternate between them (64 requests of
+  // U[4096, 32768] bf16 tokens: 207 -> 199 us; a ragged batch 180 -> 175 us; equal-length
+  // requests unchanged).
+  const int r = static_cast<int>((blockIdx.y + blockIdx.z) % static_cast<uint32_t>(B));
   const int h = blockIdx.x;
   const int Hkv = gridDim.x;
   const int row0 = qo_indptr[r];
@@ -300,9 +307,10 @@ static hipError_t launch_proxy_t(const void* q, int32_t q_dt, const int32_t* qo_
   constexpr int PPB = (kWave / (D / V)) * kProxyWaves;
   const int G = num_q_heads / kv.num_kv_heads;
   const size_t lds = static_cast<size_t>(max_qo_len) * G * D * sizeof(float);
-  // Grid x = KV head, y = request, z = run of pages: workgroups are dispatched x fastest,
-  // so the runs past a request's last page (empty, they exit at once) come at the end of
-  // the grid rather than between busy ones (≈ 1% faster on sparse_bf16).
+  // Grid x = KV head, y = request (rotated by z in the kernel), z = run of pages:
+  // workgroups are dispatched x fastest, so the runs past a request's last page (empty,
+  // they exit at once) come at the end of the grid rather than between busy ones (≈ 1%
+  // faster on 64 requests of U[4096, 32768] tokens).
   dim3 grid(kv.num_kv_heads, B, (max_pages + PPB - 1) / PPB);
   hipLaunchKernelGGL((sdv_proxy_scores_kernel<KDT, D>), grid, dim3(64 * kProxyWaves), lds, s, q, q_dt,
                      qo_indptr, kv_len, B, max_qo_len, num_q_heads, G, kv.k, kv.page_stride,
