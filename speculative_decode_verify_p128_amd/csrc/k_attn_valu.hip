@@ -41,12 +41,12 @@ __global__ void __launch_bounds__(256) sdv_attn_valu_kernel(AttnArgs a, DenseSou
   __shared__ ValuSmem<D> sm;
   constexpr int NE = kMaxRows * D / 256;   // accumulators per thread
   const int tid = threadIdx.x;
-  // grid x = (request, KV head), y = split, as the matrix-core kernels: no grid dimension
-  // bounds the batch size
+  // grid x = (request, KV head), y = split, the request rotated by the split, as in the
+  // matrix-core kernels: no grid dimension bounds the batch size
   const int Hkv = a.num_kv_heads;
   const int split = blockIdx.y;
   const int h = blockIdx.x % Hkv;
-  const int r = blockIdx.x / Hkv;
+  const int r = static_cast<int>((blockIdx.x / Hkv + split) % static_cast<uint32_t>(a.B));
   const int G = a.num_q_heads / Hkv;
   const int64_t kv_cap = SPARSE ? static_cast<int64_t>(ss.max_pages) * kPage
                                 : static_cast<int64_t>(ds.max_sub_pages) * kSub;

@@ -445,11 +445,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, OCC
 sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   __shared__ WavesLds<RT, D, KDT, MODE> sh;
   // Grid x = (request, KV head), y = split, so consecutive workgroups (dealt round-robin
-  // to the XCDs) are different (request, head) pairs of one split.
+  // to the XCDs) are different (request, head) pairs of one split; the request index is
+  // rotated by the split, so a request's splits alternate between XCDs.
   const int Hkv = a.num_kv_heads;
   const int split = blockIdx.y;
   const int h = blockIdx.x % Hkv;
-  const int r = blockIdx.x / Hkv;
+  const int r = static_cast<int>((blockIdx.x / Hkv + split) % static_cast<uint32_t>(a.B));
   const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
                                            : static_cast<int64_t>(ss.max_pages) * kPage;
   const int row0 = a.qo_indptr[r];
