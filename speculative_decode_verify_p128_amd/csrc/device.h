@@ -177,6 +177,126 @@ __device__ __forceinline__ int wave_ladder_topk(const float* srow, int n, int to
   return k_eff;
 }
 
+// ---- ladder top-k of one verify token by a bit search (wide tables, large top_k) ----
+// The same 64-bit keys, lane l holding pages l + 64 i, i < ITEMS.  Its cost does not grow
+// with top_k: the k_eff-th largest key T is found bit by bit from the top (the largest T
+// that at least k_eff keys reach), and since the page is part of the key, the keys >= T
+// are exactly the selection.
+
+template <int ITEMS>
+__device__ __forceinline__ void wave_topk_keys(const float* srow, int n, int lane,
+                                               uint64_t (&key)[ITEMS]) {
+  float sv[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) sv[i] = srow[min(lane + kWave * i, n - 1)];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = lane + kWave * i;
+    key[i] = p < n ? (static_cast<uint64_t>(ordered_key(sv[i])) << 32) |
+                         static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(p))
+                   : 0ull;
+  }
+}
+
+// T for k_eff = min(top_k, n) of n <= 4096 keys (1 when every key is selected), each
+// count a wave sum of per-lane counts (measured faster than counting each comparison's
+// lane mask in scalar registers: 15.9 against 16.5 us for 1024 pages, top-64, 128 rows);
+// the page word's high 20 bits are the same in every key (pages < 4096) and are set at
+// once.
+// Sum of v over the wave, the same in every lane: rotate-and-add inside each 16-lane row
+// (DPP row_ror), then the four row sums read into scalar registers.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  constexpr int kRowRor = 0x120;
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 1, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 2, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 4, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 8, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)) +
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+}
+
+template <int ITEMS>
+__device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&key)[ITEMS], int n, int k_eff) {
+  auto count_ge = [&](uint64_t c) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) m += key[i] >= c ? 1u : 0u;
+    return wave_sum_u32(m);
+  };
+  if (k_eff >= n) return 1ull;
+  uint64_t T = 0;
+  for (int bit = 63; bit >= 32; --bit) {
+    const uint64_t c = T | (1ull << bit);
+    if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
+  }
+  T |= 0xfffff000ull;
+  for (int bit = 11; bit >= 0; --bit) {
+    const uint64_t c = T | (1ull << bit);
+    if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
+  }
+  return T;
+}
+
+// Rank of each selected key: the keys >= T of the lanes below come first, then this
+// lane's own in item order.
+template <int ITEMS>
+__device__ __forceinline__ uint32_t wave_selection_offset(const uint64_t (&key)[ITEMS],
+                                                          uint64_t T, int lane) {
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  return incl - mine;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, kWave));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), off, kWave));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// The selection of k_eff <= 64 keys in rank order: lane k returns the rank-k key (0 from
+// lane k_eff on).  The keys are gathered through st_hi / st_lo (64 words of LDS each,
+// used by this wave alone; a wave's LDS accesses take effect in program order) and
+// sorted by a bitonic network of lane shuffles.
+template <int ITEMS>
+__device__ __forceinline__ uint64_t wave_ranked_selection(const uint64_t (&key)[ITEMS], uint64_t T,
+                                                          int lane, int k_eff, uint32_t* st_hi,
+                                                          uint32_t* st_lo) {
+  uint32_t pos = wave_selection_offset(key, T, lane);
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i)
+    if (key[i] >= T) {
+      st_hi[pos] = static_cast<uint32_t>(key[i] >> 32);
+      st_lo[pos] = static_cast<uint32_t>(key[i]);
+      ++pos;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t v = lane < k_eff ? (static_cast<uint64_t>(st_hi[lane]) << 32) | st_lo[lane] : 0ull;
+  // descending: in a block whose lane bit k is 0 the lower lane of each pair keeps the
+  // larger key
+  for (int k = 2; k <= kWave; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  return v;
+}
+
+__device__ __forceinline__ int topk_key_page(uint64_t k) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(k));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

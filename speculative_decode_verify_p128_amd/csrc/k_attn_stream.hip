@@ -393,7 +393,9 @@ hipError_t launch_attn_dense_stream(const AttnArgs& a, const DenseSource& src, h
 }
 
 hipError_t launch_attn_sparse_stream(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
-  if (src.scores) return dispatch<kSrcSparseSelect>(a, DenseSource{}, src, s);
+  if (src.scores)
+    return select_wide(src) ? dispatch<kSrcSparseSelectWide>(a, DenseSource{}, src, s)
+                            : dispatch<kSrcSparseSelect>(a, DenseSource{}, src, s);
   return dispatch<kSrcSparse>(a, DenseSource{}, src, s);
 }
 

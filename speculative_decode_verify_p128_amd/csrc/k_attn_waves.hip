@@ -548,7 +548,9 @@ hipError_t launch_attn_dense_waves(const AttnArgs& a, const DenseSource& src, hi
 }
 
 hipError_t launch_attn_sparse_waves(const AttnArgs& a, const SparseSource& src, hipStream_t s) {
-  if (src.scores) return dispatch<kSrcSparseSelect, false>(a, DenseSource{}, src, 0, s);
+  if (src.scores)
+    return select_wide(src) ? dispatch<kSrcSparseSelectWide, false>(a, DenseSource{}, src, 0, s)
+                            : dispatch<kSrcSparseSelect, false>(a, DenseSource{}, src, 0, s);
   return dispatch<kSrcSparse, false>(a, DenseSource{}, src, 0, s);
 }
 

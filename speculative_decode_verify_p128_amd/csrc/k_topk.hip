@@ -64,28 +64,7 @@ __global__ void __launch_bounds__(64) sdv_topk_kernel(
   if (topk_cnt && lane == 0) topk_cnt[row * Hkv + h] = k_eff;
 }
 
-// Sum of v over the wave, the same in every lane: rotate-and-add inside each 16-lane row
-// (DPP row_ror), then the four row sums read into scalar registers.
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  constexpr int kRowRor = 0x120;
-  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 1, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 2, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 4, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), kRowRor + 8, 0xF, 0xF, false));
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)) +
-         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)) +
-         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)) +
-         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
-}
-
 constexpr int kWideMaxK = 1024;     // selections a wave sorts (top_k <= 1024)
-
-// 64-bit shuffle (two 32-bit halves).
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
-  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, kWave));
-  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), off, kWave));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 
 // The same selection by one wave per (token row, KV head): lane l holds the keys of pages
 // l + 64 i, the bit search counts with wave sums only (no barrier), and a selection of
@@ -120,78 +99,19 @@ __global__ void __launch_bounds__(kWave) sdv_topk_bits_kernel(
   const float* srow = scores + (row * Hkv + h) * max_pages;
 
   uint64_t key[ITEMS];
-  float sv[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) sv[i] = srow[min(lane + kWave * i, n - 1)];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int p = lane + kWave * i;
-    key[i] = p < n ? (static_cast<uint64_t>(ordered_key(sv[i])) << 32) |
-                         static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(p))
-                   : 0ull;
-  }
+  wave_topk_keys(srow, n, lane, key);
   const int k_eff = top_k < n ? top_k : n;
-  auto count_ge = [&](uint64_t c) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) m += key[i] >= c ? 1u : 0u;
-    return wave_sum_u32(m);
-  };
-  // T as in the workgroup kernel: the k_eff-th largest key.
-  uint64_t T = 1;
-  if (k_eff < n) {
-    T = 0;
-    for (int bit = 63; bit >= 32; --bit) {
-      const uint64_t c = T | (1ull << bit);
-      if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
-    }
-    T |= 0xfffff000ull;
-    for (int bit = 11; bit >= 0; --bit) {
-      const uint64_t c = T | (1ull << bit);
-      if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
-    }
-  }
+  const uint64_t T = wave_kth_key(key, n, k_eff);
 
   int32_t* out = topk_idx + (row * Hkv + h) * top_k;
   if (k_eff <= kWave) {
-    // the selection, one key a lane (0 past k_eff): lane order = page order
-    uint32_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
-    uint32_t incl = mine;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += v;
-    }
-    uint32_t pos = incl - mine;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i)
-      if (key[i] >= T) sel[pos++] = key[i];
-    __syncthreads();
-    uint64_t v = lane < k_eff ? sel[lane] : 0ull;
-    // bitonic network, descending: in a block whose lane bit k is 0 the lower lane of
-    // each pair keeps the larger key
-    for (int k = 2; k <= kWave; k <<= 1)
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        const uint64_t o = shfl_xor_u64(v, j);
-        const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-        v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
-      }
+    uint32_t* st = reinterpret_cast<uint32_t*>(sel);
+    const uint64_t v = wave_ranked_selection(key, T, lane, k_eff, st, st + kWave);
     // lane k holds rank k
-    if (lane < top_k) out[lane] = lane < k_eff ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(v)) : -1;
+    if (lane < top_k) out[lane] = lane < k_eff ? topk_key_page(v) : -1;
     for (int k = kWave + lane; k < top_k; k += kWave) out[k] = -1;
   } else {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) mine += key[i] >= T ? 1u : 0u;
-    uint32_t incl = mine;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += v;
-    }
-    uint32_t pos = incl - mine;
+    uint32_t pos = wave_selection_offset(key, T, lane);
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
       if (key[i] >= T) sel[pos++] = key[i];
@@ -215,8 +135,7 @@ __global__ void __launch_bounds__(kWave) sdv_topk_bits_kernel(
         __syncthreads();
       }
     }
-    for (int k = lane; k < top_k; k += kWave)
-      out[k] = k < k_eff ? static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(sel[k])) : -1;
+    for (int k = lane; k < top_k; k += kWave) out[k] = k < k_eff ? topk_key_page(sel[k]) : -1;
   }
   if (topk_cnt && lane == 0) topk_cnt[row * Hkv + h] = k_eff;
 }

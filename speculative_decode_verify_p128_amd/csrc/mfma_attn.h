@@ -316,10 +316,15 @@ enum SourceMode : int {
   kSrcSparse = 1,   // sparse: the union of the P128 pages the tokens selected
   kSrcPaged = 2,    // dense over ordinary head-major P128 pages and a block table
   kSrcSparseSelect = 3,  // sparse, each token's pages chosen in the kernel from page scores
+  kSrcSparseSelectWide = 4,  // the same, tokens with wide tables selecting by the bit search
 };
 
+__host__ __device__ constexpr bool is_select(int mode) {
+  return mode == kSrcSparseSelect || mode == kSrcSparseSelectWide;
+}
+
 __host__ __device__ constexpr bool is_sparse(int mode) {
-  return mode == kSrcSparse || mode == kSrcSparseSelect;
+  return mode == kSrcSparse || is_select(mode);
 }
 
 // Per dense split: for kSrcView the P32 page index of each block's K sub-page (the view
@@ -349,7 +354,7 @@ struct BlockList {
                                         const DenseSource& ds, const SparseSource& ss, int r,
                                         int h, int split, int row0, int qo, int kv) {
     if constexpr (is_sparse(MODE)) {
-      const int n_union = build_union<MODE == kSrcSparseSelect>(ul, ss, r, h, a.num_kv_heads, row0, qo, kv, a.dev_err,
+      const int n_union = build_union<is_select(MODE), MODE == kSrcSparseSelectWide>(ul, ss, r, h, a.num_kv_heads, row0, qo, kv, a.dev_err,
                                       split == 0);
       const int chunk = (n_union + a.num_splits - 1) / a.num_splits;
       base = split * chunk;

@@ -25,9 +25,44 @@ struct UnionLds {
   int32_t scan[256];
 };
 
+static_assert(4 * kWave <= kMaxUnion, "the selection's staging fits the union's page arrays");
+
+// One wave selects the k_eff = min(top_k, n) <= 64 best of srow[0 .. n-1] by the bit
+// search and writes them in rank order to lout (and gout when non-null); returns k_eff.
+template <int ITEMS>
+__device__ __forceinline__ int wave_bits_select(const float* srow, int n, int top_k, int lane,
+                                                uint32_t* st_hi, uint32_t* st_lo, int32_t* lout,
+                                                int32_t* gout) {
+  uint64_t key[ITEMS];
+  wave_topk_keys(srow, n, lane, key);
+  const int k_eff = top_k < n ? top_k : n;
+  const uint64_t T = wave_kth_key(key, n, k_eff);
+  const uint64_t v = wave_ranked_selection(key, T, lane, k_eff, st_hi, st_lo);
+  if (lane < k_eff) {
+    const int page = topk_key_page(v);
+    lout[lane] = page;
+    if (gout) gout[lane] = page;
+  }
+  return k_eff;
+}
+
+// Whether a token with n valid pages selects by the bit search (WIDE kernels only): its
+// cost does not grow with top_k, while the repeated maximum costs about top_k x (items +
+// 8) dependent instructions; with top_k <= 64 the mark is passed from 11 key slots a lane
+// (over 640 pages) on.  Measured on 8 requests of 131072 fp8 tokens (1024 pages), top-64:
+// the fused selection and attention 85.6 -> 68.2 us at 16 splits.
+__host__ __device__ constexpr bool select_by_bits(int n, int top_k) {
+  return n > 4 * kWave && top_k <= kWave && top_k * ((n + kWave - 1) / kWave + 8) > 1200;
+}
+
+// Launches whose tables can hold such a token take the kernel variant that carries the
+// bit search (the others keep the smaller code of the repeated maximum alone).
+inline bool select_wide(const SparseSource& ss) { return select_by_bits(ss.max_pages, ss.top_k); }
+
 // The ladder top-k of every verify token of (r, h) from ss.scores, one wave per token,
 // into u.sel (and ss.topk_out / ss.cnt_out when non-null and write_out): the same
 // selection as the top-k kernel.  All 256 threads call; ends with a barrier.
+template <bool WIDE>
 __device__ inline void select_topk(UnionLds& u, const SparseSource& ss, int h, int Hkv, int row0,
                                    int qo, int kv, bool write_out) {
   static_assert(kFusedTopkMaxPages == 16 * kWave, "item counts below");
@@ -48,7 +83,13 @@ __device__ inline void select_topk(UnionLds& u, const SparseSource& ss, int h, i
     // register slots per lane sized to this token's pages (each round rescans them)
     const int items = (n + kWave - 1) / kWave;
     int k_eff;
-    if (items <= 1) k_eff = wave_ladder_topk<1>(srow, n, ss.top_k, lane, emit);
+    if (WIDE && select_by_bits(n, ss.top_k)) {
+      // the keys are gathered through the union's page arrays, filled only after the
+      // selection
+      uint32_t* st_hi = reinterpret_cast<uint32_t*>(u.upage) + wave * kWave;
+      uint32_t* st_lo = reinterpret_cast<uint32_t*>(u.uphys) + wave * kWave;
+      k_eff = wave_bits_select<16>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
+    } else if (items <= 1) k_eff = wave_ladder_topk<1>(srow, n, ss.top_k, lane, emit);
     else if (items <= 2) k_eff = wave_ladder_topk<2>(srow, n, ss.top_k, lane, emit);
     else if (items <= 4) k_eff = wave_ladder_topk<4>(srow, n, ss.top_k, lane, emit);
     else if (items <= 8) k_eff = wave_ladder_topk<8>(srow, n, ss.top_k, lane, emit);
@@ -65,14 +106,14 @@ __device__ inline void select_topk(UnionLds& u, const SparseSource& ss, int h, i
 // All 256 threads must call.  Returns the number of distinct selected pages; flags
 // (and ignores) indices at or beyond a token's valid-page count.  The pages come from
 // ss.topk_idx, or (SELECT) from the in-kernel selection of ss.scores, written out to
-// ss.topk_out / ss.cnt_out when write_out.
-template <bool SELECT>
+// ss.topk_out / ss.cnt_out when write_out (WIDE: by the bit search where it pays).
+template <bool SELECT, bool WIDE = false>
 __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, int h, int Hkv,
                                   int row0, int qo, int kv, int32_t* dev_err,
                                   bool write_out = false) {
   const int tid = threadIdx.x;
   const int words = (ss.max_pages + 31) / 32;
-  if constexpr (SELECT) select_topk(u, ss, h, Hkv, row0, qo, kv, write_out);
+  if constexpr (SELECT) select_topk<WIDE>(u, ss, h, Hkv, row0, qo, kv, write_out);
   auto selected = [&](int t, int k) {
     if constexpr (SELECT) return u.sel[t * ss.top_k + k];
     else return ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];

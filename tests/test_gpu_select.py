@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import speculative_decode_verify_p128_amd as sdv
 import workloads as W
 
@@ -27,6 +28,11 @@ D64 = W.SPARSE_BF16.scaled(name="d64", batch=3, kv=("uniform", 130, 1000), kv_ca
 # selection over the largest page count the in-kernel top-k takes (1024 pages)
 WIDE = W.LONG_FP8.scaled(name="wide_1024_pages", batch=2, kv=("list", (131072, 70001)),
                          kv_capacity=131072, top_k=16, num_q_heads=8, num_kv_heads=1)
+# top-64 over up to 1024 pages: tokens with 11 or more key slots a lane (over 640 valid
+# pages) select by the bit search inside the attention kernel, the 547-page request by
+# the repeated maximum
+WIDE_K64 = W.LONG_FP8.scaled(name="wide_top64", batch=3, kv=("list", (131072, 100001, 70001)),
+                             kv_capacity=131072, top_k=64, num_q_heads=8, num_kv_heads=1)
 CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64]
 
 
@@ -97,6 +103,53 @@ def test_select_widest_table():
     ok, worst = tol_ok(out_numpy(out[:n]), ref["out"], "bf16")
     assert int(err.item()) == 0
     assert ok, worst
+
+
+@pytest.mark.parametrize("splits", [1, 16])
+def test_select_bit_search_top64(splits):
+    c = W.make_sparse_case(WIDE_K64)
+    run = SparseRun(c)
+    scores = run.scores()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, idx, cnt = _select(run, scores, splits, dev_err=err)
+    idx2, _ = run.topk(scores)
+    out2 = run.attend(idx2, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = sparse_oracle(c)
+    n = run.n
+    assert np.array_equal(idx[:n].cpu().numpy(), ref["topk"][:n].astype(np.int32))
+    assert np.array_equal(cnt[:n].cpu().numpy(), ref["count"][:n].astype(np.int32))
+    ok, worst = tol_ok(out_numpy(out[:n]), ref["out"], "bf16")
+    assert int(err.item()) == 0
+    assert ok, worst
+    assert torch.equal(out[:n], out2[:n]), "fused and two-launch outputs differ"
+
+
+def test_select_bit_search_ties_and_signed_zeros():
+    # six score values (with -0 and +0) over 1024 pages: the k-th largest key sits inside
+    # long runs of equal scores, which the page word must order
+    c = W.make_sparse_case(WIDE_K64)
+    run = SparseRun(c)
+    w = WIDE_K64
+    rng = np.random.default_rng(11)
+    vals = np.array([-2.0, -0.0, 0.0, 0.25, 1.0, 3.0], dtype=np.float32)
+    s_np = vals[rng.integers(0, len(vals), size=(w.batch * w.max_qo(), w.num_kv_heads,
+                                                   w.max_pages()))]
+    scores = torch.from_numpy(s_np).to(DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, idx, cnt = _select(run, scores, 4, dev_err=err)
+    idx2, _ = run.topk(scores)
+    out2 = run.attend(idx2, num_splits=4)
+    torch.cuda.synchronize()
+    got, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    ind = c.qo_indptr.numpy()
+    for r in range(w.batch):
+        a, b = ind[r], ind[r + 1]
+        e, ec = oracle.ladder_topk_request(s_np[a:b], int(c.lengths.kv[r]), w.top_k)
+        assert np.array_equal(got[a:b], e.astype(np.int32)), f"request {r}"
+        assert np.array_equal(gcnt[a:b], ec.astype(np.int32)), f"request {r}"
+    assert int(err.item()) == 0
+    assert torch.equal(out[:run.n], out2[:run.n]), "fused and two-launch outputs differ"
 
 
 def test_select_over_1024_pages_selects_in_its_own_launch():
