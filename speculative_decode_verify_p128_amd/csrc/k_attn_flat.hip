@@ -168,19 +168,22 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
   int c_next = 0;                       // first block of the next piece
   int h_c = 0, row0_c = 0, slot_c = 0, qo_c = 1;
   bool row_live = false;
-  int t_row = 0, g_row = 0, bound_row = 0, first_bound = 0, all_tokens = 0;
+  int t_row = 0, bound_row = 0, first_bound = 0, all_tokens = 0;
   bf16x8 qb[STEPS];
   f32x4 o[NTW];
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Normalise the finished piece and write its partial and log-sum-exp (a row with no
-  // live position leaves its partial unwritten and lse = -inf, which the combine skips).
-  auto finalize = [&]() {
-    float l = l_run + __shfl_xor(l_run, 16, kWave);
+  // Normalise a finished piece and write its partial and log-sum-exp (a row with no live
+  // position leaves its partial unwritten and lse = -inf, which the combine skips).  Every
+  // lane calls: the row sum is reduced across the lane groups first.
+  auto store_partial = [&](const f32x4 (&od)[NTW], float m, float lsum, int slot, int row0,
+                           int h, int qo) {
+    float l = lsum + __shfl_xor(lsum, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
-    if (row_live) {
-      const int64_t unit = (static_cast<int64_t>(slot_c) * rows_cap + row0_c + t_row) * a.num_q_heads +
-                           h_c * G + g_row;
+    if (row < qo * G) {
+      const int t = row / G;
+      const int64_t unit = (static_cast<int64_t>(slot) * rows_cap + row0 + t) * a.num_q_heads +
+                           h * G + (row - t * G);
       if (l > 0.f) {
         const float inv = a.v_scale / l;
         float* dst = a.part_o + unit * D;
@@ -190,15 +193,43 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
           if constexpr (NTW % 4 == 0) {
 #pragma unroll
             for (int n = 0; n < NTW; n += 4)
-              *reinterpret_cast<float4*>(d0 + n) =
-                  make_float4(o[n][e] * inv, o[n + 1][e] * inv, o[n + 2][e] * inv, o[n + 3][e] * inv);
+              *reinterpret_cast<float4*>(d0 + n) = make_float4(od[n][e] * inv, od[n + 1][e] * inv,
+                                                               od[n + 2][e] * inv, od[n + 3][e] * inv);
           } else {
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) d0[n] = o[n][e] * inv;
+            for (int n = 0; n < NTW; ++n) d0[n] = od[n][e] * inv;
           }
         }
       }
-      if (cp == 0 && q == 0) a.part_lse[unit] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+      if (cp == 0 && q == 0) a.part_lse[unit] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  };
+
+  // Finished pieces whose partials wait in registers until the ring has drained.  A store
+  // issued while block copies are in flight shares their counter: the waits for the next
+  // blocks, which count only copies, would also wait for the store and leave the ring
+  // with one block in flight for about two blocks.  Up to two pieces wait this way; a
+  // range with more stores the later ones at once.
+  struct Done {
+    f32x4 o[NTW];
+    float m, l;
+    int slot, row0, h, qo;
+  };
+  Done d0, d1;
+  int ndone = 0;
+  auto finish_piece = [&]() {
+    if (ndone == 0) {
+#pragma unroll
+      for (int n = 0; n < NTW; ++n) d0.o[n] = o[n];
+      d0.m = m_run; d0.l = l_run; d0.slot = slot_c; d0.row0 = row0_c; d0.h = h_c; d0.qo = qo_c;
+      ndone = 1;
+    } else if (ndone == 1) {
+#pragma unroll
+      for (int n = 0; n < NTW; ++n) d1.o[n] = o[n];
+      d1.m = m_run; d1.l = l_run; d1.slot = slot_c; d1.row0 = row0_c; d1.h = h_c; d1.qo = qo_c;
+      ndone = 2;
+    } else {
+      store_partial(o, m_run, l_run, slot_c, row0_c, h_c, qo_c);
     }
   };
 
@@ -211,7 +242,6 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
     const int nrows = qo_c * G;
     row_live = row < nrows;
     t_row = row_live ? row / G : 0;
-    g_row = row_live ? row - t_row * G : 0;
     bound_row = row_live ? kv - qo_c + t_row + 1 : 0;
     first_bound = kv - qo_c + 1;
     all_tokens = qo_c >= 32 ? ~0 : (1 << qo_c) - 1;
@@ -242,7 +272,7 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
     wait_blocks<Gm::LPT, kStages - 2>(min(nblk - 1 - j, kStages - 2));
     ring_barrier();
     if (j == c_next) {
-      if (kc >= 0) finalize();
+      if (kc >= 0) finish_piece();
       ++kc;
       begin_piece(kc, u);
       c_next = __builtin_amdgcn_readfirstlane(sh.piece[kc + 1].start);
@@ -330,9 +360,12 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
     });
   }
 
-  // The last piece goes out through the ring, idle now, as whole coalesced rows.
+  // The waiting pieces go out from registers; the last piece through the ring, idle now,
+  // as whole coalesced rows.
   wait_vmcnt<0>();
   __syncthreads();
+  if (ndone >= 1) store_partial(d0.o, d0.m, d0.l, d0.slot, d0.row0, d0.h, d0.qo);
+  if (ndone >= 2) store_partial(d1.o, d1.m, d1.l, d1.slot, d1.row0, d1.h, d1.qo);
   constexpr int OPAD = D + 4;
   static_assert(LdsT::ROWS * OPAD * 4 <= kStages * Gm::BLOCK + kStages * LdsT::QBYTES,
                 "output rows fit the ring and query buffers");
@@ -451,7 +484,9 @@ sdv_attn_flat_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
       sh.x[b] = xb;
     }
     __syncthreads();
-    // pieces that end their pair: the pair's later split slots hold no keys
+    flat_attend<RT, D, KDT, MODE>(sh, a, ds, ss, nblk);
+    // pieces that end their pair: the pair's later split slots hold no keys (written after
+    // the ring, so that no store is queued ahead of the first block copies)
     for (int k = 0; k < npieces; ++k) {
       const int rr = __builtin_amdgcn_readfirstlane(sh.piece[k].r);
       const int nb = __builtin_amdgcn_readfirstlane(sh.pl.cum[rr + 1]) -
@@ -470,7 +505,6 @@ sdv_attn_flat_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
         a.part_lse[(kk * rows_cap + row0 + t) * a.num_q_heads + h * G + (row - t * G)] = -INFINITY;
       }
     }
-    flat_attend<RT, D, KDT, MODE>(sh, a, ds, ss, nblk);
     __syncthreads();   // LDS is planned again for the rest of the range
   }
 }
