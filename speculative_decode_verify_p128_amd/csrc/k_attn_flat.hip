@@ -208,26 +208,29 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
   // Finished pieces whose partials wait in registers until the ring has drained.  A store
   // issued while block copies are in flight shares their counter: the waits for the next
   // blocks, which count only copies, would also wait for the store and leave the ring
-  // with one block in flight for about two blocks.  Up to two pieces wait this way; a
-  // range with more stores the later ones at once.
+  // with one block in flight for about two blocks.  Up to ND pieces wait this way (as
+  // many as the registers allow at one workgroup per CU); a range with more stores the
+  // later ones at once.  Pieces finish in order, so waiting piece k is piece k of the
+  // plan, whose metadata stays in LDS.
+  constexpr int ND = RT >= 4 ? 2 : 4;
   struct Done {
     f32x4 o[NTW];
     float m, l;
-    int slot, row0, h, qo;
   };
-  Done d0, d1;
+  Done done[ND];
   int ndone = 0;
   auto finish_piece = [&]() {
-    if (ndone == 0) {
+    if (ndone < ND) {
 #pragma unroll
-      for (int n = 0; n < NTW; ++n) d0.o[n] = o[n];
-      d0.m = m_run; d0.l = l_run; d0.slot = slot_c; d0.row0 = row0_c; d0.h = h_c; d0.qo = qo_c;
-      ndone = 1;
-    } else if (ndone == 1) {
+      for (int k = 0; k < ND; ++k) {
+        if (k == ndone) {
 #pragma unroll
-      for (int n = 0; n < NTW; ++n) d1.o[n] = o[n];
-      d1.m = m_run; d1.l = l_run; d1.slot = slot_c; d1.row0 = row0_c; d1.h = h_c; d1.qo = qo_c;
-      ndone = 2;
+          for (int n = 0; n < NTW; ++n) done[k].o[n] = o[n];
+          done[k].m = m_run;
+          done[k].l = l_run;
+        }
+      }
+      ++ndone;
     } else {
       store_partial(o, m_run, l_run, slot_c, row0_c, h_c, qo_c);
     }
@@ -364,8 +367,14 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
   // as whole coalesced rows.
   wait_vmcnt<0>();
   __syncthreads();
-  if (ndone >= 1) store_partial(d0.o, d0.m, d0.l, d0.slot, d0.row0, d0.h, d0.qo);
-  if (ndone >= 2) store_partial(d1.o, d1.m, d1.l, d1.slot, d1.row0, d1.h, d1.qo);
+#pragma unroll
+  for (int k = 0; k < ND; ++k)
+    if (k < ndone)
+      store_partial(done[k].o, done[k].m, done[k].l,
+                    __builtin_amdgcn_readfirstlane(sh.piece[k].slot),
+                    __builtin_amdgcn_readfirstlane(sh.piece[k].row0),
+                    __builtin_amdgcn_readfirstlane(sh.piece[k].h),
+                    __builtin_amdgcn_readfirstlane(sh.piece[k].qo));
   constexpr int OPAD = D + 4;
   static_assert(LdsT::ROWS * OPAD * 4 <= kStages * Gm::BLOCK + kStages * LdsT::QBYTES,
                 "output rows fit the ring and query buffers");
