@@ -23,6 +23,12 @@ FAMILIES = [5, 6]   # the per-wave and the LDS-ring kernels under the persistent
 
 MANY_SHORT_VIEW = W.DENSE_BF16.scaled(name="many_short_view", batch=600, kv=("uniform", 4, 100),
                                       kv_capacity=128, num_q_heads=16)
+# 64 and 32 query rows per pair: the row tiles whose ranges hold fewer finished pieces in
+# registers than these ranges have pieces, so later pieces are written at once
+MANY_SHORT_VIEW64 = W.DENSE_BF16.scaled(name="many_short_view64", batch=600, kv=("uniform", 4, 100),
+                                        kv_capacity=128)
+MANY_SHORT_VIEW32 = W.DENSE_BF16.scaled(name="many_short_view32", batch=600, kv=("uniform", 4, 100),
+                                        kv_capacity=128, num_q_heads=32)
 FEW_LONG_VIEW = W.DENSE_BF16.scaled(name="few_long_view", batch=2, kv=("uniform", 3000, 6000),
                                     kv_capacity=6144)
 MANY_SHORT_PAGED = W.PAGED_BF16.scaled(name="many_short_paged", batch=600, kv=("uniform", 4, 100),
@@ -54,7 +60,8 @@ def _announce(request):
 
 @pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("splits", [2, 3, 16])
-@pytest.mark.parametrize("w", [MANY_SHORT_VIEW, FEW_LONG_VIEW], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [MANY_SHORT_VIEW, MANY_SHORT_VIEW64, MANY_SHORT_VIEW32, FEW_LONG_VIEW],
+                         ids=lambda w: w.name)
 def test_persist_view_parity(w, splits, family):
     c, ref = _dense(w)
     run = DenseRun(c)
