@@ -146,7 +146,8 @@ __device__ __forceinline__ void ring_attend(RingLds<RT, D, KDT, MODE, ST>& sh, c
                       q * (D / 4)) * 2;
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-      const uint4 w = row_live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      const uint4 w = row_live ? *reinterpret_cast<const uint4*>(qp + Gm::step_unit(q, s) * 16)
+                               : make_uint4(0, 0, 0, 0);
       qb[s] = __builtin_bit_cast(bf16x8, w);
     }
   }

@@ -37,8 +37,8 @@ constexpr int kWaveSlots = 2;   // ring slots per wave
 
 // One wave's copy of a whole 32-token block (K then V) into a ring slot: 32 / RPI
 // asynchronous 16-byte-per-lane loads per half.  Lane l of instruction n lands at
-// half + (n * 64 + l) * 16, which is row n * RPI + l / CPR, chunk l % CPR of the
-// swizzled block; the lane reads the global chunk that belongs there.
+// half + (n * 64 + l) * 16, which is LDS row n * RPI + l / CPR, chunk l % CPR of the
+// swizzled block; the lane reads the global chunk that belongs there (Geo::src).
 template <int D, int KDT>
 struct WaveCopier {
   using Gm = Geo<D, KDT>;
@@ -49,9 +49,7 @@ struct WaveCopier {
   __device__ __forceinline__ void init(int lane) {
 #pragma unroll
     for (int n = 0; n < PER_HALF; ++n) {
-      const int row = n * Gm::RPI + lane / Gm::CPR;
-      const int gchunk = ((lane % Gm::CPR) ^ Gm::swz(row)) & (Gm::CPR - 1);
-      off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
+      off[n] = static_cast<uint32_t>(Gm::src(n * Gm::RPI + lane / Gm::CPR, lane % Gm::CPR));
     }
   }
 
@@ -195,7 +193,8 @@ __device__ __forceinline__ void waves_attend(WavesLds<RT, D, KDT, MODE>& sh, con
                       q * (D / 4)) * 2;
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-      const uint4 w = live ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      const uint4 w = live ? *reinterpret_cast<const uint4*>(qp + Gm::step_unit(q, s) * 16)
+                           : make_uint4(0, 0, 0, 0);
       qb[rt][s] = __builtin_bit_cast(bf16x8, w);
     }
   }

@@ -81,6 +81,17 @@ __device__ __forceinline__ constexpr int row_key16(int row) {
 }
 
 // Geometry of one 32-token block of one head in LDS.
+//
+// fp8 rows of 128 channels (128 bytes, eight 16-byte chunks) are read 8 bytes a lane
+// (ds_read_b64), which gfx950 serves in two passes, lanes 0-31 and 32-63 (measured with
+// lane-pair probes under SQ_LDS_BANK_CONFLICT); a pass is conflict-free when its 32 lanes
+// hit 32 different 8-byte bank pairs.  With the 16-byte layout's row-only XOR, the K
+// operand reads (rows i = 0..15 of lane groups q, one 8-byte half of a chunk) met 4-way
+// conflicts and the value reads (four token rows, one per lane group) 2-way.  For this
+// shape the layout also swaps rows 4-7 of every eight in pairs (prow), XORs chunks with
+// row / 2, and the lane groups take their four 8-channel units of a step in the order
+// s ^ (q & 1) (step_unit), so that the two lane groups of a pass read opposite halves of
+// their chunks: both read patterns measured conflict-free.
 template <int D, int KDT>
 struct Geo {
   static constexpr int EB = elem_bytes<KDT>();
@@ -92,16 +103,32 @@ struct Geo {
   static constexpr int LPT = (2 * 32 / RPI) / 4;    // load instructions per wave per block
   static constexpr int STEPS = D / 32;              // 32-channel MFMA steps
   static constexpr int NT = D / 16;                 // 16-channel output tiles
+  static constexpr bool B64_ROWS = KDT == SDV_FP8_E4M3 && D == 128;   // the 8-byte-read layout
   static_assert(LPT >= 1, "block too small for four waves");
+  // LDS row of token row `row` inside its group of eight (an involution)
+  __device__ static __forceinline__ constexpr int prow(int row) {
+    return B64_ROWS ? row ^ ((row >> 2) & 1) : row;
+  }
   // XOR key of a row's 16-byte chunks (rows of 16 chunks: row_key16; rows of 8 chunks
   // start every other row in the other half of the bank groups by themselves)
   __device__ static __forceinline__ constexpr int swz(int row) {
-    return CPR == 16 ? row_key16(row) : row & (CPR - 1);
+    return B64_ROWS ? (row >> 1) & 7 : (CPR == 16 ? row_key16(row) : row & (CPR - 1));
   }
   // byte offset in a block's K or V half of (row, byte-in-row)
   __device__ static __forceinline__ int at(int row, int byte) {
     const int chunk = byte >> 4;
-    return row * ROWB + (((chunk ^ swz(row)) & (CPR - 1)) << 4) + (byte & 15);
+    return prow(row) * ROWB + (((chunk ^ swz(row)) & (CPR - 1)) << 4) + (byte & 15);
+  }
+  // byte offset in the global K or V run of the chunk that lands at LDS position
+  // (lds_row, lds_chunk): the inverse of at()
+  __device__ static __forceinline__ int src(int lds_row, int lds_chunk) {
+    const int row = prow(lds_row);
+    return row * ROWB + (((lds_chunk ^ swz(row)) & (CPR - 1)) << 4);
+  }
+  // 8-channel unit of its quarter row that lane group q feeds the matrix core at step s
+  // (the same for K and for Q, so the dot products are unchanged)
+  __device__ static __forceinline__ constexpr int step_unit(int q, int s) {
+    return B64_ROWS ? s ^ (q & 1) : s;
   }
 };
 
@@ -135,7 +162,7 @@ template <int D, int KDT>
 __device__ __forceinline__ bf16x8 k_operand(const char* kb, int tt, int s, int i, int q) {
   using Gm = Geo<D, KDT>;
   const int row = tt * 16 + i;
-  const int byte = (q * (D / 4) + s * 8) * Gm::EB;
+  const int byte = (q * (D / 4) + Gm::step_unit(q, s) * 8) * Gm::EB;
   uint32_t w[4];
   if constexpr (KDT == SDV_BF16) {
     lds_read<16>(kb + Gm::at(row, byte), w);
@@ -215,8 +242,7 @@ struct BlockCopier {
       const int ins = wave * Gm::LPT + n;               // 0 .. 2 * 32 / RPI - 1
       const int half = ins / (32 / Gm::RPI);            // 0 = K, 1 = V
       const int row = (ins % (32 / Gm::RPI)) * Gm::RPI + lane / Gm::CPR;
-      const int gchunk = ((lane % Gm::CPR) ^ Gm::swz(row)) & (Gm::CPR - 1);
-      off[n] = static_cast<uint32_t>(row * Gm::ROWB + gchunk * 16);
+      off[n] = static_cast<uint32_t>(Gm::src(row, lane % Gm::CPR));
       lds[n] = static_cast<uint32_t>(half * Gm::HALF + (ins % (32 / Gm::RPI)) * 64 * 16);
       is_v[n] = half != 0;
     }
