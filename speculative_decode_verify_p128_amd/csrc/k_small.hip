@@ -45,8 +45,9 @@ hipError_t launch_subpage_offsets(const int32_t* block_table, int32_t B, int32_t
 // Split-KV combine: LPU = head_dim / 8 lanes per (query row, query head), each lane
 // eight channels.  LSE = log sum_s exp(lse_s), out = sum_s exp(lse_s - LSE) * O_s, in
 // ascending s; partials with lse = -inf (no keys) are skipped and never read.  A lane
-// loads every split's lse at once and then every split's partial, so the call costs two
-// memory round trips, not two per split (up to kCombineUnroll splits; more loop).
+// loads every split's lse at once (with the batch's row range) and then every split's
+// partial, so the call costs two memory round trips, not two per split (up to
+// kCombineUnroll splits; more loop).
 constexpr int kCombineUnroll = 8;
 
 template <int D>
@@ -61,19 +62,25 @@ __global__ void __launch_bounds__(256) sdv_combine_kernel(
   const int64_t units = static_cast<int64_t>(rows_cap) * num_heads;
   if (unit >= units) return;
   const int64_t row = unit / num_heads;
-  if (row_begin_dev && (row < *row_begin_dev || row >= *row_end_dev)) return;
   const int64_t plane = units;   // rows_cap * num_heads
   const int S = num_splits;
+  // The first chunk's log-sum-exps load together with the batch's row range (they lie
+  // inside the workspace whatever the row), so the range check adds no round trip.
+  float l[kCombineUnroll];
+#pragma unroll
+  for (int k = 0; k < kCombineUnroll; ++k) l[k] = k < S ? part_lse[k * plane + unit] : -INFINITY;
+  if (row_begin_dev && (row < *row_begin_dev || row >= *row_end_dev)) return;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float m = -INFINITY, tot = 0.f;
   for (int s0 = 0; s0 < S; s0 += kCombineUnroll) {
     const int n = min(kCombineUnroll, S - s0);
-    float l[kCombineUnroll];
+    if (s0 > 0) {
 #pragma unroll
-    for (int k = 0; k < kCombineUnroll; ++k)
-      l[k] = k < n ? part_lse[(s0 + k) * plane + unit] : -INFINITY;
+      for (int k = 0; k < kCombineUnroll; ++k)
+        l[k] = k < n ? part_lse[(s0 + k) * plane + unit] : -INFINITY;
+    }
     float mc = m;
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) mc = fmaxf(mc, l[k]);
