@@ -156,18 +156,22 @@ __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, in
     int idx = u.word_prefix[w];
     while (bits) {
       const int b = __ffs(bits) - 1;
-      const int p = w * 32 + b;
-      int phys = ss.block_table[static_cast<int64_t>(r) * ss.bt_stride + p];
-      if (phys < 0 || phys >= ss.num_pages) {
-        set_err(dev_err, SDV_DEVERR_PAGE_RANGE);
-        phys = -1;
-      }
-      u.upage[idx] = p;
-      u.uphys[idx] = phys;
+      u.upage[idx] = w * 32 + b;
       u.umask[idx] = 0;
       ++idx;
       bits &= bits - 1;
     }
+  }
+  __syncthreads();
+  // every union entry's block-table entry at once (one memory round trip, not one per
+  // page a thread's words hold)
+  for (int e = tid; e < total; e += 256) {
+    int phys = ss.block_table[static_cast<int64_t>(r) * ss.bt_stride + u.upage[e]];
+    if (phys < 0 || phys >= ss.num_pages) {
+      set_err(dev_err, SDV_DEVERR_PAGE_RANGE);
+      phys = -1;
+    }
+    u.uphys[e] = phys;
   }
   __syncthreads();
   for (int e = tid; e < n_el; e += 256) {
