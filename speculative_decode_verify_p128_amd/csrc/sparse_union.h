@@ -119,37 +119,55 @@ __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, in
     else return ss.topk_idx[(static_cast<int64_t>(row0 + t) * Hkv + h) * ss.top_k + k];
   };
   for (int w = tid; w < words; w += 256) u.bitmap[w] = 0u;
-  __syncthreads();
+  // This thread's (token, rank) elements, e = tid and tid + 256 (qo * top_k <= 512): the
+  // page of each, or -1 when it selects none or is out of the token's range (flagged).
+  static_assert(kMaxUnion <= 2 * 256, "two selection elements a thread");
   const int n_el = qo * ss.top_k;
-  for (int e = tid; e < n_el; e += 256) {
-    const int t = e / ss.top_k;
-    const int k = e - t * ss.top_k;
-    const int p = selected(t, k);
-    if (p < 0) continue;
-    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
-    if (p >= nvalid) {
-      set_err(dev_err, SDV_DEVERR_TOPK_INDEX);
-      continue;
+  int el_page[2], el_tok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i;
+    el_page[i] = -1;
+    el_tok[i] = 0;
+    if (e < n_el) {
+      const int t = e / ss.top_k;
+      const int p = selected(t, e - t * ss.top_k);
+      const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
+      if (p >= nvalid) set_err(dev_err, SDV_DEVERR_TOPK_INDEX);
+      el_page[i] = p >= 0 && p < nvalid ? p : -1;
+      el_tok[i] = t;
     }
-    atomicOr(&u.bitmap[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
-  // exclusive prefix of per-word popcounts; each thread owns two consecutive words
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (el_page[i] >= 0) atomicOr(&u.bitmap[el_page[i] >> 5], 1u << (el_page[i] & 31));
+  __syncthreads();
+  // exclusive prefix of per-word popcounts; each thread owns two consecutive words: a
+  // prefix inside each wave by lane shuffles, then the waves' totals
   const int w0 = 2 * tid;
   const int c0 = (w0 < words) ? __popc(u.bitmap[w0]) : 0;
   const int c1 = (w0 + 1 < words) ? __popc(u.bitmap[w0 + 1]) : 0;
-  u.scan[tid] = c0 + c1;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = tid >= off ? u.scan[tid - off] : 0;
-    __syncthreads();
-    u.scan[tid] += v;
-    __syncthreads();
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  int inc = c0 + c1;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += v;
   }
-  const int excl = u.scan[tid] - (c0 + c1);
+  if (lane == kWave - 1) u.scan[wv] = inc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < 256 / kWave; ++k) {
+    const int tw = u.scan[k];
+    base += k < wv ? tw : 0;
+    total += tw;
+  }
+  const int excl = base + inc - (c0 + c1);
   if (w0 < words) u.word_prefix[w0] = excl;
   if (w0 + 1 < words) u.word_prefix[w0 + 1] = excl + c0;
-  const int total = u.scan[255];
   __syncthreads();
   for (int w = tid; w < words; w += 256) {
     uint32_t bits = u.bitmap[w];
@@ -174,15 +192,13 @@ __device__ inline int build_union(UnionLds& u, const SparseSource& ss, int r, in
     u.uphys[e] = phys;
   }
   __syncthreads();
-  for (int e = tid; e < n_el; e += 256) {
-    const int t = e / ss.top_k;
-    const int k = e - t * ss.top_k;
-    const int p = selected(t, k);
-    const int nvalid = (kv - qo + t + 1 + kPage - 1) / kPage;
-    if (p < 0 || p >= nvalid) continue;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = el_page[i];
+    if (p < 0) continue;
     const int w = p >> 5;
     const int idx = u.word_prefix[w] + __popc(u.bitmap[w] & ((1u << (p & 31)) - 1u));
-    if (u.uphys[idx] >= 0) atomicOr(&u.umask[idx], 1 << t);
+    if (u.uphys[idx] >= 0) atomicOr(&u.umask[idx], 1 << el_tok[i]);
   }
   __syncthreads();
   // Pages outside the pool keep an empty token mask and read page 0 (in bounds); the
