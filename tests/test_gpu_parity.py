@@ -32,11 +32,16 @@ LONG_S = W.LONG_FP8.scaled(name="long_small", batch=2, kv=("fixed", 5000), kv_ca
 D64 = W.SPARSE_BF16.scaled(name="d64", batch=3, kv=("uniform", 130, 1000), kv_capacity=1024,
                            head_dim=64, num_q_heads=8, num_kv_heads=2, top_k=3)
 
+# eight verify tokens selecting 64 pages each: 512 (token, rank) entries per (request, KV
+# head), the most a union takes (two per thread of the workgroup)
+WIDE_UNION = W.SPARSE_BF16.scaled(name="wide_union", batch=3, qo=8,
+                                  kv=("list", (9000, 12000, 16000)), kv_capacity=16384, top_k=64)
+
 D64_FP8 = W.LONG_FP8.scaled(name="d64_fp8", batch=3, kv=("uniform", 130, 1500), kv_capacity=1536,
                             head_dim=64, num_q_heads=8, num_kv_heads=2, top_k=3)
 
 DENSE_CASES = [TINY, DENSE_S, DENSE_S_FP8, RAGGED_S]
-SPARSE_CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64]
+SPARSE_CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64, WIDE_UNION]
 
 
 @pytest.fixture(autouse=True)

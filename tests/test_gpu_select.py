@@ -33,7 +33,10 @@ WIDE = W.LONG_FP8.scaled(name="wide_1024_pages", batch=2, kv=("list", (131072, 7
 # the repeated maximum
 WIDE_K64 = W.LONG_FP8.scaled(name="wide_top64", batch=3, kv=("list", (131072, 100001, 70001)),
                              kv_capacity=131072, top_k=64, num_q_heads=8, num_kv_heads=1)
-CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64]
+# eight tokens selecting 64 pages each: the union's 512-entry limit
+WIDE_UNION = W.SPARSE_BF16.scaled(name="wide_union", batch=3, qo=8,
+                                  kv=("list", (9000, 12000, 16000)), kv_capacity=16384, top_k=64)
+CASES = [TINY, SPARSE_S, LONG_S, RAGGED_S, D64, WIDE_UNION]
 
 
 @pytest.fixture(autouse=True)
