@@ -857,11 +857,12 @@ def main():
             "workload": "ragged_mixed: batch 256, qo_len 1..8, kv_len log-normal (median 2048, "
                         "clipped [64, 65536]) with page-crossing rows, 16 q / 4 kv heads, "
                         "head_dim 128, bf16, top-k 16 clamped",
-            # split counts: the fastest measured for each path (sparse 1-4, dense 2-16)
+            # split counts: the fastest measured for each path (sparse 1-4, dense 2-16: 6 and 8
+            # within 1 us, 4 about 8 us slower)
             "sparse": sparse_config_line(torch, sdv, W, wr, dev, args, flush, fam,
                                          args.ragged_splits or 1),
             "dense": dense_config_line(torch, sdv, W, wr, dev, args, flush, fam,
-                                       args.ragged_dense_splits or 4)}
+                                       args.ragged_dense_splits or 6)}
 
     # ---- target dense layers: ladder attention over ordinary head-major P128 pages ----
     if want("paged", args.no_paged):

@@ -31,7 +31,6 @@
 namespace sdv {
 namespace {
 
-constexpr int kFlatStages = 4;     // ring slots: 3 blocks in flight while one is computed
 constexpr int kFlatMaxPieces = 64; // pieces planned at once (more: the range is cut)
 
 struct FlatPiece {
@@ -39,18 +38,41 @@ struct FlatPiece {
   int first;   // the piece's first block within its pair
   int start;   // its first block within the planned run
   int slot;    // split slot of the partial
+  int nb;      // blocks of its pair
 };
+
+// LDS bytes of the flat kernel with st ring slots.  The request prefix shares the ring's
+// bytes: it is read only while a range is planned, before the ring runs.
+template <int RT, int D, int KDT>
+constexpr int flat_lds_bytes(int st) {
+  return st * Geo<D, KDT>::BLOCK + st * RT * 16 * D * 2 + kMaxDenseBlocks * 4 +
+         (kFlatMaxPieces + 1) * static_cast<int>(sizeof(FlatPiece));
+}
+
+// Ring slots: four (three blocks in flight while one is computed), or three where that
+// lets two workgroups share a CU (80 KiB of LDS each) and four do not.  Only row tiles of
+// up to 32 rows leave the registers of two waves per SIMD; 64-row tiles keep four slots.
+template <int RT, int D, int KDT>
+constexpr int flat_stages() {
+  constexpr int kTwoPerCu = 80 * 1024;
+  return RT > 2 || flat_lds_bytes<RT, D, KDT>(4) <= kTwoPerCu ? 4
+         : flat_lds_bytes<RT, D, KDT>(3) <= kTwoPerCu ? 3 : 4;
+}
 
 template <int RT, int D, int KDT>
 struct FlatLds {
   using Gm = Geo<D, KDT>;
+  static constexpr int ST = flat_stages<RT, D, KDT>();
   static constexpr int ROWS = RT * 16;
   static constexpr int QBYTES = ROWS * D * 2;   // one piece's query rows, bf16 [row][D]
-  __attribute__((aligned(16))) char ring[kFlatStages * Gm::BLOCK];
-  __attribute__((aligned(16))) char qbuf[kFlatStages * QBYTES];
+  static_assert(sizeof(PersistLds) <= ST * Gm::BLOCK, "the request prefix fits the ring");
+  union {
+    __attribute__((aligned(16))) char ring[ST * Gm::BLOCK];
+    PersistLds pl;                          // while a range is planned
+  };
+  __attribute__((aligned(16))) char qbuf[ST * QBYTES];
   int x[kMaxDenseBlocks];                   // page index of each planned block, -1 invalid
   FlatPiece piece[kFlatMaxPieces + 1];      // + sentinel: piece[n].start = planned blocks
-  PersistLds pl;
 };
 
 template <int RT, int D, int KDT, int MODE>
@@ -63,7 +85,7 @@ __device__ __forceinline__ void flat_attend(FlatLds<RT, D, KDT>& sh, const AttnA
   constexpr int NT = Gm::NT;
   constexpr int NCP = 4 / RT;          // output-channel parts
   constexpr int NTW = NT / NCP;        // output tiles per wave
-  constexpr int kStages = kFlatStages;
+  constexpr int kStages = LdsT::ST;
   constexpr int QI = LdsT::QBYTES / 1024;           // 1 KiB copy instructions per query tile
   constexpr int QPW = (QI + 3) / 4;                 // per wave
   static_assert(NTW >= 1 && QI >= 1, "tiles per wave");
@@ -434,8 +456,12 @@ sdv_attn_flat_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   const int end = static_cast<int>(min<int64_t>(static_cast<int64_t>(begin) + L, W));
   int r = persistent_request(sh.pl, a.B, Hkv, begin);
   int pos = begin;
+  bool planned_before = false;
   while (pos < end) {
     // ---- plan: the pieces of [pos, end), at most kFlatMaxPieces of them ----
+    // (the ring has overwritten the request prefix since the last plan: rebuild it)
+    if (planned_before) persistent_prefix<MODE>(sh.pl, a, ds, ss);
+    planned_before = true;
     int npieces = 0, nblk = 0;
     while (pos < end && npieces < kFlatMaxPieces) {
       const int c0 = __builtin_amdgcn_readfirstlane(sh.pl.cum[r]);
@@ -455,6 +481,7 @@ sdv_attn_flat_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
         pc.first = pos - pair0;
         pc.start = nblk;
         pc.slot = g - pair0 / L;
+        pc.nb = nb;
       }
       nblk += stop - pos;
       ++npieces;
@@ -498,9 +525,7 @@ sdv_attn_flat_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
     // pieces that end their pair: the pair's later split slots hold no keys (written after
     // the ring, so that no store is queued ahead of the first block copies)
     for (int k = 0; k < npieces; ++k) {
-      const int rr = __builtin_amdgcn_readfirstlane(sh.piece[k].r);
-      const int nb = __builtin_amdgcn_readfirstlane(sh.pl.cum[rr + 1]) -
-                     __builtin_amdgcn_readfirstlane(sh.pl.cum[rr]);
+      const int nb = __builtin_amdgcn_readfirstlane(sh.piece[k].nb);
       const int n = __builtin_amdgcn_readfirstlane(sh.piece[k + 1].start) -
                     __builtin_amdgcn_readfirstlane(sh.piece[k].start);
       const int slot = __builtin_amdgcn_readfirstlane(sh.piece[k].slot);
