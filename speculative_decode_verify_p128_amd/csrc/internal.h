@@ -84,6 +84,8 @@ struct AttnArgs {
   int32_t out_dt;
   int32_t* dev_err;
   int32_t target_wgs;           // workgroups the GPU holds at once for the chosen kernel
+  int32_t order_by_work;        // grid positions take requests longest first (sparse
+                                // per-wave launches of more workgroups than the GPU holds)
 };
 
 // Bytes per stored element of an sdv_dtype.

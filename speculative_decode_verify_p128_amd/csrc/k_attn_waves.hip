@@ -439,6 +439,118 @@ constexpr int waves_occupancy() {
   return RT == 1 && sizeof(WavesLds<RT, D, KDT, MODE>) <= 80 * 1024 ? 2 : 1;
 }
 
+// Requests a launch may order by work, and the largest work key (qo_len x top_k <= 512).
+constexpr int kOrderMaxRequests = 1024;
+constexpr int kOrderKeys = 512;
+
+// LDS of the ordering step (inside the ring, not yet in use when it runs).
+struct OrderLds {
+  int row0[kOrderMaxRequests];
+  int qo[kOrderMaxRequests];
+  int kv[kOrderMaxRequests];
+  int key[kOrderMaxRequests];
+  int hist[kOrderKeys];
+  int start[kOrderKeys];      // requests with a larger key (or equal key, lower bin)
+  int wave_tot[256 / kWave];
+  int pick[2];
+};
+
+// Exclusive prefix over the workgroup of one int per thread (thread order), with the
+// total: lane shuffles inside each wave, then the four wave totals.  All threads call;
+// two barriers.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += t;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < 256 / kWave; ++k) {
+    const int tw = wave_tot[k];
+    base += k < wv ? tw : 0;
+    total += tw;
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
+// The request that grid position pos takes when the requests are ordered longest first:
+// by the pages their tokens can select, min(valid pages, qo_len x top_k) (inconsistent
+// requests count 0), ties by index.  With more (request, KV head) workgroups than the GPU
+// holds at once, the long ones then start in the first generation and the short ones
+// fill the last.  Every workgroup derives the same order from the lengths: a histogram
+// of the keys, its prefix from the largest key down, the key bin that holds position
+// pos, then the requests of that bin in index order.  The request's lengths are returned
+// from the same loads.  All threads call.
+__device__ int request_by_work(OrderLds& o, const AttnArgs& a, const SparseSource& ss, int pos,
+                               int& row0, int& qo, int& kv) {
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  for (int k = tid; k < kOrderKeys; k += 256) o.hist[k] = 0;
+  for (int i = tid; i < B; i += 256) {
+    const int r0 = a.qo_indptr[i];
+    const int q = a.qo_indptr[i + 1] - r0;
+    const int k = a.kv_len[i];
+    o.row0[i] = r0;
+    o.qo[i] = q;
+    o.kv[i] = k;
+    // any lengths give a key in [0, kOrderKeys): the kernel's own checks reject the
+    // inconsistent ones later
+    const bool ok = q >= 1 && q <= a.max_qo_len && k >= q;
+    const int pages = k / kPage + (k % kPage != 0);
+    o.key[i] = ok ? min(min(pages, q * ss.top_k), kOrderKeys - 1) : 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < B; i += 256) atomicAdd(&o.hist[o.key[i]], 1);
+  __syncthreads();
+  // start[k] = requests with key > k: thread t owns keys 511 - 2t and 510 - 2t
+  static_assert(kOrderKeys == 2 * 256, "two key bins a thread");
+  const int k_hi = kOrderKeys - 1 - 2 * tid;
+  const int c0 = o.hist[k_hi];
+  const int c1 = o.hist[k_hi - 1];
+  int total;
+  const int excl = block_exclusive_scan(c0 + c1, o.wave_tot, total);
+  o.start[k_hi] = excl;
+  o.start[k_hi - 1] = excl + c0;
+  if (pos >= excl && pos < excl + c0) o.pick[0] = k_hi;
+  if (pos >= excl + c0 && pos < excl + c0 + c1) o.pick[0] = k_hi - 1;
+  __syncthreads();
+  const int ks = o.pick[0];
+  const int m = pos - o.start[ks];
+  // the m-th request (by index) whose key is ks: thread t holds indices 4t .. 4t + 3
+  static_assert(kOrderMaxRequests == 4 * 256, "four requests a thread");
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * tid + j;
+    cnt += i < B && o.key[i] == ks;
+  }
+  int unused;
+  int before = block_exclusive_scan(cnt, o.wave_tot, unused);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * tid + j;
+    if (i < B && o.key[i] == ks) {
+      if (before == m) o.pick[1] = i;
+      ++before;
+    }
+  }
+  __syncthreads();
+  const int r = o.pick[1];
+  row0 = o.row0[r];
+  qo = o.qo[r];
+  kv = o.kv[r];
+  __syncthreads();   // the ordering's LDS is ring space again
+  return r;
+}
+
 template <int RT, int D, int KDT, int MODE, int OCC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
@@ -449,12 +561,26 @@ sdv_attn_waves_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   const int Hkv = a.num_kv_heads;
   const int split = blockIdx.y;
   const int h = blockIdx.x % Hkv;
-  const int r = static_cast<int>((blockIdx.x / Hkv + split) % static_cast<uint32_t>(a.B));
+  const int pos = static_cast<int>((blockIdx.x / Hkv + split) % static_cast<uint32_t>(a.B));
+  int r, row0, qo, kv;
+  if constexpr (is_sparse(MODE)) {
+    static_assert(sizeof(OrderLds) <= sizeof(sh.ring), "the ordering fits the ring");
+    if (a.order_by_work) {
+      r = request_by_work(*reinterpret_cast<OrderLds*>(sh.ring), a, ss, pos, row0, qo, kv);
+    } else {
+      r = pos;
+      row0 = a.qo_indptr[r];
+      qo = a.qo_indptr[r + 1] - row0;
+      kv = a.kv_len[r];
+    }
+  } else {
+    r = pos;
+    row0 = a.qo_indptr[r];
+    qo = a.qo_indptr[r + 1] - row0;
+    kv = a.kv_len[r];
+  }
   const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
                                            : static_cast<int64_t>(ss.max_pages) * kPage;
-  const int row0 = a.qo_indptr[r];
-  const int qo = a.qo_indptr[r + 1] - row0;
-  const int kv = a.kv_len[r];
   const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
                        static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
   const bool bad_cap = !bad_len && kv > kv_cap;
@@ -493,6 +619,9 @@ hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource
   static const int per_cu = resident_per_cu(sdv_attn_waves_kernel<RT, D, KDT, MODE, OCC>);
   AttnArgs args = a;
   args.target_wgs = per_cu * device_cu_count();
+  // Longest-first order where the grid runs in several generations (from the shapes only).
+  args.order_by_work = is_sparse(MODE) && a.B <= kOrderMaxRequests &&
+                       static_cast<int64_t>(a.num_kv_heads) * a.B * a.num_splits > args.target_wgs;
   dim3 grid(a.num_kv_heads * a.B, a.num_splits);
   hipLaunchKernelGGL((sdv_attn_waves_kernel<RT, D, KDT, MODE, OCC>), grid, dim3(256), 0, s, args,
                      ds, ss);
