@@ -162,10 +162,14 @@ def test_sparse_parity(w, splits, family):
 RAGGED_MANY = W.RAGGED_MIXED.scaled(name="ragged_many", batch=48,
                                     kv=("lognormal", 300, 1.0, 1, 1500, 0.25), kv_capacity=1536)
 RAGGED_MANY_FP8 = RAGGED_MANY.scaled(name="ragged_many_fp8", kv_dtype="fp8")
+# 1280 (request, KV head) pairs: more workgroups than the GPU holds even unsplit, so the
+# launch takes its requests longest first
+RAGGED_ORDER = W.RAGGED_MIXED.scaled(name="ragged_order", batch=320,
+                                     kv=("lognormal", 300, 1.0, 1, 1500, 0.25), kv_capacity=1536)
 
 
-@pytest.mark.parametrize("splits", [4, 8])
-@pytest.mark.parametrize("w", [RAGGED_MANY, RAGGED_MANY_FP8], ids=lambda w: w.name)
+@pytest.mark.parametrize("splits", [1, 4, 8])
+@pytest.mark.parametrize("w", [RAGGED_MANY, RAGGED_MANY_FP8, RAGGED_ORDER], ids=lambda w: w.name)
 def test_sparse_many_workgroups(w, splits):
     """Ragged 32-row (request, KV head) pairs, bf16 and fp8, in launches of several
     workgroups per CU: the standalone and the fused-selection forms against the oracle,
