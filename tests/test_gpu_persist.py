@@ -89,6 +89,29 @@ def test_persist_paged_parity(w, splits, family):
     assert ok, f"max abs err {worst}"
 
 
+# one long request beside many short ones at two splits: the range length follows the
+# long request, so a range holds more pieces than one plan takes and is planned again
+_MIXED_KV = (6000,) + tuple(4 + (7 * i) % 33 for i in range(1, 300))
+MIXED_VIEW64 = W.DENSE_BF16.scaled(name="mixed_view64", batch=300, kv=("list", _MIXED_KV),
+                                   kv_capacity=6016)
+MIXED_VIEW16 = W.DENSE_BF16.scaled(name="mixed_view16", batch=300, kv=("list", _MIXED_KV),
+                                   kv_capacity=6016, num_q_heads=16)
+
+
+@pytest.mark.parametrize("family", FAMILIES)
+@pytest.mark.parametrize("w", [MIXED_VIEW64, MIXED_VIEW16], ids=lambda w: w.name)
+def test_persist_view_replanned_ranges(w, family):
+    c, ref = _dense(w)
+    run = DenseRun(c)
+    view, offs = run.view()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = run.attend(view, offs, num_splits=2, dev_err=err, family=family)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ok, worst = tol_ok(out_numpy(out[:run.n]), ref, "bf16")
+    assert ok, f"max abs err {worst}"
+
+
 @pytest.mark.parametrize("family", FAMILIES)
 def test_persist_inconsistent_requests_flagged_others_exact(family):
     """Request 2 shorter than its verify tokens, request 5 beyond the table's capacity:
