@@ -106,7 +106,10 @@ __device__ __forceinline__ void halving_levels(float (&u)[V]) {
   }
 }
 
-template <int KDT, int D>
+// QDT: the stored query type, kept in LDS as stored (bf16 queries take half the bytes of
+// float: with 8 verify tokens of 4 heads a wave stages 8 KiB instead of 16 KiB, which
+// otherwise holds a CU to 10 waves where the registers allow 16).
+template <int KDT, int D, int QDT>
 __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     const void* __restrict__ q, int32_t q_dt, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ kv_len, int32_t B, int32_t max_qo_len, int32_t num_q_heads,
@@ -120,7 +123,8 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   constexpr int PPB = PPW * kProxyWaves;   // pages per workgroup
   constexpr int EB = elem_bytes<KDT>();
   constexpr int U = 16 * 16 / (V * EB);   // positions per unrolled step: 256 bytes a lane
-  extern __shared__ float q_lds[];   // [qo][G][D] float
+  extern __shared__ float q_lds[];   // [qo][G][D] float or bf16 (QDT)
+  constexpr int QEB = QDT == SDV_F32 ? 4 : 2;   // bytes per staged query channel
 
   // Request of this workgroup: y rotated by the page run z.  The hardware deals
   // consecutive workgroups round-robin to the eight XCDs, so without the rotation every
@@ -158,34 +162,34 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   int32_t phys = 0;
   if (active) phys = block_table[static_cast<int64_t>(r) * bt_stride + p];
 
-  // Stage this request's queries of KV head h as float, row (t * G + g) of D channels,
-  // eight channels (one 16- or 32-byte load) per item, QB items per thread in flight at
-  // once.  Within a row, channel chunk k (channels 4k .. 4k + 3) sits at chunk position
-  // (k % (V/4)) * LPR + k / (V/4): the e-th chunk of every lane of a page group is
-  // contiguous, so the score step's reads (one chunk per lane) are free of bank conflicts.
+  // Stage this request's queries of KV head h as stored (QDT), row (t * G + g) of D
+  // channels, eight channels (one 16- or 32-byte load) per item, QB items per thread in
+  // flight at once.  Within a row, channel chunk k (channels 4k .. 4k + 3) sits at chunk
+  // position (k % (V/4)) * LPR + k / (V/4): the e-th chunk of every lane of a page group
+  // is contiguous, so the score step's reads (one chunk per lane) are free of bank
+  // conflicts.
   constexpr int QB = 4;
+  using QChunk = typename std::conditional<QDT == SDV_F32, float4, uint2>::type;   // 4 channels
+  char* q_bytes = reinterpret_cast<char*>(q_lds);
   const int q_items = qo * G * (D / 8);
   for (int i0 = threadIdx.x; i0 < q_items; i0 += QB * blockDim.x) {
-    float4 x[QB][2];
+    QChunk x[QB][2];
 #pragma unroll
     for (int k = 0; k < QB; ++k) {
-      const int i8 = i0 + k * blockDim.x;
-      if (i8 >= q_items) continue;
+      const int i8 = min(i0 + k * static_cast<int>(blockDim.x), q_items - 1);   // in range
       const int tg = i8 / (D / 8);
       const int c0 = (i8 - tg * (D / 8)) * 8;
       const int t = tg / G;
       const int g = tg - t * G;
       const int64_t src = (static_cast<int64_t>(row0 + t) * num_q_heads + h * G + g) * D + c0;
-      if (q_dt == SDV_F32) {
+      if constexpr (QDT == SDV_F32) {
         const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + src);
         x[k][0] = s4[0];
         x[k][1] = s4[1];
       } else {
         const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + src);
-        x[k][0] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
-        x[k][1] = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
-                              __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
+        x[k][0] = make_uint2(w.x, w.y);
+        x[k][1] = make_uint2(w.z, w.w);
       }
     }
 #pragma unroll
@@ -194,7 +198,7 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
       if (i8 >= q_items) continue;
       const int tg = i8 / (D / 8);
       const int k0 = 2 * (i8 - tg * (D / 8));
-      float4* row = reinterpret_cast<float4*>(q_lds + static_cast<int64_t>(tg) * D);
+      QChunk* row = reinterpret_cast<QChunk*>(q_bytes + static_cast<int64_t>(tg) * D * QEB);
       row[(k0 % (V / 4)) * LPR + k0 / (V / 4)] = x[k][0];
       row[((k0 + 1) % (V / 4)) * LPR + (k0 + 1) / (V / 4)] = x[k][1];
     }
@@ -269,11 +273,18 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
     // Steps 2-4 for every query head of the group.
     float best = -INFINITY;
     for (int g = 0; g < G; ++g) {
-      const float4* qv = reinterpret_cast<const float4*>(q_lds + (t * G + g) * D) + sub;
+      const QChunk* qv = reinterpret_cast<const QChunk*>(q_bytes + (t * G + g) * D * QEB) + sub;
       float u[V];
 #pragma unroll
       for (int e4 = 0; e4 < V / 4; ++e4) {
-        const float4 q4 = qv[e4 * LPR];
+        float4 q4;
+        if constexpr (QDT == SDV_F32) {
+          q4 = qv[e4 * LPR];
+        } else {
+          const uint2 w = qv[e4 * LPR];   // bf16 widened exactly
+          q4 = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+        }
         u[4 * e4 + 0] = q4.x * acc[4 * e4 + 0];
         u[4 * e4 + 1] = q4.y * acc[4 * e4 + 1];
         u[4 * e4 + 2] = q4.z * acc[4 * e4 + 2];
@@ -297,7 +308,7 @@ __global__ void __launch_bounds__(64 * kProxyWaves) sdv_proxy_scores_kernel(
   }
 }
 
-template <int KDT, int D>
+template <int KDT, int D, int QDT>
 static hipError_t launch_proxy_t(const void* q, int32_t q_dt, const int32_t* qo_indptr,
                                  const int32_t* kv_len, int32_t B, int32_t max_qo_len,
                                  int32_t num_q_heads, const sdv_paged_kv& kv,
@@ -306,13 +317,13 @@ static hipError_t launch_proxy_t(const void* q, int32_t q_dt, const int32_t* qo_
   constexpr int V = ProxyVec<KDT, proxy_vb<KDT>()>::N;
   constexpr int PPB = (kWave / (D / V)) * kProxyWaves;
   const int G = num_q_heads / kv.num_kv_heads;
-  const size_t lds = static_cast<size_t>(max_qo_len) * G * D * sizeof(float);
+  const size_t lds = static_cast<size_t>(max_qo_len) * G * D * (QDT == SDV_F32 ? 4 : 2);
   // Grid x = KV head, y = request (rotated by z in the kernel), z = run of pages:
   // workgroups are dispatched x fastest, so the runs past a request's last page (empty,
   // they exit at once) come at the end of the grid rather than between busy ones (≈ 1%
   // faster on 64 requests of U[4096, 32768] tokens).
   dim3 grid(kv.num_kv_heads, B, (max_pages + PPB - 1) / PPB);
-  hipLaunchKernelGGL((sdv_proxy_scores_kernel<KDT, D>), grid, dim3(64 * kProxyWaves), lds, s, q, q_dt,
+  hipLaunchKernelGGL((sdv_proxy_scores_kernel<KDT, D, QDT>), grid, dim3(64 * kProxyWaves), lds, s, q, q_dt,
                      qo_indptr, kv_len, B, max_qo_len, num_q_heads, G, kv.k, kv.page_stride,
                      kv.num_pages, block_table, bt_stride, max_pages, scores, dev_err);
   return hipGetLastError();
@@ -325,8 +336,13 @@ hipError_t launch_proxy_scores(const void* q, int32_t q_dt, const int32_t* qo_in
                                float* scores, int32_t* dev_err, hipStream_t s) {
 #define SDV_PROXY_CASE(KDT, D)                                                               \
   if (kv.kv_dtype == KDT && kv.head_dim == D)                                                \
-    return launch_proxy_t<KDT, D>(q, q_dt, qo_indptr, kv_len, B, max_qo_len, num_q_heads, kv, \
-                                  block_table, max_pages, bt_stride, scores, dev_err, s);
+    return q_dt == SDV_F32                                                                   \
+               ? launch_proxy_t<KDT, D, SDV_F32>(q, q_dt, qo_indptr, kv_len, B, max_qo_len,  \
+                                                 num_q_heads, kv, block_table, max_pages,    \
+                                                 bt_stride, scores, dev_err, s)              \
+               : launch_proxy_t<KDT, D, SDV_BF16>(q, q_dt, qo_indptr, kv_len, B, max_qo_len, \
+                                                  num_q_heads, kv, block_table, max_pages,   \
+                                                  bt_stride, scores, dev_err, s);
   SDV_PROXY_CASE(SDV_F32, 64)
   SDV_PROXY_CASE(SDV_F32, 128)
   SDV_PROXY_CASE(SDV_BF16, 64)
