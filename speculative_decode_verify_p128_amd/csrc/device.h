@@ -198,11 +198,16 @@ __device__ __forceinline__ void wave_topk_keys(const float* srow, int n, int lan
   }
 }
 
-// T for k_eff = min(top_k, n) of n <= 4096 keys (1 when every key is selected), each
-// count a wave sum of per-lane counts (measured faster than counting each comparison's
-// lane mask in scalar registers: 15.9 against 16.5 us for 1024 pages, top-64, 128 rows);
-// the page word's high 20 bits are the same in every key (pages < 4096) and are set at
-// once.
+// A threshold T with exactly k_eff = min(top_k, n) of n <= 4096 keys at or above it (1
+// when every key is selected), each count a wave sum of per-lane counts (measured faster
+// than counting each comparison's lane mask in scalar registers: 15.9 against 16.5 us for
+// 1024 pages, top-64, 128 rows); the page word's high 20 bits are the same in every key
+// (pages < 4096) and are set at once.  The search stops at the first candidate that
+// exactly k_eff keys reach: keys are unique, so those are the k_eff largest, the same
+// selection as the k_eff-th largest key itself gives.  Real-valued scores usually leave a
+// gap of thousands of ulps between the k_eff-th and the next key, and the search stops
+// after 10-26 of its 44 rounds (about 16 on normal scores over 1024 pages, top-64);
+// equal scores across the threshold still take every round.
 // Sum of v over the wave, the same in every lane: rotate-and-add inside each 16-lane row
 // (DPP row_ror), then the four row sums read into scalar registers.
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
@@ -226,15 +231,24 @@ __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&key)[ITEMS], i
     return wave_sum_u32(m);
   };
   if (k_eff >= n) return 1ull;
+  const uint32_t want = static_cast<uint32_t>(k_eff);
   uint64_t T = 0;
   for (int bit = 63; bit >= 32; --bit) {
     const uint64_t c = T | (1ull << bit);
-    if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
+    const uint32_t m = count_ge(c);
+    if (m >= want) {
+      T = c;
+      if (m == want) return T;
+    }
   }
   T |= 0xfffff000ull;
   for (int bit = 11; bit >= 0; --bit) {
     const uint64_t c = T | (1ull << bit);
-    if (count_ge(c) >= static_cast<uint32_t>(k_eff)) T = c;
+    const uint32_t m = count_ge(c);
+    if (m >= want) {
+      T = c;
+      if (m == want) return T;
+    }
   }
   return T;
 }

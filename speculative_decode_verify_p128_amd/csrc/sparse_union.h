@@ -28,7 +28,10 @@ struct UnionLds {
 static_assert(4 * kWave <= kMaxUnion, "the selection's staging fits the union's page arrays");
 
 // One wave selects the k_eff = min(top_k, n) <= 64 best of srow[0 .. n-1] by the bit
-// search and writes them in rank order to lout (and gout when non-null); returns k_eff.
+// search and writes them to lout, in rank order when gout is non-null (and to gout too);
+// returns k_eff.  Without gout the selection only feeds the page union, which does not
+// depend on the order, so the pages go to lout unsorted: each selected key to its slot
+// among the keys >= T (no bitonic network, no staging round trip through LDS).
 template <int ITEMS>
 __device__ __forceinline__ int wave_bits_select(const float* srow, int n, int top_k, int lane,
                                                 uint32_t* st_hi, uint32_t* st_lo, int32_t* lout,
@@ -37,6 +40,13 @@ __device__ __forceinline__ int wave_bits_select(const float* srow, int n, int to
   wave_topk_keys(srow, n, lane, key);
   const int k_eff = top_k < n ? top_k : n;
   const uint64_t T = wave_kth_key(key, n, k_eff);
+  if (!gout) {
+    uint32_t pos = wave_selection_offset(key, T, lane);
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (key[i] >= T) lout[pos++] = topk_key_page(key[i]);
+    return k_eff;
+  }
   const uint64_t v = wave_ranked_selection(key, T, lane, k_eff, st_hi, st_lo);
   if (lane < k_eff) {
     const int page = topk_key_page(v);
@@ -50,7 +60,8 @@ __device__ __forceinline__ int wave_bits_select(const float* srow, int n, int to
 // cost does not grow with top_k, while the repeated maximum costs about top_k x (items +
 // 8) dependent instructions; with top_k <= 64 the mark is passed from 11 key slots a lane
 // (over 640 pages) on.  Measured on 8 requests of 131072 fp8 tokens (1024 pages), top-64:
-// the fused selection and attention 85.6 -> 68.2 us at 16 splits.
+// the fused selection and attention 85.6 -> 68.2 us at 16 splits (66.6 -> 61.5 us once
+// the search stops early and feeds the union unsorted).
 __host__ __device__ constexpr bool select_by_bits(int n, int top_k) {
   return n > 4 * kWave && top_k <= kWave && top_k * ((n + kWave - 1) / kWave + 8) > 1200;
 }
