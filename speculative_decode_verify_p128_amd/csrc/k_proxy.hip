@@ -19,9 +19,11 @@
 //   64/LPR full page rows.  fp8 takes 8-byte slices so that a wave holds four pages rather
 //   than eight: on 8 x 131072 fp8 tokens (32 pairs of 1024 pages) the 16-byte form fills
 //   the GPU with exactly one generation of waves and nothing evens out their finishing
-//   times (104.9 against 98.3 us, same scores bit for bit). (bf16 in 8-byte slices, two
-//   pages a wave, measured slower: 208 against 205 us on 64 x U[4096, 32768] tokens, 230
-//   against 180 us on a ragged batch.)  Small workgroups keep the tail of the grid short
+//   times (104.9 against 98.3 us, same scores bit for bit); 4-byte slices, two pages a
+//   wave and four generations, measured slower again (101 against 98.5 us). (bf16 in
+//   8-byte slices, two pages a wave, measured slower: 208 against 205 us on 64 x
+//   U[4096, 32768] tokens, 230 against 180 us on a ragged batch.)  Small workgroups keep
+//   the tail of the grid short
 //   when requests differ in length.  Each lane keeps 256 bytes of rows in flight (16 rows
 //   of 16-byte slices, 32 of 8-byte: fp8 with 16 rows measured 2.8% slower); the loads are
 //   non-temporal (the keys are read once, so they should not displace what the caches
