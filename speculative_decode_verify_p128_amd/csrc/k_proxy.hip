@@ -13,7 +13,7 @@
 //   4. maximum over the G query heads; -0 becomes +0.
 //
 // Design (HBM-bound; K of every valid page is read exactly once for all tokens):
-//   one workgroup = one wave per (request, KV head, run of 64/LPR pages); a group of LPR
+//   one workgroup = four waves per (request, KV head, run of 4 x 64/LPR pages); a group of LPR
 //   lanes owns one page, each lane a contiguous slice of every key row (16 bytes: 8 bf16
 //   or 4 f32 channels; 8 bytes: 8 fp8 channels), so each wave load instruction reads
 //   64/LPR full page rows.  fp8 takes 8-byte slices so that a wave holds four pages rather
@@ -22,9 +22,12 @@
 //   times (104.9 against 98.3 us, same scores bit for bit); 4-byte slices, two pages a
 //   wave and four generations, measured slower again (101 against 98.5 us). (bf16 in
 //   8-byte slices, two pages a wave, measured slower: 208 against 205 us on 64 x
-//   U[4096, 32768] tokens, 230 against 180 us on a ragged batch.)  Small workgroups keep
-//   the tail of the grid short
-//   when requests differ in length.  Each lane keeps 256 bytes of rows in flight (16 rows
+//   U[4096, 32768] tokens, 230 against 180 us on a ragged batch.)  Four waves a workgroup
+//   share one staging of the queries and make a quarter of the workgroups: against one
+//   wave 198 -> 195 us on 64 x U[4096, 32768] bf16 tokens, 97.7 -> 94.8 us on 8 x 131072
+//   fp8 tokens, 159.6 -> 156.9 us on a ragged batch (two waves: 198, 97, 157; eight: 204,
+//   94, 162: past a short request's last page the waves of a large workgroup idle, and
+//   its LDS stays held until they all end).  Each lane keeps 256 bytes of rows in flight (16 rows
 //   of 16-byte slices, 32 of 8-byte: fp8 with 16 rows measured 2.8% slower); the loads are
 //   non-temporal (the keys are read once, so they should not displace what the caches
 //   hold), which measured about 20% faster than ordinary loads on this streaming pattern.
@@ -49,7 +52,7 @@ __device__ __forceinline__ uint4 load_stream(const char* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
 }
 
-constexpr int kProxyWaves = 1;   // waves per workgroup
+constexpr int kProxyWaves = 4;   // waves per workgroup
 
 // A lane's slice of a key row: VB bytes loaded non-temporally and decoded to N floats.
 // 16-byte slices for f32 and bf16; fp8 rows are cut in 8-byte slices (8 channels a
