@@ -56,12 +56,15 @@ __device__ __forceinline__ int wave_bits_select(const float* srow, int n, int to
   return k_eff;
 }
 
-// Whether a token with n valid pages selects by the bit search (WIDE kernels only): its
-// cost does not grow with top_k, while the repeated maximum costs about top_k x (items +
-// 8) dependent instructions; with top_k <= 64 the mark is passed from 11 key slots a lane
-// (over 640 pages) on.  Measured on 8 requests of 131072 fp8 tokens (1024 pages), top-64:
-// the fused selection and attention 85.6 -> 68.2 us at 16 splits (66.6 -> 61.5 us once
-// the search stops early and feeds the union unsorted).
+// Whether a token with n valid pages selects by the bit search when its ranked selection
+// is written out too (WIDE kernels only): its cost does not grow with top_k, while the
+// repeated maximum costs about top_k x (items + 8) dependent instructions; with top_k <=
+// 64 the mark is passed from 11 key slots a lane (over 640 pages) on.  Measured on 8
+// requests of 131072 fp8 tokens (1024 pages), top-64: the fused selection and attention
+// 85.6 -> 68.2 us at 16 splits (66.6 -> 61.5 us once the search stops early and feeds the
+// union unsorted).  A selection that only feeds the union takes the bit search whenever
+// top_k <= 64 and n > top_k, since no sort follows it then (64 x U[4096, 32768] tokens,
+// top-16: 146.0 -> 145.0 us for the fused call; a ragged batch 239.2 -> 238.4 us).
 __host__ __device__ constexpr bool select_by_bits(int n, int top_k) {
   return n > 4 * kWave && top_k <= kWave && top_k * ((n + kWave - 1) / kWave + 8) > 1200;
 }
@@ -94,12 +97,20 @@ __device__ inline void select_topk(UnionLds& u, const SparseSource& ss, int h, i
     // register slots per lane sized to this token's pages (each round rescans them)
     const int items = (n + kWave - 1) / kWave;
     int k_eff;
+    // the keys are gathered through the union's page arrays, filled only after the
+    // selection
+    uint32_t* st_hi = reinterpret_cast<uint32_t*>(u.upage) + wave * kWave;
+    uint32_t* st_lo = reinterpret_cast<uint32_t*>(u.uphys) + wave * kWave;
     if (WIDE && select_by_bits(n, ss.top_k)) {
-      // the keys are gathered through the union's page arrays, filled only after the
-      // selection
-      uint32_t* st_hi = reinterpret_cast<uint32_t*>(u.upage) + wave * kWave;
-      uint32_t* st_lo = reinterpret_cast<uint32_t*>(u.uphys) + wave * kWave;
       k_eff = wave_bits_select<16>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
+    } else if (!gout && ss.top_k <= kWave && n > ss.top_k) {
+      // feeding the union only (no ranked output): the bit search, which stops after
+      // about 14 rounds on real-valued scores, against top_k rounds of the maximum
+      if (items <= 1) k_eff = wave_bits_select<1>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
+      else if (items <= 2) k_eff = wave_bits_select<2>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
+      else if (items <= 4) k_eff = wave_bits_select<4>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
+      else if (items <= 8) k_eff = wave_bits_select<8>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
+      else k_eff = wave_bits_select<16>(srow, n, ss.top_k, lane, st_hi, st_lo, lout, gout);
     } else if (items <= 1) k_eff = wave_ladder_topk<1>(srow, n, ss.top_k, lane, emit);
     else if (items <= 2) k_eff = wave_ladder_topk<2>(srow, n, ss.top_k, lane, emit);
     else if (items <= 4) k_eff = wave_ladder_topk<4>(srow, n, ss.top_k, lane, emit);
