@@ -86,6 +86,8 @@ struct AttnArgs {
   int32_t target_wgs;           // workgroups the GPU holds at once for the chosen kernel
   int32_t order_by_work;        // grid positions take requests longest first (sparse
                                 // per-wave launches of more workgroups than the GPU holds)
+  int32_t dense_compact;        // dense split-KV grid positions take the (request, KV head,
+                                // chunk) pieces that hold blocks, in order (ring kernel)
 };
 
 // Bytes per stored element of an sdv_dtype.

@@ -328,16 +328,39 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
   // (empty for short requests) are dispatched last.  The request index is rotated by the
   // split, so that a request's splits alternate between XCDs instead of all landing on the
   // XCDs its unrotated position picks (with four KV heads, one half of them): 78 -> 76 us
-  // on 32 requests of U[1024, 8192] bf16 tokens at 4 splits, 92 -> 85 us at 8.
+  // on 32 requests of U[1024, 8192] bf16 tokens at 4 splits, 92 -> 85 us at 8.  Dense
+  // calls with splits number their pieces by dense_compact_piece instead (77 -> 73-75 us
+  // on the same requests at 6 splits).
   const int Hkv = a.num_kv_heads;
-  const int split = blockIdx.y;
-  const int h = blockIdx.x % Hkv;
-  const int r = static_cast<int>((blockIdx.x / Hkv + split) % static_cast<uint32_t>(a.B));
+  int split = blockIdx.y;
+  int h = blockIdx.x % Hkv;
+  int r = static_cast<int>((blockIdx.x / Hkv + split) % static_cast<uint32_t>(a.B));
   const int64_t kv_cap = MODE == kSrcView ? static_cast<int64_t>(ds.max_sub_pages) * kSub
                                            : static_cast<int64_t>(ss.max_pages) * kPage;
-  const int row0 = a.qo_indptr[r];
-  const int qo = a.qo_indptr[r + 1] - row0;
-  const int kv = a.kv_len[r];
+  // Dense split-KV: grid positions take the pieces sized to the requests instead (the
+  // ring is free before the first copy).
+  DensePiece pc{};
+  int row0, qo, kv;
+  bool compact = false;
+  if constexpr (!is_sparse(MODE)) {
+    if (a.dense_compact) {
+      const int cap = MODE == kSrcView ? ds.max_sub_pages : 4 * ss.max_pages;
+      if (!dense_compact_piece(a, cap, reinterpret_cast<int*>(sh.ring), pc)) return;
+      compact = true;
+      r = pc.r;
+      h = pc.h;
+      split = pc.j;
+    }
+  }
+  if (compact) {
+    row0 = pc.row0;
+    qo = pc.qo;
+    kv = pc.kv;
+  } else {
+    row0 = a.qo_indptr[r];
+    qo = a.qo_indptr[r + 1] - row0;
+    kv = a.kv_len[r];
+  }
   const bool bad_len = qo < 1 || qo > a.max_qo_len || kv < qo || row0 < 0 ||
                        static_cast<int64_t>(row0) + qo > static_cast<int64_t>(a.B) * a.max_qo_len;
   const bool bad_cap = !bad_len && kv > kv_cap;
@@ -347,6 +370,25 @@ sdv_attn_stream_kernel(AttnArgs a, DenseSource ds, SparseSource ss) {
     return;
   }
   BlockList<MODE, D, KDT> bl;
+  if constexpr (!is_sparse(MODE)) {
+    if (compact) {
+      // the pair's run 0 marks the partial slots past its last run empty for the combine
+      if (split == 0) {
+        const int G = a.num_q_heads / Hkv;
+        const int64_t rows_cap = static_cast<int64_t>(a.B) * a.max_qo_len;
+        const int n_fill = (a.num_splits - pc.k) * qo * G;
+        for (int e = threadIdx.x; e < n_fill; e += blockDim.x) {
+          const int s = pc.k + e / (qo * G);
+          const int t = (e / G) % qo;
+          const int g = e % G;
+          a.part_lse[(s * rows_cap + row0 + t) * a.num_q_heads + h * G + g] = -INFINITY;
+        }
+      }
+      bl.stage_range(sh.ul, a, ds, ss, r, pc.first, pc.n);
+      ring_attend<RT, D, KDT, MODE, kRingStages>(sh, a, ds, ss, bl, r, h, row0, qo, kv, split);
+      return;
+    }
+  }
   bl.stage(sh.ul, &sh.chunk, a, ds, ss, r, h, split, row0, qo, kv);
   ring_attend<RT, D, KDT, MODE, kRingStages>(sh, a, ds, ss, bl, r, h, row0, qo, kv,
                                              a.num_splits > 1 ? split : -1);
@@ -358,6 +400,7 @@ hipError_t launch_t(const AttnArgs& a, const DenseSource& ds, const SparseSource
   static const int per_cu = resident_per_cu(sdv_attn_stream_kernel<RT, D, KDT, MODE>);
   AttnArgs args = a;
   args.target_wgs = per_cu * device_cu_count();
+  args.dense_compact = !is_sparse(MODE) && a.num_splits > 1 && a.B <= kCompactMaxRequests;
   dim3 grid(a.num_kv_heads * a.B, a.num_splits);
   hipLaunchKernelGGL((sdv_attn_stream_kernel<RT, D, KDT, MODE>), grid, dim3(256), 0, s, args, ds, ss);
   return hipGetLastError();

@@ -336,6 +336,158 @@ __device__ inline int dense_chunk(const AttnArgs& a, int max_blocks, int* slot_l
   return *slot_lds;
 }
 
+// Dense split-KV pieces sized to the requests (ring kernel, num_splits > 1).  Each
+// (request, KV head) pair with nb blocks is cut into k = max(1, ceil(nb / c)) near-equal
+// runs, c the smallest run length for which all pairs' runs fit the workgroups the GPU
+// holds at once and no pair needs more than num_splits of them (its partial slots), so
+// that every workgroup with work is resident from the start and none carries more than
+// c blocks; one run length for all pairs instead puts up to num_splits runs of the
+// longest request's length on a CU while short requests leave theirs idle.  The runs
+// are numbered level by level (every pair's run 0, then run 1 of the pairs with two or
+// more, ...), pairs in request-major order, and grid position lin (dispatch order) takes
+// run lin; positions past the last run return false.  B <= kCompactMaxRequests.  All
+// threads call; wave 0 reads every request's lengths (one round trip); lds holds 9 ints.
+constexpr int kCompactMaxRequests = 512;
+
+struct DensePiece {
+  int r, h, j;       // request, KV head, run (= partial slot)
+  int first, n;      // blocks [first, first + n) of the request
+  int k;             // runs of the pair
+  int row0, qo, kv;  // the request's first query row, query rows and KV length
+};
+
+// ceil(v / c) for 0 <= v < 2^24, 1 <= c < 2^24: a float quotient corrected by one step
+// (an integer division is a long instruction sequence, and the search below takes many)
+__device__ __forceinline__ int ceil_div_small(int v, int c, float rc) {
+  int q = static_cast<int>(static_cast<float>(v) * rc);
+  q += (q + 1) * c <= v ? 1 : 0;
+  q -= q * c > v ? 1 : 0;
+  return q + (q * c < v ? 1 : 0);
+}
+
+__device__ inline bool dense_compact_piece(const AttnArgs& a, int max_blocks, int* lds,
+                                           DensePiece& pc) {
+  constexpr int NI = kCompactMaxRequests / kWave;
+  const int tid = threadIdx.x;
+  const int Hkv = a.num_kv_heads;
+  const int S = a.num_splits;
+  const int lin = static_cast<int>(blockIdx.y * gridDim.x + blockIdx.x);
+  if (tid < kWave) {
+    const int lane = tid;
+    const int ni = (a.B + kWave - 1) / kWave;   // item slots in use (wave-uniform)
+    int nb[NI], row0s[NI], qos[NI], kvs[NI];
+    int sum = 0, mx = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int rr = lane + kWave * i;
+      int v = 0, r0 = 0, q1 = 0, kk = 0;
+      if (i < ni && rr < a.B) {
+        kk = a.kv_len[rr];
+        r0 = a.qo_indptr[rr];
+        q1 = a.qo_indptr[rr + 1];
+        v = kk <= 0 ? 0 : min((kk + kSub - 1) / kSub, max_blocks);
+      }
+      nb[i] = v;
+      row0s[i] = r0;
+      qos[i] = q1 - r0;
+      kvs[i] = kk;
+      sum += v;
+      mx = max(mx, v);
+    }
+    // wave reductions by DPP rotations and lane reads (no LDS round trips: the search
+    // below takes a dozen of them in a row)
+    sum = static_cast<int>(wave_sum_u32(static_cast<uint32_t>(sum)));
+    mx = static_cast<int>(wave_max_u32(static_cast<uint32_t>(mx)));
+    auto runs_of = [&](int v, int c, float rc) { return v <= c ? 1 : ceil_div_small(v, c, rc); };
+    auto pieces = [&](int c) {   // runs over all pairs at run length c (wave-uniform)
+      const float rc = 1.0f / static_cast<float>(c);
+      int t = 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (i < ni && lane + kWave * i < a.B) t += runs_of(nb[i], c, rc);
+      return static_cast<int>(wave_sum_u32(static_cast<uint32_t>(t))) * Hkv;
+    };
+    // smallest c in [lo, hi] with pieces(c) <= resident workgroups (pieces is
+    // non-increasing in c; at c = mx every pair is one run), at least what num_splits
+    // runs need for the longest request and at most the kMaxDenseBlocks a workgroup
+    // stages (the caller guarantees ceil(max_blocks / num_splits) fits)
+    const int full = max(a.target_wgs, 1);
+    const int need = max((mx + S - 1) / S, 1);
+    const int64_t even = (static_cast<int64_t>(sum) * Hkv + full - 1) / full;
+    int lo = static_cast<int>(max<int64_t>(need, min<int64_t>(even, kMaxDenseBlocks)));
+    int hi = max(min(mx, kMaxDenseBlocks), lo);
+    // pieces(c) <= sum * Hkv / c + pairs, so c = ceil(sum * Hkv / (full - pairs)) fits
+    const int pairs = a.B * Hkv;
+    if (full > pairs) {
+      const int64_t fit = (static_cast<int64_t>(sum) * Hkv + (full - pairs) - 1) / (full - pairs);
+      hi = max(lo, static_cast<int>(min<int64_t>(hi, max<int64_t>(fit, 1))));
+    }
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (pieces(mid) <= full) hi = mid;
+      else lo = mid + 1;
+    }
+    const int c = lo;
+    const float rc = 1.0f / static_cast<float>(c);
+    int k[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) k[i] = runs_of(nb[i], c, rc);
+    // level j holds the pairs of the requests with more than j runs
+    int base = 0, j = -1, idx = 0;
+    for (int jj = 0; jj < S; ++jj) {
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) cnt += (i < ni && lane + kWave * i < a.B && k[i] > jj) ? 1 : 0;
+      cnt = static_cast<int>(wave_sum_u32(static_cast<uint32_t>(cnt)));
+      if (cnt == 0) break;
+      if (lin < base + cnt * Hkv) {
+        j = jj;
+        idx = lin - base;
+        break;
+      }
+      base += cnt * Hkv;
+    }
+    if (lane == 0) lds[0] = j;
+    if (j >= 0) {
+      // the (idx / Hkv)-th request (in index order) with more than j runs
+      const int want = idx / Hkv;
+      int seen = 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bool f = i < ni && lane + kWave * i < a.B && k[i] > j;
+        const uint64_t m = __ballot(f);
+        const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+        if (f && seen + below == want) {
+          const int sz = (nb[i] + k[i] - 1) / k[i];
+          const int first = j * sz;
+          lds[1] = lane + kWave * i;
+          lds[2] = idx - want * Hkv;
+          lds[3] = first;
+          lds[4] = max(0, min(nb[i], first + sz) - first);
+          lds[5] = k[i];
+          lds[6] = row0s[i];
+          lds[7] = qos[i];
+          lds[8] = kvs[i];
+        }
+        seen += __builtin_popcountll(m);
+      }
+    }
+  }
+  __syncthreads();
+  pc.j = lds[0];
+  if (pc.j < 0) return false;
+  pc.r = lds[1];
+  pc.h = lds[2];
+  pc.first = lds[3];
+  pc.n = lds[4];
+  pc.k = lds[5];
+  pc.row0 = lds[6];
+  pc.qo = lds[7];
+  pc.kv = lds[8];
+  return true;
+}
+
 // Where the 32-token blocks of a (request, KV head) come from.
 enum SourceMode : int {
   kSrcView = 0,     // dense, through the P32 sub-page view of the draft layer

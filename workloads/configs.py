@@ -88,7 +88,7 @@ TINY_FP32 = VerifyWorkload(
 DENSE_BF16 = VerifyWorkload(
     name="dense_bf16", batch=32, qo=4, kv=("uniform", 1024, 8192),
     num_q_heads=64, num_kv_heads=4, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
-    values="normal", top_k=16, num_splits=4, slot_stride=8, root_page=6,
+    values="normal", top_k=16, num_splits=6, slot_stride=8, root_page=6,
     pool_index_scale=8)
 
 # 3. Block-sparse target layer, bf16.
