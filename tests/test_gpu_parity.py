@@ -94,6 +94,33 @@ def test_dense_parity(w, splits, family):
     assert ok, f"max abs err {worst}"
 
 
+# Over 64 requests (two of them a lane in the plan of the dense pieces) and fewer
+# (request, KV head) pairs than the GPU holds: the ring kernel's request-sized pieces,
+# with unused partial slots marked empty when a pair takes fewer runs than splits.
+DENSE_MANY = W.DENSE_BF16.scaled(name="dense_many", batch=100, kv=("uniform", 40, 1200),
+                                 kv_capacity=1216)
+
+
+@pytest.fixture(scope="module")
+def dense_many():
+    c = W.make_dense_case(DENSE_MANY)
+    return c, dense_oracle(c)
+
+
+@pytest.mark.parametrize("family", [0, 4])
+@pytest.mark.parametrize("splits", [2, 6, 16])
+def test_dense_pieces_many_requests(dense_many, splits, family):
+    c, ref = dense_many
+    run = DenseRun(c)
+    view, offs = run.view()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = run.attend(view, offs, num_splits=splits, dev_err=err, family=family)
+    torch.cuda.synchronize()
+    ok, worst = tol_ok(out_numpy(out[:run.n]), ref, "bf16")
+    assert int(err.item()) == 0
+    assert ok, f"max abs err {worst}"
+
+
 @pytest.mark.parametrize("w", SPARSE_CASES + [D64_FP8], ids=lambda w: w.name)
 def test_proxy_scores_bit_exact(w):
     c = W.make_sparse_case(w)
