@@ -166,13 +166,17 @@ int32_t kv_subpage_view_init(const sdv_subpage_geom* geom, const int32_t* block_
  * view         host: from kv_subpage_view_init.
  * sub_offsets  device int32 [B][2][max_sub_pages]; kv_len[r] <= 32 * max_sub_pages.
  * num_splits   >= 1: the most partial results per (request, KV head).  Each request's
- *              sub-pages are cut into contiguous chunks of one length C for the whole
- *              call, chunk s being split s; partials are merged by the log-sum-exp
- *              combine.  The matrix-core kernels take C = about the call's total
- *              sub-pages over all (request, KV head) pairs divided by the workgroups
- *              the GPU holds at once (so long and short requests balance), at least
- *              ceil(longest request's sub-pages / num_splits) and at most 1024; the
- *              vector-ALU kernels take C = ceil(max_sub_pages / num_splits).  With at
+ *              sub-pages are cut into contiguous runs, run s being split s; partials
+ *              are merged by the log-sum-exp combine.  The default matrix-core kernel
+ *              (B <= 512) cuts a pair of n sub-pages into k = ceil(n / C) near-equal
+ *              runs, C the smallest length for which every pair's runs fit the
+ *              workgroups the GPU holds at once, at least ceil(longest request's
+ *              sub-pages / num_splits) (so k <= num_splits) and at most 1024, chosen on
+ *              the device from kv_len; splits past a pair's k are empty.  The others
+ *              take runs of one length C for the whole call: about the call's total
+ *              sub-pages over all pairs divided by the workgroups the GPU holds at once,
+ *              within the same bounds (the vector-ALU kernels: C = ceil(max_sub_pages /
+ *              num_splits)).  With at
  *              least two (request, KV head) pairs per compute unit, num_splits >= 2,
  *              B <= 2048 and ceil(max_sub_pages / (num_splits - 1)) <= 1024, the call
  *              runs persistent instead: the pairs are laid end to end and every
