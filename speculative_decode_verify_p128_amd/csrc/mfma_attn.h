@@ -356,8 +356,9 @@ struct DensePiece {
   int row0, qo, kv;  // the request's first query row, query rows and KV length
 };
 
-// ceil(v / c) for 0 <= v < 2^24, 1 <= c < 2^24: a float quotient corrected by one step
-// (an integer division is a long instruction sequence, and the search below takes many)
+// ceil(v / c) for 0 <= v <= 2^20, c >= 1, rc within a few ulp of 1 / c: the float
+// quotient is then within 1 of v / c and one correction step makes it exact (an integer
+// division is a long instruction sequence, and the search below takes many)
 __device__ __forceinline__ int ceil_div_small(int v, int c, float rc) {
   int q = static_cast<int>(static_cast<float>(v) * rc);
   q += (q + 1) * c <= v ? 1 : 0;
@@ -365,9 +366,10 @@ __device__ __forceinline__ int ceil_div_small(int v, int c, float rc) {
   return q + (q * c < v ? 1 : 0);
 }
 
-__device__ inline bool dense_compact_piece(const AttnArgs& a, int max_blocks, int* lds,
-                                           DensePiece& pc) {
-  constexpr int NI = kCompactMaxRequests / kWave;
+// NI: request slots a lane of wave 0 holds (B <= 64 * NI).
+template <int NI>
+__device__ inline bool dense_compact_piece_t(const AttnArgs& a, int max_blocks, int* lds,
+                                             DensePiece& pc) {
   const int tid = threadIdx.x;
   const int Hkv = a.num_kv_heads;
   const int S = a.num_splits;
@@ -400,7 +402,7 @@ __device__ inline bool dense_compact_piece(const AttnArgs& a, int max_blocks, in
     mx = static_cast<int>(wave_max_u32(static_cast<uint32_t>(mx)));
     auto runs_of = [&](int v, int c, float rc) { return v <= c ? 1 : ceil_div_small(v, c, rc); };
     auto pieces = [&](int c) {   // runs over all pairs at run length c (wave-uniform)
-      const float rc = 1.0f / static_cast<float>(c);
+      const float rc = __builtin_amdgcn_rcpf(static_cast<float>(c));   // within 1 ulp
       int t = 0;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
@@ -428,7 +430,7 @@ __device__ inline bool dense_compact_piece(const AttnArgs& a, int max_blocks, in
       else lo = mid + 1;
     }
     const int c = lo;
-    const float rc = 1.0f / static_cast<float>(c);
+    const float rc = __builtin_amdgcn_rcpf(static_cast<float>(c));
     int k[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) k[i] = runs_of(nb[i], c, rc);
@@ -486,6 +488,15 @@ __device__ inline bool dense_compact_piece(const AttnArgs& a, int max_blocks, in
   pc.qo = lds[7];
   pc.kv = lds[8];
   return true;
+}
+
+// The plan with as few request slots a lane as the batch needs (the slots are unrolled).
+__device__ inline bool dense_compact_piece(const AttnArgs& a, int max_blocks, int* lds,
+                                           DensePiece& pc) {
+  static_assert(kCompactMaxRequests == 8 * kWave, "slot counts below");
+  if (a.B <= kWave) return dense_compact_piece_t<1>(a, max_blocks, lds, pc);
+  if (a.B <= 2 * kWave) return dense_compact_piece_t<2>(a, max_blocks, lds, pc);
+  return dense_compact_piece_t<8>(a, max_blocks, lds, pc);
 }
 
 // Where the 32-token blocks of a (request, KV head) come from.

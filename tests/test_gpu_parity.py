@@ -101,9 +101,14 @@ DENSE_MANY = W.DENSE_BF16.scaled(name="dense_many", batch=100, kv=("uniform", 40
                                  kv_capacity=1216)
 
 
-@pytest.fixture(scope="module")
-def dense_many():
-    c = W.make_dense_case(DENSE_MANY)
+# Over 128 requests (eight a lane) in fewer than 512 pairs: two KV heads.
+DENSE_MANY_200 = W.DENSE_BF16.scaled(name="dense_many_200", batch=200, num_q_heads=16,
+                                     num_kv_heads=2, kv=("uniform", 40, 600), kv_capacity=640)
+
+
+@pytest.fixture(scope="module", params=[DENSE_MANY, DENSE_MANY_200], ids=lambda w: w.name)
+def dense_many(request):
+    c = W.make_dense_case(request.param)
     return c, dense_oracle(c)
 
 
