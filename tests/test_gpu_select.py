@@ -155,6 +155,34 @@ def test_select_bit_search_ties_and_signed_zeros():
     assert torch.equal(out[:run.n], out2[:run.n]), "fused and two-launch outputs differ"
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+@pytest.mark.parametrize("w", [SPARSE_S, RAGGED_S], ids=lambda w: w.name)
+def test_select_union_only_ties(w, splits):
+    # six score values (with -0 and +0) over tables of up to a few hundred pages: the
+    # selection that only feeds the page union (no ranked output asked for) must take the
+    # same pages as the standalone top-k, ties going to the lower page
+    c = W.make_sparse_case(w)
+    run = SparseRun(c)
+    rng = np.random.default_rng(12)
+    vals = np.array([-2.0, -0.0, 0.0, 0.25, 1.0, 3.0], dtype=np.float32)
+    s_np = vals[rng.integers(0, len(vals), size=(w.batch * w.max_qo(), w.num_kv_heads,
+                                                   w.max_pages()))]
+    scores = torch.from_numpy(s_np).to(DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, _, _ = _select(run, scores, splits, write=False, dev_err=err)
+    idx2, _ = run.topk(scores)
+    out2 = run.attend(idx2, num_splits=splits)
+    torch.cuda.synchronize()
+    got = idx2.cpu().numpy()
+    ind = c.qo_indptr.numpy()
+    for r in range(w.batch):
+        a, b = ind[r], ind[r + 1]
+        e, _ = oracle.ladder_topk_request(s_np[a:b], int(c.lengths.kv[r]), w.top_k)
+        assert np.array_equal(got[a:b], e.astype(np.int32)), f"request {r}"
+    assert int(err.item()) == 0
+    assert torch.equal(out[:run.n], out2[:run.n]), "fused and two-launch outputs differ"
+
+
 def test_select_over_1024_pages_selects_in_its_own_launch():
     # 1100-page table: the selection runs as the standalone top-k into topk_idx, then the
     # sparse attention over it; without topk_idx the call is refused on the host
